@@ -1,0 +1,314 @@
+"""Benchmark of the FSDP data-parallel hot path on one MI355X.
+
+One step = for every FSDP unit of the model, in order: all-gather +
+unflatten its bf16 shards into R full-unit receivers, then the fused
+reduce-scatter-average of the R bf16 gradient replicas + AdamW on the fp32
+master/m/v shards + bf16 recast.  Default workload: the 12-layer model of
+TransformerBlocks (hidden 512, ffn 2048), one FSDP2 per-parameter unit per
+block, R = 8 virtual ranks in one GPU's memory (37,761,024 parameters).
+Inputs are synthetic, seeded and resident in HBM before timing starts.
+
+Prints one JSON line: params/s of the whole step, achieved algorithmic HBM
+GB/s, the roofline of the dominant (fused) kernel from HIP events around its
+launches, and the CPU oracle timed on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="model12_r8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_src_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.hpp", "plan.cpp", "abi.cpp"):
+        with open(os.path.join(ROOT, "fully_sharded_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """Counter-measured HBM bytes per fused launch, if taken on the current
+    kernel sources (profiles/traffic_<workload>.json), else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_src_sha") != kernel_src_hash():
+        return None
+    return tr.get("fused_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the R ranks are virtual ranks in one GPU's "
+              f"memory and this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fully_sharded_amd as F
+    from workloads import gen
+    from workloads.configs import ADAMW, WORKLOADS, shapes_of
+
+    wl = WORKLOADS[args.workload]
+    R = wl["R"]
+    units = wl["units"]
+    dev = "cuda"
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    gdt = torch.bfloat16 if wl["grad_dtype"] == "bf16" else torch.float32
+    pdt = torch.bfloat16 if wl["param_dtype"] == "bf16" else torch.float32
+
+    # ---------------------------------------------------------------- set-up
+    plans = {}
+    state = []
+    t_setup = time.perf_counter()
+    for u, unit in enumerate(units):
+        shapes = tuple(shapes_of(unit))
+        if shapes not in plans:
+            plans[shapes] = F.Plan(list(shapes), R, wl["layout"])
+            plans[shapes].prepare()
+        pl = plans[shapes]
+        full = gen.device_master(wl, u, list(shapes), dev)
+        master = torch.empty(R * pl.S, dtype=torch.float32, device=dev)
+        F.fsdp_shard_pack(pl, full, master)
+        param = torch.empty(R * pl.S, dtype=pdt, device=dev)
+        F.fsdp_shard_pack(pl, full, param)
+        del full
+        grads = [gen.device_grad(wl, 1, u, r, pl.T, dev) for r in range(R)]
+        state.append(dict(plan=pl, master=master, m=torch.zeros_like(master),
+                          v=torch.zeros_like(master), param=param, grads=grads))
+    T_max = max(p.T for p in plans.values())
+    recv = [torch.empty(T_max, dtype=pdt, device=dev) for _ in range(R)]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    P = sum(s["plan"].T for s in state)
+
+    step_no = [0]
+
+    def step(events=None):
+        step_no[0] += 1
+        t = step_no[0]
+        for i, s in enumerate(state):
+            pl = s["plan"]
+            outs = [x[:pl.T] for x in recv]
+            if events is not None:
+                events[i][0].record(stream)
+            F.fsdp_gather_unflatten(pl, s["param"], outs)
+            if events is not None:
+                events[i][1].record(stream)
+            F.fsdp_adamw_shard_step(pl, ADAMW, t, s["grads"], s["master"], s["m"], s["v"],
+                                    s["param"])
+            if events is not None:
+                events[i][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ----------------------------------------- timed region: the clean steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ------------------ per-kernel durations: HIP events around every launch
+    n_inst = max(10, min(args.steps, 50))
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in state]
+          for _ in range(n_inst)]
+    torch.cuda.synchronize()
+    for k in range(n_inst):
+        step(ev[k])
+    torch.cuda.synchronize()
+    gather_ms = np.array([[ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(len(state))]
+                          for k in range(n_inst)])
+    fused_ms = np.array([[ev[k][i][1].elapsed_time(ev[k][i][2]) for i in range(len(state))]
+                         for k in range(n_inst)])
+
+    # algorithmic bytes (valid parameters only, padding excluded)
+    fused_bytes_unit = [s["plan"].T * (2 * R + 26) if gdt == torch.bfloat16 else
+                        s["plan"].T * (4 * R + 26) for s in state]
+    pes = 2 if pdt == torch.bfloat16 else 4
+    gather_bytes_unit = [s["plan"].T * (pes + pes * R) for s in state]
+    step_bytes = sum(fused_bytes_unit) + sum(gather_bytes_unit)
+    fused_avg_ms = float(fused_ms.mean())
+    fused_bytes = float(np.mean(fused_bytes_unit))
+    achieved = fused_bytes / (fused_avg_ms * 1e-3) / 1e9
+    gather_avg_ms = float(gather_ms.mean())
+    gather_gbps = float(np.mean(gather_bytes_unit)) / (gather_avg_ms * 1e-3) / 1e9
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+
+    copy_info = None
+    if args.calibrate_copy:
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            b.copy_(a)
+        c0.record(stream)
+        for _ in range(10):
+            b.copy_(a)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / 10
+        copy_info = dict(bytes=2 * n * 4, ms=ms, gbps=2 * n * 4 / (ms * 1e-3) / 1e9)
+        del a, b
+
+    # ------------------------------------------ CPU baseline: the oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(state, R, wl, args.cpu_seconds)
+
+    line = {
+        "metric": "shard-step params/s and achieved HBM GB/s (% of peak), 12-layer R=8",
+        "value": P / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "units": len(units),
+            "R": R,
+            "layout": wl["layout"],
+            "params": P,
+            "param_dtype": wl["param_dtype"],
+            "grad_dtype": wl["grad_dtype"],
+            "state_dtype": "f32",
+            "launches_per_step": 2 * len(units),
+            "step": "per unit: gather+unflatten to R receivers, fused RS-avg+AdamW+recast",
+        },
+        "hbm_gbps": step_gbps,
+        "hbm_frac": step_gbps / PEAK_HBM_GBPS,
+        "step_bytes": step_bytes,
+        "kernels": {
+            "fused_rs_adamw": {"avg_ms": fused_avg_ms, "bytes": fused_bytes, "gbps": achieved},
+            "gather_unflatten": {"avg_ms": gather_avg_ms,
+                                 "bytes": float(np.mean(gather_bytes_unit)), "gbps": gather_gbps},
+            "event_launches": int(fused_ms.size),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+        "setup_s": setup_s,
+    }
+    if copy_info:
+        line["copy_calibration"] = copy_info
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(state, R, wl, budget_s):
+    """The oracle, as it stands, on the same inputs (copied back to the host):
+    per unit, R gathers (one per receiving rank) then the shard step, units
+    in order until about budget_s seconds of CPU work."""
+    import numpy as np
+
+    from oracle import fsdp_oracle as O
+
+    def host(t):
+        import torch
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    hp = {k: wl_hp for k, wl_hp in __import__("workloads.configs", fromlist=["ADAMW"]).ADAMW.items()}
+    done = 0
+    secs = 0.0
+    units = 0
+    plans = {}
+    for i, s in enumerate(state):
+        pl = s["plan"]
+        key = tuple(pl.shapes)
+        if key not in plans:
+            plans[key] = O.plan_layout(list(pl.shapes), R, wl["layout"])
+        po = plans[key]
+        grads = [host(g) for g in s["grads"]]
+        master = host(s["master"]).reshape(R, po.S).copy()
+        m = host(s["m"]).reshape(R, po.S).copy()
+        v = host(s["v"]).reshape(R, po.S).copy()
+        param = host(s["param"]).reshape(R, po.S).copy()
+        t0 = time.perf_counter()
+        for _ in range(R):
+            O.gather_unflatten(po, param)
+        O.shard_step(po, grads, master, m, v, 1, hp, wl["param_dtype"])
+        secs += time.perf_counter() - t0
+        done += po.T
+        units += 1
+        if secs >= budget_s:
+            break
+    import platform
+    cpu_model = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": done / secs,
+        "unit": "params/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{units} of {len(state)} units of one step (R={R}: {R} gathers + "
+                  f"reduce-scatter-average + AdamW + recast per unit), {done} params, "
+                  f"{secs:.2f} s; NumPy element-wise on one thread; {cpu_model}",
+    }
+
+
+if __name__ == "__main__":
+    main()

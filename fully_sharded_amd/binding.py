@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libfsdp_hip.so, with the C ABI's names.
+
+Only argument marshalling happens here: torch tensors become device
+pointers and torch's current HIP stream becomes the stream argument.  Every
+step of the path runs in the library's HIP kernels; if the library is missing
+this module raises instead of computing anything itself.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsdp_hip.so")
+
+PER_PARAM = 0
+FLAT = 1
+F32 = 0
+BF16 = 1
+MAX_RANKS = 64
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "out of memory",
+           -4: "HIP runtime error"}
+
+
+class FsdpError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("numel_full", ctypes.c_int64), ("shard_numel", ctypes.c_int64),
+                ("world", ctypes.c_int32), ("n_params", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("n_segments", ctypes.c_int32)]
+
+
+_lib = None
+
+# name -> (restype, argtypes); mirrors include/fsdp_hip.h
+_SIGS = {
+    "fsdp_plan_layout": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]),
+    "fsdp_plan_destroy": (None, [ctypes.c_void_p]),
+    "fsdp_plan_get_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]),
+    "fsdp_plan_param": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_int64)]),
+    "fsdp_plan_rank_valid": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int64)]),
+    "fsdp_plan_segments": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.c_int32]),
+    "fsdp_plan_comm_ledger": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_int64)]),
+    "fsdp_plan_state_bytes_per_rank": (ctypes.c_int64, [ctypes.c_void_p]),
+    "fsdp_plan_prepare": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "fsdp_shard_pack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "fsdp_gather_unflatten": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p]),
+    "fsdp_reduce_scatter_avg": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "fsdp_adamw_shard_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(AdamWHParams),
+                                             ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p),
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_void_p]),
+    "fsdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m fully_sharded_amd._build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise FsdpError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16 bits)")
+
+
+def _dev(t: torch.Tensor, what: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A unit's sharding plan (host object owning the C plan)."""
+
+    def __init__(self, shapes, R: int, layout):
+        if isinstance(layout, str):
+            layout = {"per_param": PER_PARAM, "flat": FLAT}[layout]
+        shapes = [tuple(int(d) for d in s) for s in shapes]
+        nd = (ctypes.c_int32 * len(shapes))(*[len(s) for s in shapes])
+        flat = [d for s in shapes for d in s]
+        dims = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+        h = ctypes.c_void_p()
+        _check("fsdp_plan_layout",
+               lib().fsdp_plan_layout(len(shapes), nd, dims, int(R), int(layout), ctypes.byref(h)))
+        self._h = h
+        info = PlanInfo()
+        _check("fsdp_plan_get_info", lib().fsdp_plan_get_info(h, ctypes.byref(info)))
+        self.shapes = shapes
+        self.T = info.numel_full
+        self.S = info.shard_numel
+        self.R = info.world
+        self.n_params = info.n_params
+        self.layout = info.layout
+        self.n_segments = info.n_segments
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.fsdp_plan_destroy(h)
+            self._h = None
+
+    def param(self, p: int):
+        out = (ctypes.c_int64 * 5)()
+        _check("fsdp_plan_param", lib().fsdp_plan_param(self._h, p, out))
+        return dict(flat_off=out[0], numel=out[1], shard_off=out[2], rows_per_shard=out[3],
+                    row_numel=out[4])
+
+    def rank_valid(self, r: int) -> int:
+        v = ctypes.c_int64()
+        _check("fsdp_plan_rank_valid", lib().fsdp_plan_rank_valid(self._h, r, ctypes.byref(v)))
+        return v.value
+
+    def segments(self):
+        out = (ctypes.c_int64 * (4 * max(1, self.n_segments)))()
+        _check("fsdp_plan_segments", lib().fsdp_plan_segments(self._h, out, self.n_segments))
+        return [tuple(out[4 * i:4 * i + 4]) for i in range(self.n_segments)]
+
+    def comm_ledger(self, reshard_after_forward: bool = True):
+        out = (ctypes.c_int64 * 4)()
+        _check("fsdp_plan_comm_ledger",
+               lib().fsdp_plan_comm_ledger(self._h, int(bool(reshard_after_forward)), out))
+        return dict(all_gather=out[0], reduce_scatter=out[1], optimizer=out[2], total=out[3])
+
+    def state_bytes_per_rank(self) -> int:
+        return lib().fsdp_plan_state_bytes_per_rank(self._h)
+
+    def prepare(self, stream=None):
+        _check("fsdp_plan_prepare", lib().fsdp_plan_prepare(self._h, _stream(stream)))
+
+    def unflatten(self, full: torch.Tensor):
+        """Per-parameter views of a full-unit buffer [T] (no copy)."""
+        views = []
+        for p, shape in enumerate(self.shapes):
+            q = self.param(p)
+            views.append(full[q["flat_off"]:q["flat_off"] + q["numel"]].view(shape))
+        return views
+
+
+def fsdp_plan_layout(shapes, R: int, layout) -> Plan:
+    return Plan(shapes, R, layout)
+
+
+def _ptr_array(tensors, what):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = None if t is None else _dev(t, f"{what}[{i}]")
+    return arr
+
+
+def fsdp_shard_pack(plan: Plan, full: torch.Tensor, shards: torch.Tensor, stream=None):
+    """full [T] -> shards [R, S] (same dtype: exact copy; f32 -> bf16: RNE)."""
+    if full.numel() != plan.T or shards.numel() != plan.R * plan.S:
+        raise ValueError("size mismatch with the plan")
+    _check("fsdp_shard_pack",
+           lib().fsdp_shard_pack(plan.handle, _dev(full, "full"), _dtype_code(full),
+                                 _dev(shards, "shards"), _dtype_code(shards), _stream(stream)))
+
+
+def fsdp_gather_unflatten(plan: Plan, shards: torch.Tensor, full_out, stream=None):
+    """shards [R, S] -> R full-unit buffers (list of R tensors [T] or None)."""
+    if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
+        raise ValueError("size mismatch with the plan")
+    for t in full_out:
+        if t is not None and (t.numel() != plan.T or t.dtype != shards.dtype):
+            raise ValueError("receiver size or dtype mismatch")
+    arr = _ptr_array(full_out, "full_out")
+    _check("fsdp_gather_unflatten",
+           lib().fsdp_gather_unflatten(plan.handle, _dev(shards, "shards"), _dtype_code(shards),
+                                       arr, _stream(stream)))
+
+
+def fsdp_reduce_scatter_avg(plan: Plan, grads, out: torch.Tensor, stream=None):
+    """R per-rank full-unit grads [T] -> averaged fp32 shards out [R, S]."""
+    if len(grads) != plan.R or out.numel() != plan.R * plan.S or out.dtype != torch.float32:
+        raise ValueError("size or dtype mismatch with the plan")
+    dt = _dtype_code(grads[0])
+    for g in grads:
+        if g.numel() != plan.T or _dtype_code(g) != dt:
+            raise ValueError("gradient size or dtype mismatch")
+    arr = _ptr_array(grads, "grads")
+    _check("fsdp_reduce_scatter_avg",
+           lib().fsdp_reduce_scatter_avg(plan.handle, arr, dt, _dev(out, "out"), _stream(stream)))
+
+
+def fsdp_adamw_shard_step(plan: Plan, hp: dict, step: int, grads, master, m, v, param_out,
+                          grads_are_replicas: bool = True, stream=None):
+    """AdamW on the [R, S] fp32 shards (in place) + recast into param_out.
+
+    grads: list of R full-unit replicas [T] (fused reduce-scatter-average) or,
+    with grads_are_replicas=False, one fp32 [R, S] tensor (or a 1-list)."""
+    n = plan.R * plan.S
+    for t, nm in ((master, "master"), (m, "m"), (v, "v")):
+        if t.numel() != n or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be fp32 with R*S elements")
+    if param_out.numel() != n:
+        raise ValueError("param_out must have R*S elements")
+    if grads_are_replicas:
+        if len(grads) != plan.R:
+            raise ValueError("need R gradient replicas")
+        dt = _dtype_code(grads[0])
+        for g in grads:
+            if g.numel() != plan.T or _dtype_code(g) != dt:
+                raise ValueError("gradient size or dtype mismatch")
+    else:
+        if isinstance(grads, torch.Tensor):
+            grads = [grads]
+        if grads[0].numel() != n or grads[0].dtype != torch.float32:
+            raise ValueError("reduced gradient must be fp32 [R, S]")
+        dt = F32
+    arr = _ptr_array(grads, "grads")
+    h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    _check("fsdp_adamw_shard_step",
+           lib().fsdp_adamw_shard_step(plan.handle, ctypes.byref(h), int(step), arr, dt,
+                                       int(bool(grads_are_replicas)), _dev(master, "master"),
+                                       _dev(m, "m"), _dev(v, "v"), _dev(param_out, "param_out"),
+                                       _dtype_code(param_out), _stream(stream)))

@@ -1,0 +1,323 @@
+// extern "C" boundary of the FSDP hot-path library: argument checks, then
+// one kernel launch per call on the caller's stream.  Declarations and the
+// contract of every entry point are in include/fsdp_hip.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "fsdp_hip.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+using fsdp::AdamScalars;
+using fsdp::DeviceTables;
+using fsdp::PtrArray;
+
+namespace {
+
+bool valid_dtype(int32_t dt) { return dt == FSDP_F32 || dt == FSDP_BF16; }
+int64_t dtype_size(int32_t dt) { return dt == FSDP_F32 ? 4 : 2; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+bool any_overlap(const std::vector<Range>& rs) {
+  for (size_t i = 0; i < rs.size(); ++i)
+    for (size_t j = i + 1; j < rs.size(); ++j)
+      if (overlap(rs[i], rs[j])) return true;
+  return false;
+}
+
+fsdp_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return FSDP_OK;
+  (void)hipGetLastError();
+  return e == hipErrorOutOfMemory ? FSDP_ERR_OUT_OF_MEMORY : FSDP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fsdp_status fsdp_plan_layout(int32_t n_params, const int32_t* ndims, const int64_t* dims,
+                             int32_t R, int32_t layout, fsdp_plan** out) {
+  if (!out) return FSDP_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (n_params < 1 || !ndims || !dims) return FSDP_ERR_INVALID_ARG;
+  if (R < 1) return FSDP_ERR_INVALID_ARG;
+  if (R > FSDP_MAX_RANKS) return FSDP_ERR_UNSUPPORTED;
+  if (layout != FSDP_LAYOUT_PER_PARAM && layout != FSDP_LAYOUT_FLAT) return FSDP_ERR_INVALID_ARG;
+  fsdp_plan* pl = new (std::nothrow) fsdp_plan();
+  if (!pl) return FSDP_ERR_OUT_OF_MEMORY;
+  try {
+    pl->R = R;
+    pl->layout = layout;
+    int64_t at = 0;
+    for (int32_t p = 0; p < n_params; ++p) {
+      if (ndims[p] < 1 || ndims[p] > 8) {
+        delete pl;
+        return FSDP_ERR_INVALID_ARG;
+      }
+      std::vector<int64_t> shape(dims + at, dims + at + ndims[p]);
+      at += ndims[p];
+      for (int64_t d : shape)
+        if (d <= 0) {
+          delete pl;
+          return FSDP_ERR_INVALID_ARG;
+        }
+      pl->shapes.push_back(shape);
+    }
+    const fsdp_status st = fsdp::build_plan(pl);
+    if (st != FSDP_OK) {
+      delete pl;
+      return st;
+    }
+  } catch (const std::bad_alloc&) {
+    delete pl;
+    return FSDP_ERR_OUT_OF_MEMORY;
+  } catch (...) {
+    delete pl;
+    return FSDP_ERR_INVALID_ARG;
+  }
+  *out = pl;
+  return FSDP_OK;
+}
+
+void fsdp_plan_destroy(fsdp_plan* plan) {
+  if (!plan) return;
+  for (auto& kv : plan->device) (void)hipFree(kv.second.shard_work);
+  delete plan;
+}
+
+fsdp_status fsdp_plan_get_info(const fsdp_plan* plan, fsdp_plan_info* out) {
+  if (!plan || !out) return FSDP_ERR_INVALID_ARG;
+  out->numel_full = plan->T;
+  out->shard_numel = plan->S;
+  out->world = plan->R;
+  out->n_params = static_cast<int32_t>(plan->params.size());
+  out->layout = plan->layout;
+  out->n_segments = static_cast<int32_t>(plan->segments.size());
+  return FSDP_OK;
+}
+
+fsdp_status fsdp_plan_param(const fsdp_plan* plan, int32_t p, int64_t* out) {
+  if (!plan || !out || p < 0 || p >= static_cast<int32_t>(plan->params.size()))
+    return FSDP_ERR_INVALID_ARG;
+  const fsdp::Param& q = plan->params[p];
+  out[0] = q.flat_off;
+  out[1] = q.numel;
+  out[2] = q.shard_off;
+  out[3] = q.k;
+  out[4] = q.row;
+  return FSDP_OK;
+}
+
+fsdp_status fsdp_plan_rank_valid(const fsdp_plan* plan, int32_t r, int64_t* valid) {
+  if (!plan || !valid || r < 0 || r >= plan->R) return FSDP_ERR_INVALID_ARG;
+  int64_t n = 0;
+  for (const fsdp::Segment& s : plan->segments)
+    if (s.rank == r) n += s.len;
+  *valid = n;
+  return FSDP_OK;
+}
+
+fsdp_status fsdp_plan_segments(const fsdp_plan* plan, int64_t* out, int32_t capacity) {
+  if (!plan || !out || capacity < static_cast<int64_t>(plan->segments.size()))
+    return FSDP_ERR_INVALID_ARG;
+  for (size_t i = 0; i < plan->segments.size(); ++i) {
+    const fsdp::Segment& s = plan->segments[i];
+    out[4 * i + 0] = s.rank;
+    out[4 * i + 1] = s.shard_off;
+    out[4 * i + 2] = s.flat_off;
+    out[4 * i + 3] = s.len;
+  }
+  return FSDP_OK;
+}
+
+fsdp_status fsdp_plan_comm_ledger(const fsdp_plan* plan, int32_t reshard_after_forward,
+                                  int64_t* out) {
+  if (!plan || !out) return FSDP_ERR_INVALID_ARG;
+  const int64_t per_collective = (plan->R - 1) * plan->S;
+  out[0] = (reshard_after_forward ? 2 : 1) * per_collective;
+  out[1] = per_collective;
+  out[2] = 0;
+  out[3] = out[0] + out[1] + out[2];
+  return FSDP_OK;
+}
+
+int64_t fsdp_plan_state_bytes_per_rank(const fsdp_plan* plan) {
+  return plan ? 16 * plan->S : -1;
+}
+
+fsdp_status fsdp_plan_prepare(const fsdp_plan* plan, void* stream) {
+  (void)stream;
+  if (!plan) return FSDP_ERR_INVALID_ARG;
+  const DeviceTables* t = nullptr;
+  return fsdp::device_tables(plan, &t);
+}
+
+fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t full_dtype,
+                            void* shards, int32_t shard_dtype, void* stream) {
+  if (!plan || !full || !shards) return FSDP_ERR_INVALID_ARG;
+  if (!valid_dtype(full_dtype) || !valid_dtype(shard_dtype)) return FSDP_ERR_INVALID_ARG;
+  if (!aligned(full, dtype_size(full_dtype)) || !aligned(shards, dtype_size(shard_dtype)))
+    return FSDP_ERR_INVALID_ARG;
+  if (overlap(range_of(full, plan->T * dtype_size(full_dtype)),
+              range_of(shards, plan->R * plan->S * dtype_size(shard_dtype))))
+    return FSDP_ERR_INVALID_ARG;
+  const DeviceTables* t = nullptr;
+  fsdp_status st = fsdp::device_tables(plan, &t);
+  if (st != FSDP_OK) return st;
+  const bool vec = aligned(full, 16) && aligned(shards, 16);
+  const auto n_work = static_cast<int64_t>(plan->shard_work.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (full_dtype == shard_dtype) {
+    PtrArray dst{};
+    dst.p[0] = shards;
+    return from_hip(fsdp::launch_copy(t->shard_work, n_work, full, dst, 1,
+                                      static_cast<int>(dtype_size(full_dtype)), vec, s));
+  }
+  return from_hip(
+      fsdp::launch_pack_cast(t->shard_work, n_work, full, full_dtype, shards, shard_dtype, vec, s));
+}
+
+fsdp_status fsdp_gather_unflatten(const fsdp_plan* plan, const void* shards, int32_t dtype,
+                                  void* const* full_out, void* stream) {
+  if (!plan || !shards || !full_out || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
+  const int64_t es = dtype_size(dtype);
+  if (!aligned(shards, es)) return FSDP_ERR_INVALID_ARG;
+  std::vector<Range> ranges{range_of(shards, plan->R * plan->S * es)};
+  PtrArray dst{};
+  bool vec = aligned(shards, 16);
+  int n = 0;
+  for (int r = 0; r < plan->R; ++r) {
+    void* d = full_out[r];
+    dst.p[r] = d;
+    if (!d) continue;
+    if (!aligned(d, es)) return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(d, 16);
+    ranges.push_back(range_of(d, plan->T * es));
+    ++n;
+  }
+  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
+  if (n == 0) return FSDP_OK;
+  const DeviceTables* t = nullptr;
+  fsdp_status st = fsdp::device_tables(plan, &t);
+  if (st != FSDP_OK) return st;
+  return from_hip(fsdp::launch_copy(t->flat_work, static_cast<int64_t>(plan->flat_work.size()),
+                                    shards, dst, plan->R, static_cast<int>(es), vec,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* grads,
+                                    int32_t grad_dtype, float* out, void* stream) {
+  if (!plan || !grads || !out || !valid_dtype(grad_dtype)) return FSDP_ERR_INVALID_ARG;
+  const int64_t es = dtype_size(grad_dtype);
+  if (!aligned(out, 4)) return FSDP_ERR_INVALID_ARG;
+  const Range out_r = range_of(out, plan->R * plan->S * 4);
+  PtrArray g{};
+  bool vec = aligned(out, 16);
+  for (int q = 0; q < plan->R; ++q) {
+    if (!grads[q] || !aligned(grads[q], es)) return FSDP_ERR_INVALID_ARG;
+    if (overlap(out_r, range_of(grads[q], plan->T * es))) return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(grads[q], 16);
+    g.p[q] = grads[q];
+  }
+  const DeviceTables* t = nullptr;
+  fsdp_status st = fsdp::device_tables(plan, &t);
+  if (st != FSDP_OK) return st;
+  return from_hip(fsdp::launch_rs_avg(t->shard_work,
+                                      static_cast<int64_t>(plan->shard_work.size()), g, plan->R,
+                                      grad_dtype, out, vec, static_cast<hipStream_t>(stream)));
+}
+
+fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
+                                  int64_t step, const void* const* grads, int32_t grad_dtype,
+                                  int32_t grads_are_replicas, float* master, float* m, float* v,
+                                  void* param_out, int32_t param_dtype, void* stream) {
+  if (!plan || !hp || !grads || !master || !m || !v || !param_out) return FSDP_ERR_INVALID_ARG;
+  if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype)) return FSDP_ERR_INVALID_ARG;
+  if (step < 1) return FSDP_ERR_INVALID_ARG;
+  if (grads_are_replicas != 0 && grads_are_replicas != 1) return FSDP_ERR_INVALID_ARG;
+  const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps,
+               wd = hp->weight_decay;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || lr < 0 ||
+      !(b1 >= 0 && b1 < 1) || !(b2 >= 0 && b2 < 1) || !(eps > 0) || wd < 0)
+    return FSDP_ERR_INVALID_ARG;
+
+  const int64_t n = plan->R * plan->S;
+  const int64_t pes = dtype_size(param_dtype);
+  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(param_out, pes))
+    return FSDP_ERR_INVALID_ARG;
+  std::vector<Range> ranges{range_of(master, n * 4), range_of(m, n * 4), range_of(v, n * 4),
+                            range_of(param_out, n * pes)};
+  bool vec = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) && aligned(param_out, 16);
+  PtrArray g{};
+  if (grads_are_replicas) {
+    const int64_t ges = dtype_size(grad_dtype);
+    for (int q = 0; q < plan->R; ++q) {
+      if (!grads[q] || !aligned(grads[q], ges)) return FSDP_ERR_INVALID_ARG;
+      const Range gr = range_of(grads[q], plan->T * ges);
+      for (const Range& o : ranges)
+        if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
+      vec = vec && aligned(grads[q], 16);
+      g.p[q] = grads[q];
+    }
+  } else {
+    if (grad_dtype != FSDP_F32 || !grads[0] || !aligned(grads[0], 4)) return FSDP_ERR_INVALID_ARG;
+    const Range gr = range_of(grads[0], n * 4);
+    for (const Range& o : ranges)
+      if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(grads[0], 16);
+  }
+  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
+
+  AdamScalars sc;
+  const double t = static_cast<double>(step);
+  sc.decay = 1.0 - lr * wd;
+  sc.beta1 = b1;
+  sc.omb1 = 1.0 - b1;
+  sc.beta2 = b2;
+  sc.omb2 = 1.0 - b2;
+  sc.bc1 = 1.0 - std::pow(b1, t);
+  sc.bc2 = 1.0 - std::pow(b2, t);
+  sc.lr = lr;
+  sc.eps = eps;
+  if (!(sc.bc1 > 0) || !(sc.bc2 > 0)) return FSDP_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!grads_are_replicas)
+    return from_hip(fsdp::launch_adamw(n, static_cast<const float*>(grads[0]), master, m, v,
+                                       param_out, param_dtype, sc, vec, s));
+  const DeviceTables* tb = nullptr;
+  fsdp_status st = fsdp::device_tables(plan, &tb);
+  if (st != FSDP_OK) return st;
+  return from_hip(fsdp::launch_fused(tb->shard_work,
+                                     static_cast<int64_t>(plan->shard_work.size()), g, plan->R,
+                                     grad_dtype, master, m, v, param_out, param_dtype, sc, vec, s));
+}
+
+const char* fsdp_status_string(fsdp_status status) {
+  switch (status) {
+    case FSDP_OK: return "ok";
+    case FSDP_ERR_INVALID_ARG: return "invalid argument";
+    case FSDP_ERR_UNSUPPORTED: return "unsupported";
+    case FSDP_ERR_OUT_OF_MEMORY: return "out of memory";
+    case FSDP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

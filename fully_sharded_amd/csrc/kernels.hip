@@ -1,0 +1,499 @@
+// gfx950 kernels of the FSDP data-parallel hot path.
+//
+// All of them stream through HBM with no data reuse, so each is bound by
+// HBM bandwidth, not by arithmetic: every lane moves 8 consecutive elements
+// per pass (16-byte loads/stores for bf16, 2 x 16 bytes for fp32), a
+// 256-lane workgroup moves 2048 consecutive elements per pass, and one
+// workgroup owns one work item (a contiguous range that never crosses a
+// shard/parameter boundary, so the source offset is one constant per
+// workgroup).  Lanes whose 8-element chunk is cut by the ends of the range,
+// or whose source is not 16-byte aligned relative to the destination, take
+// an element-by-element path with the same arithmetic.
+//
+// Reductions are fp32, in rank order 0..R-1 starting from rank 0's value,
+// then one correctly rounded division by R: one lane owns an element and
+// nothing is reassociated, so results are deterministic and independent of
+// the launch shape.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace fsdp {
+namespace {
+
+constexpr int kThreads = 256;
+
+using u16 = uint16_t;
+
+// ------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set, sign kept);
+// values beyond the largest bf16 become infinity.
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 8 elements of T <-> 8 floats.  vec: one/two aligned 16-byte accesses;
+// otherwise element by element.
+template <typename T>
+struct Io;
+
+template <>
+struct Io<float> {
+  __device__ __forceinline__ static void load8(const float* p, bool vec, float (&x)[8]) {
+    if (vec) {
+      const float4 a = reinterpret_cast<const float4*>(p)[0];
+      const float4 b = reinterpret_cast<const float4*>(p)[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = p[k];
+    }
+  }
+  __device__ __forceinline__ static void store8(float* p, bool vec, const float (&x)[8]) {
+    if (vec) {
+      reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+      reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = x[k];
+    }
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float x) { *p = x; }
+};
+
+template <>
+struct Io<u16> {
+  __device__ __forceinline__ static void load8(const u16* p, bool vec, float (&x)[8]) {
+    if (vec) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p);
+      x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+      x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+      x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
+      x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = bf16_to_f32(p[k]);
+    }
+  }
+  __device__ __forceinline__ static void store8(u16* p, bool vec, const float (&x)[8]) {
+    if (vec) {
+      uint4 u;
+      u.x = f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16);
+      u.y = f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16);
+      u.z = f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16);
+      u.w = f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16);
+      *reinterpret_cast<uint4*>(p) = u;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] = static_cast<u16>(f32_to_bf16(x[k]));
+    }
+  }
+  __device__ __forceinline__ static float load1(const u16* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store1(u16* p, float x) {
+    *p = static_cast<u16>(f32_to_bf16(x));
+  }
+};
+
+// ------------------------------------------------------ rank-order average
+// avg[k] = (g_0[s+k] + g_1[s+k] + ... + g_{R-1}[s+k]) / R, fp32, left to
+// right.  RT > 0: R known at compile time (all R loads issued before the
+// adds); RT == 0: any R.
+template <typename G, int RT>
+__device__ __forceinline__ void grad_avg8(const PtrArray& g, int R, int64_t s, bool vec,
+                                          float (&avg)[8]) {
+  if constexpr (RT > 0) {
+    float x[RT][8];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) Io<G>::load8(static_cast<const G*>(g.p[q]) + s, vec, x[q]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float acc = x[0][k];
+#pragma unroll
+      for (int q = 1; q < RT; ++q) acc = acc + x[q][k];
+      avg[k] = acc / static_cast<float>(RT);
+    }
+  } else {
+    Io<G>::load8(static_cast<const G*>(g.p[0]) + s, vec, avg);
+    for (int q = 1; q < R; ++q) {
+      float x[8];
+      Io<G>::load8(static_cast<const G*>(g.p[q]) + s, vec, x);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) avg[k] = avg[k] + x[k];
+    }
+    const float fr = static_cast<float>(R);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) avg[k] = avg[k] / fr;
+  }
+}
+
+template <typename G, int RT>
+__device__ __forceinline__ float grad_avg1(const PtrArray& g, int R, int64_t s) {
+  const int n = RT > 0 ? RT : R;
+  float acc = Io<G>::load1(static_cast<const G*>(g.p[0]) + s);
+  for (int q = 1; q < n; ++q) acc = acc + Io<G>::load1(static_cast<const G*>(g.p[q]) + s);
+  return acc / static_cast<float>(n);
+}
+
+// ------------------------------------------------------------------ AdamW
+// One element, in float64 from the fp32 state, in the order the update is
+// defined:
+//   p1 = p (1 - lr wd);  m' = b1 m + (1-b1) g;  v' = b2 v + ((1-b2) g) g;
+//   m^ = m' / (1 - b1^t);  v^ = v' / (1 - b2^t);
+//   p' = p1 - (lr m^) / (sqrt(v^) + eps)
+// with IEEE double operations (correctly rounded divide and sqrt, no
+// contraction), then each result rounded once to fp32.  A memory-bound
+// kernel has the ALU time for it: about 70 double operations per element
+// against 42 bytes of HBM traffic.
+__device__ __forceinline__ void adamw1(float gf, float& pf, float& mf, float& vf,
+                                       const AdamScalars& c) {
+  const double g = gf;
+  const double p1 = static_cast<double>(pf) * c.decay;
+  const double m1 = c.beta1 * static_cast<double>(mf) + c.omb1 * g;
+  const double v1 = c.beta2 * static_cast<double>(vf) + (c.omb2 * g) * g;
+  const double mh = m1 / c.bc1;
+  const double vh = v1 / c.bc2;
+  const double p2 = p1 - (c.lr * mh) / (sqrt(vh) + c.eps);
+  pf = static_cast<float>(p2);
+  mf = static_cast<float>(m1);
+  vf = static_cast<float>(v1);
+}
+
+// ------------------------------------------------------------------ copy
+template <int ES>
+struct Raw;
+template <>
+struct Raw<2> {
+  using E = u16;
+  struct V { uint4 a; };
+};
+template <>
+struct Raw<4> {
+  using E = uint32_t;
+  struct V { uint4 a, b; };
+};
+
+struct CopyArgs {
+  const void* src;
+  PtrArray dst;
+  int n_dst;
+  int vec;
+};
+
+template <int ES>
+__global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work, CopyArgs a) {
+  using E = typename Raw<ES>::E;
+  using V = typename Raw<ES>::V;
+  const Work w = work[blockIdx.x];
+  const E* __restrict__ src = static_cast<const E*>(a.src);
+  const bool pad = w.src < 0;
+  const int64_t delta = w.src - w.dst;
+  const bool vec = a.vec && (pad || (delta & 7) == 0);
+  const int64_t end = w.dst + w.len;
+  for (int64_t c = (w.dst >> 3) + threadIdx.x; (c << 3) < end; c += kThreads) {
+    const int64_t e0 = c << 3;
+    if (vec && e0 >= w.dst && e0 + 8 <= end) {
+      V v;
+      if (pad) {
+        v = V{};
+      } else {
+        v = *reinterpret_cast<const V*>(src + e0 + delta);
+      }
+      for (int k = 0; k < a.n_dst; ++k) {
+        E* d = static_cast<E*>(const_cast<void*>(a.dst.p[k]));
+        if (d) *reinterpret_cast<V*>(d + e0) = v;
+      }
+    } else {
+      const int64_t lo = e0 > w.dst ? e0 : w.dst;
+      const int64_t hi = e0 + 8 < end ? e0 + 8 : end;
+      for (int64_t e = lo; e < hi; ++e) {
+        const E x = pad ? E(0) : src[e + delta];
+        for (int k = 0; k < a.n_dst; ++k) {
+          E* d = static_cast<E*>(const_cast<void*>(a.dst.p[k]));
+          if (d) d[e] = x;
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- pack+cast
+struct CastArgs {
+  const void* src;
+  void* dst;
+  int vec;
+};
+
+template <typename S, typename D>
+__global__ __launch_bounds__(kThreads) void k_pack_cast(const Work* __restrict__ work,
+                                                        CastArgs a) {
+  const Work w = work[blockIdx.x];
+  const S* __restrict__ src = static_cast<const S*>(a.src);
+  D* __restrict__ dst = static_cast<D*>(a.dst);
+  const bool pad = w.src < 0;
+  const int64_t delta = w.src - w.dst;
+  const bool vec_dst = a.vec != 0;
+  const bool vec_src = vec_dst && (pad || (delta & 7) == 0);
+  const int64_t end = w.dst + w.len;
+  for (int64_t c = (w.dst >> 3) + threadIdx.x; (c << 3) < end; c += kThreads) {
+    const int64_t e0 = c << 3;
+    if (vec_dst && e0 >= w.dst && e0 + 8 <= end) {
+      float x[8];
+      if (pad) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+      } else {
+        Io<S>::load8(src + e0 + delta, vec_src, x);
+      }
+      Io<D>::store8(dst + e0, true, x);
+    } else {
+      const int64_t lo = e0 > w.dst ? e0 : w.dst;
+      const int64_t hi = e0 + 8 < end ? e0 + 8 : end;
+      for (int64_t e = lo; e < hi; ++e)
+        Io<D>::store1(dst + e, pad ? 0.0f : Io<S>::load1(src + e + delta));
+    }
+  }
+}
+
+// ------------------------------------------------------ reduce-scatter-avg
+struct RsArgs {
+  PtrArray g;
+  float* out;
+  int R;
+  int vec;
+};
+
+template <typename G, int RT>
+__global__ __launch_bounds__(kThreads) void k_rs_avg(const Work* __restrict__ work, RsArgs a) {
+  const Work w = work[blockIdx.x];
+  const bool pad = w.src < 0;
+  const int64_t delta = w.src - w.dst;
+  const bool vec_dst = a.vec != 0;
+  const bool vec_src = vec_dst && (pad || (delta & 7) == 0);
+  const int64_t end = w.dst + w.len;
+  for (int64_t c = (w.dst >> 3) + threadIdx.x; (c << 3) < end; c += kThreads) {
+    const int64_t e0 = c << 3;
+    if (vec_dst && e0 >= w.dst && e0 + 8 <= end) {
+      float avg[8];
+      if (pad) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) avg[k] = 0.0f;
+      } else {
+        grad_avg8<G, RT>(a.g, a.R, e0 + delta, vec_src, avg);
+      }
+      Io<float>::store8(a.out + e0, true, avg);
+    } else {
+      const int64_t lo = e0 > w.dst ? e0 : w.dst;
+      const int64_t hi = e0 + 8 < end ? e0 + 8 : end;
+      for (int64_t e = lo; e < hi; ++e)
+        a.out[e] = pad ? 0.0f : grad_avg1<G, RT>(a.g, a.R, e + delta);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ AdamW
+struct AdamArgs {
+  const float* g;
+  float* master;
+  float* m;
+  float* v;
+  void* param;
+  AdamScalars sc;
+  int64_t n;
+  int vec;
+};
+
+template <typename P>
+__global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
+  P* __restrict__ param = static_cast<P*>(a.param);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; (c << 3) < a.n;
+       c += stride) {
+    const int64_t e0 = c << 3;
+    if (a.vec && e0 + 8 <= a.n) {
+      float g[8], p[8], m[8], v[8];
+      Io<float>::load8(a.g + e0, true, g);
+      Io<float>::load8(a.master + e0, true, p);
+      Io<float>::load8(a.m + e0, true, m);
+      Io<float>::load8(a.v + e0, true, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) adamw1(g[k], p[k], m[k], v[k], a.sc);
+      Io<float>::store8(a.master + e0, true, p);
+      Io<float>::store8(a.m + e0, true, m);
+      Io<float>::store8(a.v + e0, true, v);
+      Io<P>::store8(param + e0, true, p);
+    } else {
+      const int64_t hi = e0 + 8 < a.n ? e0 + 8 : a.n;
+      for (int64_t e = e0; e < hi; ++e) {
+        float p = a.master[e], m = a.m[e], v = a.v[e];
+        adamw1(a.g[e], p, m, v, a.sc);
+        a.master[e] = p;
+        a.m[e] = m;
+        a.v[e] = v;
+        Io<P>::store1(param + e, p);
+      }
+    }
+  }
+}
+
+// -------------------------------------- fused reduce-scatter + AdamW + cast
+struct FusedArgs {
+  PtrArray g;
+  float* master;
+  float* m;
+  float* v;
+  void* param;
+  AdamScalars sc;
+  int R;
+  int vec;
+};
+
+template <typename G, typename P, int RT>
+__global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work, FusedArgs a) {
+  const Work w = work[blockIdx.x];
+  P* __restrict__ param = static_cast<P*>(a.param);
+  const bool pad = w.src < 0;
+  const int64_t delta = w.src - w.dst;
+  const bool vec_state = a.vec != 0;
+  const bool vec_src = vec_state && (pad || (delta & 7) == 0);
+  const int64_t end = w.dst + w.len;
+  for (int64_t c = (w.dst >> 3) + threadIdx.x; (c << 3) < end; c += kThreads) {
+    const int64_t e0 = c << 3;
+    if (vec_state && e0 >= w.dst && e0 + 8 <= end) {
+      float g[8];
+      if (pad) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) g[k] = 0.0f;
+      } else {
+        grad_avg8<G, RT>(a.g, a.R, e0 + delta, vec_src, g);
+      }
+      float p[8], m[8], v[8];
+      Io<float>::load8(a.master + e0, true, p);
+      Io<float>::load8(a.m + e0, true, m);
+      Io<float>::load8(a.v + e0, true, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) adamw1(g[k], p[k], m[k], v[k], a.sc);
+      Io<float>::store8(a.master + e0, true, p);
+      Io<float>::store8(a.m + e0, true, m);
+      Io<float>::store8(a.v + e0, true, v);
+      Io<P>::store8(param + e0, true, p);
+    } else {
+      const int64_t lo = e0 > w.dst ? e0 : w.dst;
+      const int64_t hi = e0 + 8 < end ? e0 + 8 : end;
+      for (int64_t e = lo; e < hi; ++e) {
+        const float g = pad ? 0.0f : grad_avg1<G, RT>(a.g, a.R, e + delta);
+        float p = a.master[e], m = a.m[e], v = a.v[e];
+        adamw1(g, p, m, v, a.sc);
+        a.master[e] = p;
+        a.m[e] = m;
+        a.v[e] = v;
+        Io<P>::store1(param + e, p);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- launch
+template <typename Args>
+hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a,
+                       hipStream_t stream) {
+  if (n_work <= 0) return hipSuccess;
+  if (n_work > 0x7fffffff) return hipErrorInvalidValue;
+  void* args[] = {const_cast<Work**>(&work), &a};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(n_work)), dim3(kThreads), args, 0,
+                         stream);
+}
+
+template <typename G>
+const void* pick_rs(int R) {
+  switch (R) {
+    case 1: return reinterpret_cast<const void*>(&k_rs_avg<G, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_rs_avg<G, 2>);
+    case 3: return reinterpret_cast<const void*>(&k_rs_avg<G, 3>);
+    case 4: return reinterpret_cast<const void*>(&k_rs_avg<G, 4>);
+    case 5: return reinterpret_cast<const void*>(&k_rs_avg<G, 5>);
+    case 6: return reinterpret_cast<const void*>(&k_rs_avg<G, 6>);
+    case 7: return reinterpret_cast<const void*>(&k_rs_avg<G, 7>);
+    case 8: return reinterpret_cast<const void*>(&k_rs_avg<G, 8>);
+    default: return reinterpret_cast<const void*>(&k_rs_avg<G, 0>);
+  }
+}
+
+template <typename G, typename P>
+const void* pick_fused(int R) {
+  switch (R) {
+    case 1: return reinterpret_cast<const void*>(&k_fused<G, P, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_fused<G, P, 2>);
+    case 3: return reinterpret_cast<const void*>(&k_fused<G, P, 3>);
+    case 4: return reinterpret_cast<const void*>(&k_fused<G, P, 4>);
+    case 5: return reinterpret_cast<const void*>(&k_fused<G, P, 5>);
+    case 6: return reinterpret_cast<const void*>(&k_fused<G, P, 6>);
+    case 7: return reinterpret_cast<const void*>(&k_fused<G, P, 7>);
+    case 8: return reinterpret_cast<const void*>(&k_fused<G, P, 8>);
+    default: return reinterpret_cast<const void*>(&k_fused<G, P, 0>);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const PtrArray& dst,
+                       int n_dst, int es, bool vec, hipStream_t stream) {
+  CopyArgs a{src, dst, n_dst, vec ? 1 : 0};
+  const void* fn = es == 2 ? reinterpret_cast<const void*>(&k_copy<2>)
+                           : reinterpret_cast<const void*>(&k_copy<4>);
+  return launch_work(fn, work, n_work, a, stream);
+}
+
+hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, int src_dt,
+                            void* dst, int dst_dt, bool vec, hipStream_t stream) {
+  CastArgs a{src, dst, vec ? 1 : 0};
+  const void* fn = nullptr;
+  if (src_dt == FSDP_F32 && dst_dt == FSDP_BF16)
+    fn = reinterpret_cast<const void*>(&k_pack_cast<float, u16>);
+  else if (src_dt == FSDP_BF16 && dst_dt == FSDP_F32)
+    fn = reinterpret_cast<const void*>(&k_pack_cast<u16, float>);
+  else
+    return hipErrorInvalidValue;
+  return launch_work(fn, work, n_work, a, stream);
+}
+
+hipError_t launch_rs_avg(const Work* work, int64_t n_work, const PtrArray& grads, int R,
+                         int grad_dt, float* out, bool vec, hipStream_t stream) {
+  RsArgs a{grads, out, R, vec ? 1 : 0};
+  const void* fn = grad_dt == FSDP_BF16 ? pick_rs<u16>(R) : pick_rs<float>(R);
+  return launch_work(fn, work, n_work, a, stream);
+}
+
+hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, float* v,
+                        void* param, int param_dt, const AdamScalars& sc, bool vec,
+                        hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  AdamArgs a{g, master, m, v, param, sc, n, vec ? 1 : 0};
+  const int64_t chunks = (n + 7) / 8;
+  int64_t blocks = (chunks + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  const void* fn = param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16>)
+                                         : reinterpret_cast<const void*>(&k_adamw<float>);
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0,
+                         stream);
+}
+
+hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads, int R,
+                        int grad_dt, float* master, float* m, float* v, void* param,
+                        int param_dt, const AdamScalars& sc, bool vec, hipStream_t stream) {
+  FusedArgs a{grads, master, m, v, param, sc, R, vec ? 1 : 0};
+  const void* fn;
+  if (grad_dt == FSDP_BF16)
+    fn = param_dt == FSDP_BF16 ? pick_fused<u16, u16>(R) : pick_fused<u16, float>(R);
+  else
+    fn = param_dt == FSDP_BF16 ? pick_fused<float, u16>(R) : pick_fused<float, float>(R);
+  return launch_work(fn, work, n_work, a, stream);
+}
+
+}  // namespace fsdp

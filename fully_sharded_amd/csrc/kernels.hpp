@@ -1,0 +1,50 @@
+// Launchers of the gfx950 kernels (internal; the C ABI validates first).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fsdp_hip.h"
+#include "plan.hpp"
+
+namespace fsdp {
+
+struct PtrArray {
+  const void* p[FSDP_MAX_RANKS];
+};
+
+// Scalars of one AdamW step, in float64, each computed on the host with the
+// same expression the definition uses (1 - lr*wd, 1 - b1, 1 - b1^t, ...).
+struct AdamScalars {
+  double decay;  // 1 - lr * wd
+  double beta1, omb1;  // b1, 1 - b1
+  double beta2, omb2;  // b2, 1 - b2
+  double bc1, bc2;     // 1 - b1^t, 1 - b2^t
+  double lr, eps;
+};
+
+// Copy along work items; es = element size in bytes (2 or 4).  dst holds
+// n_dst pointers (NULL entries are skipped); padding items write zeros.
+hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const PtrArray& dst,
+                       int n_dst, int es, bool vec, hipStream_t stream);
+
+// Pack with a dtype change (F32 -> BF16 round to nearest even, BF16 -> F32).
+hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, int src_dt,
+                            void* dst, int dst_dt, bool vec, hipStream_t stream);
+
+// Reduce-scatter-average over shard-space work items.
+hipError_t launch_rs_avg(const Work* work, int64_t n_work, const PtrArray& grads, int R,
+                         int grad_dt, float* out, bool vec, hipStream_t stream);
+
+// AdamW on n contiguous elements with an fp32 gradient of the same indexing.
+hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, float* v,
+                        void* param, int param_dt, const AdamScalars& sc, bool vec,
+                        hipStream_t stream);
+
+// Fused reduce-scatter-average + AdamW + recast over shard-space work items.
+hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads, int R,
+                        int grad_dt, float* master, float* m, float* v, void* param,
+                        int param_dt, const AdamScalars& sc, bool vec, hipStream_t stream);
+
+}  // namespace fsdp

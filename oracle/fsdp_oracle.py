@@ -238,15 +238,21 @@ def reduce_scatter_avg(pl: Plan, grads) -> np.ndarray:
     taken in rank order starting from rank 0's value, then divided by R.
     bf16 gradients (uint16 bits) are widened exactly.  Padding is +0."""
     assert len(grads) == pl.R
-    g32 = [_as_f32(g) for g in grads]
     out = np.zeros((pl.R, pl.S), np.float32)
     for r in range(pl.R):
         for f0, s0, n in pl.pieces(r):
-            acc = g32[0][f0:f0 + n].copy()
-            for q in range(1, pl.R):
-                acc = acc + g32[q][f0:f0 + n]
-            out[r, s0:s0 + n] = acc / np.float32(pl.R)
+            out[r, s0:s0 + n] = rank_order_mean([g[f0:f0 + n] for g in grads])
     return out
+
+
+def rank_order_mean(values) -> np.ndarray:
+    """Element-wise fp32 mean of R equally shaped arrays (fp32, or bf16 bits
+    widened exactly): acc = v_0; acc = acc + v_q for q = 1..R-1; acc / R.
+    The reduction every rank applies to its slice ([WALK] step 4.4)."""
+    acc = _as_f32(values[0]).copy()
+    for q in range(1, len(values)):
+        acc = acc + _as_f32(values[q])
+    return acc / np.float32(len(values))
 
 
 def reduce_scatter_sum(pl: Plan, grads) -> np.ndarray:

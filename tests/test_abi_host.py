@@ -1,0 +1,162 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/fsdp_hip.h declares, and its shapes-only plan agrees
+with the oracle's independently written layout."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fully_sharded_amd as F
+from oracle import fsdp_oracle as O
+from workloads.configs import WORKLOADS, shapes_of
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsdp_hip.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsdp_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "fsdp_plan_layout" in names and "fsdp_adamw_shard_step" in names
+    L = ctypes.CDLL(F.binding.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared but not exported"
+    for n in ("fsdp_plan_layout", "fsdp_shard_pack", "fsdp_gather_unflatten",
+              "fsdp_reduce_scatter_avg", "fsdp_adamw_shard_step"):
+        assert n in names
+
+
+def test_status_strings():
+    L = F.lib()
+    assert L.fsdp_status_string(0) == b"ok"
+    assert L.fsdp_status_string(-1) == b"invalid argument"
+
+
+def check_plan(shapes, R, layout):
+    po = O.plan_layout(shapes, R, layout)
+    pg = F.Plan(shapes, R, layout)
+    assert (pg.T, pg.S, pg.R, pg.n_params) == (po.T, po.S, R, len(shapes))
+    for p in range(len(shapes)):
+        q = pg.param(p)
+        assert q["flat_off"] == po.flat_off[p] and q["numel"] == po.numel[p]
+        assert q["rows_per_shard"] == po.k[p] and q["row_numel"] == po.row[p]
+        if layout == O.PER_PARAM:
+            assert q["shard_off"] == po.shard_off[p]
+    for r in range(R):
+        assert pg.rank_valid(r) == O.rank_valid(po, r)
+    # the segments are exactly the oracle's pieces (merged where contiguous)
+    seg = pg.segments()
+    merged = []
+    for r in range(R):
+        for f0, s0, n in po.pieces(r):
+            if n == 0:
+                continue
+            if merged and merged[-1][0] == r and merged[-1][1] + merged[-1][3] == s0 \
+                    and merged[-1][2] + merged[-1][3] == f0:
+                merged[-1] = (r, merged[-1][1], merged[-1][2], merged[-1][3] + n)
+            else:
+                merged.append((r, s0, f0, n))
+    assert seg == merged
+    for raf in (True, False):
+        assert pg.comm_ledger(raf) == O.comm_ledger(po, raf)
+    assert pg.state_bytes_per_rank() == O.state_bytes_per_rank(po)
+    if R * po.S > 1 << 22:
+        return
+    # and, expanded to elements, the same map as the oracle's
+    got = np.full((R, po.S), -1, np.int64)
+    for rank, s0, f0, n in seg:
+        assert n > 0 and 0 <= s0 and s0 + n <= po.S
+        got[rank, s0:s0 + n] = np.arange(f0, f0 + n)
+    want = np.full((R, po.S), -1, np.int64)
+    for r in range(R):
+        for f0, s0, n in po.pieces(r):
+            want[r, s0:s0 + n] = np.arange(f0, f0 + n)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_plan_matches_oracle_on_workloads(name):
+    wl = WORKLOADS[name]
+    check_plan(shapes_of(wl["units"][0]), wl["R"], wl["layout"])
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 7, 8, 16, 64])
+def test_plan_matches_oracle_on_random_tiny_shapes(R):
+    rng = np.random.default_rng(R)
+    for trial in range(30):
+        shapes = []
+        for _ in range(int(rng.integers(1, 6))):
+            nd = int(rng.integers(1, 4))
+            shapes.append((int(rng.integers(1, 2 * R + 2)),) +
+                          tuple(int(x) for x in rng.integers(1, 5, nd - 1)))
+        check_plan(shapes, R, O.PER_PARAM if trial % 2 else O.FLAT)
+
+
+def test_plan_rejects_bad_arguments():
+    L = F.lib()
+
+    def plan(shapes, R, layout, ndims=None):
+        nd = ndims if ndims is not None else [len(s) for s in shapes]
+        flat = [d for s in shapes for d in s] or [0]
+        h = ctypes.c_void_p(1234)
+        st = L.fsdp_plan_layout(len(nd), (ctypes.c_int32 * max(1, len(nd)))(*nd),
+                                (ctypes.c_int64 * len(flat))(*flat), R, layout, ctypes.byref(h))
+        if st == 0:
+            L.fsdp_plan_destroy(h)
+        else:
+            assert h.value is None
+        return st
+
+    assert plan([(4,)], 2, 0) == 0
+    assert plan([], 2, 0) == -1                 # no parameters
+    assert plan([(4,)], 0, 0) == -1             # R < 1
+    assert plan([(4,)], 65, 0) == -2            # R beyond the kernel argument limit
+    assert plan([(4,)], 2, 7) == -1             # unknown layout
+    assert plan([(0, 3)], 2, 0) == -1           # empty dimension
+    assert plan([(-2,)], 2, 1) == -1
+    assert plan([(4,)], 2, 0, ndims=[0]) == -1  # 0-d parameter
+    assert plan([(1,) * 9], 2, 0) == -1         # more than 8 dims
+    with pytest.raises(F.FsdpError):
+        F.Plan([(3,)], 100, "flat")
+
+
+def test_plan_queries_reject_bad_arguments():
+    pg = F.Plan([(5, 2)], 3, "per_param")
+    L = F.lib()
+    out = (ctypes.c_int64 * 5)()
+    assert L.fsdp_plan_param(pg.handle, 1, out) == -1
+    assert L.fsdp_plan_param(None, 0, out) == -1
+    v = ctypes.c_int64()
+    assert L.fsdp_plan_rank_valid(pg.handle, 3, ctypes.byref(v)) == -1
+    seg = (ctypes.c_int64 * 4)()
+    assert L.fsdp_plan_segments(pg.handle, seg, 0) == -1
+    assert L.fsdp_plan_state_bytes_per_rank(None) == -1
+
+
+def test_page_layout_pins_through_the_library():
+    """The FlatParameter offsets and per-GPU counts of the TransformerBlock
+    example, read back from the library's plan."""
+    from workloads.configs import LINEARS_512
+    fl = F.Plan(shapes_of(LINEARS_512), 4, "flat")
+    starts = sorted(f0 for _, _, f0, _ in fl.segments())
+    assert starts == [0, 786432, 1572864, 2359296] and fl.T == 3145728
+    pp = F.Plan(shapes_of(LINEARS_512), 4, "per_param")
+    assert pp.S == 786432
+    assert pp.comm_ledger(False)["all_gather"] * 2 == 4718592  # 3/4 of 6.3 MB fp16
+
+
+def test_product_code_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "fully_sharded_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in src.lower(), fn

@@ -1,0 +1,475 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: bit-exact for layout, pack, gather and reduce-scatter (fp32 sums in
+rank order); AdamW master, m and v within max|d| <= 1e-6 * max(1, |ref|);
+the bf16 recast within one bf16 ulp of the oracle's and exactly the RNE of
+the GPU's own master.  Inputs come from the seeded generators in workloads/.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fully_sharded_amd as F
+from oracle import fsdp_oracle as O
+from tests.gpu_util import (assert_adamw_close, assert_bf16_within_ulp, assert_bitexact,
+                            to_dev, to_host)
+from workloads import gen
+from workloads.configs import ADAMW, WORKLOADS, shapes_of
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["toy_2layer_r2", "block512_r4", "block512_flat_r4", "block512_r3", "block512_flat_r3"]
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    F.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def tdt(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def banner(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+# ------------------------------------------------- full step, small workloads
+@pytest.mark.parametrize("name", SMALL)
+def test_step_parity_small_workloads(name):
+    wl = WORKLOADS[name]
+    R = wl["R"]
+    banner(f"{name}: R={R} layout={wl['layout']}")
+    for u, unit in enumerate(wl["units"]):
+        shapes = shapes_of(unit)
+        po = O.plan_layout(shapes, R, wl["layout"])
+        pg = F.Plan(shapes, R, wl["layout"])
+        assert (pg.T, pg.S) == (po.T, po.S)
+        T, S = po.T, po.S
+        master_full = gen.host_master(wl, u, shapes)
+        full_d = to_dev(master_full)
+
+        # a2: pack the fp32 master exactly and the parameter with its recast
+        master_d = torch.empty(R * S, dtype=torch.float32, device=DEV)
+        F.fsdp_shard_pack(pg, full_d, master_d)
+        master_o = O.shard_pack(po, master_full)
+        assert_bitexact(to_host(master_d).reshape(R, S), master_o, "pack fp32")
+        pdt = wl["param_dtype"]
+        param_d = torch.empty(R * S, dtype=tdt(pdt), device=DEV)
+        F.fsdp_shard_pack(pg, full_d, param_d)
+        param_o = O.bf16_rne(master_o) if pdt == "bf16" else master_o.copy()
+        assert_bitexact(to_host(param_d).reshape(R, S), param_o, "pack+cast")
+        m_d = torch.zeros(R * S, dtype=torch.float32, device=DEV)
+        v_d = torch.zeros_like(m_d)
+        m_o = np.zeros((R, S), np.float32)
+        v_o = np.zeros((R, S), np.float32)
+
+        for t in range(1, wl["steps"] + 1):
+            # a3: all-gather + unflatten into R receivers
+            recv = [torch.empty(T, dtype=tdt(pdt), device=DEV) for _ in range(R)]
+            F.fsdp_gather_unflatten(pg, param_d, recv)
+            full_o, views_o = O.gather_unflatten(po, param_o)
+            for r in range(R):
+                got = to_host(recv[r])
+                if t == 1:
+                    assert_bitexact(got, full_o, f"gather step {t} recv {r}")
+                else:   # the parameters themselves may differ by an ulp here
+                    if pdt == "bf16":
+                        assert_bf16_within_ulp(got, full_o, "gather")
+                    else:
+                        assert_adamw_close(got, full_o, "gather")
+            for p, view in enumerate(pg.unflatten(recv[0])):
+                assert tuple(view.shape) == views_o[p].shape
+            # gather of the GPU's own shards round-trips through pack exactly
+            back = torch.empty_like(param_d)
+            F.fsdp_shard_pack(pg, recv[R - 1], back)
+            assert torch.equal(back.view(torch.int16) if pdt == "bf16" else back,
+                               param_d.view(torch.int16) if pdt == "bf16" else param_d)
+
+            grads = [gen.host_grad(wl, t, u, r, T) for r in range(R)]
+            g_d = [to_dev(g) for g in grads]
+            # a4: reduce-scatter-average
+            rs_d = torch.empty(R * S, dtype=torch.float32, device=DEV)
+            F.fsdp_reduce_scatter_avg(pg, g_d, rs_d)
+            assert_bitexact(to_host(rs_d).reshape(R, S), O.reduce_scatter_avg(po, grads), "rs")
+
+            # unfused AdamW on copies, for the fused/unfused identity below
+            mc, mmc, vvc = master_d.clone(), m_d.clone(), v_d.clone()
+            pc = torch.empty_like(param_d)
+            F.fsdp_adamw_shard_step(pg, ADAMW, t, rs_d, mc, mmc, vvc, pc, grads_are_replicas=False)
+
+            # a4+a5+a6 fused
+            F.fsdp_adamw_shard_step(pg, ADAMW, t, g_d, master_d, m_d, v_d, param_d)
+            master_o, m_o, v_o, param_o = O.shard_step(po, grads, master_o, m_o, v_o, t, ADAMW, pdt)
+            gm = to_host(master_d).reshape(R, S)
+            banner(f"{name} u={u} t={t}: master bit-exact fraction "
+                   f"{np.mean(gm.view(np.uint32) == master_o.view(np.uint32)):.9f}")
+            assert_adamw_close(gm, master_o, f"master t={t}")
+            assert_adamw_close(to_host(m_d).reshape(R, S), m_o, f"m t={t}")
+            assert_adamw_close(to_host(v_d).reshape(R, S), v_o, f"v t={t}")
+            gp = to_host(param_d).reshape(R, S)
+            if pdt == "bf16":
+                assert_bf16_within_ulp(gp, param_o, f"param t={t}")
+                assert_bitexact(gp, O.bf16_rne(gm), "param is RNE of the GPU master")
+            else:
+                assert_adamw_close(gp, param_o, f"param t={t}")
+                assert_bitexact(gp, gm, "fp32 param is the master")
+            # fused == RS then AdamW, bit for bit
+            assert_bitexact(to_host(mc), to_host(master_d), "fused vs unfused master")
+            assert_bitexact(to_host(mmc), to_host(m_d), "fused vs unfused m")
+            assert_bitexact(to_host(vvc), to_host(v_d), "fused vs unfused v")
+            assert_bitexact(to_host(pc), to_host(param_d), "fused vs unfused param")
+            # padding stays +0
+            pad = O.shard_pack(po, np.ones(T, np.float32)) == 0
+            for a in (gm, to_host(m_d).reshape(R, S), to_host(v_d).reshape(R, S)):
+                assert np.all(a[pad].view(np.uint32) == 0)
+
+
+# ------------------------------------------------ tiny ragged shapes, many R
+def random_shapes(rng, R):
+    shapes = []
+    for _ in range(int(rng.integers(1, 6))):
+        nd = int(rng.integers(1, 4))
+        d0 = int(rng.integers(1, 3 * R + 3))
+        shapes.append((d0,) + tuple(int(x) for x in rng.integers(1, 40, nd - 1)))
+    return shapes
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 13, 64])
+def test_tiny_ragged_shapes_all_ops(R):
+    rng = np.random.default_rng(1000 + R)
+    banner(f"tiny ragged R={R}")
+    for trial in range(12):
+        shapes = random_shapes(rng, R)
+        layout = O.FLAT if trial % 2 else O.PER_PARAM
+        gdt = "bf16" if trial % 3 else "f32"
+        pdt = "bf16" if trial % 4 != 1 else "f32"
+        po = O.plan_layout(shapes, R, layout)
+        pg = F.Plan(shapes, R, layout)
+        assert (pg.T, pg.S) == (po.T, po.S)
+        T, S = po.T, po.S
+        master_full = rng.uniform(-1, 1, T).astype(np.float32)
+        master_d = torch.empty(R * S, dtype=torch.float32, device=DEV)
+        F.fsdp_shard_pack(pg, to_dev(master_full), master_d)
+        master_o = O.shard_pack(po, master_full)
+        assert_bitexact(to_host(master_d).reshape(R, S), master_o, "pack")
+        p16 = O.bf16_rne(master_full)
+        sh16 = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+        F.fsdp_shard_pack(pg, to_dev(p16), sh16)
+        assert_bitexact(to_host(sh16).reshape(R, S), O.shard_pack(po, p16), "pack bf16")
+        recv = [torch.empty(T, dtype=torch.bfloat16, device=DEV) if r % 3 != 2 else None
+                for r in range(R)]
+        F.fsdp_gather_unflatten(pg, sh16, recv)
+        want, _ = O.gather_unflatten(po, O.shard_pack(po, p16))
+        for r in range(R):
+            if recv[r] is not None:
+                assert_bitexact(to_host(recv[r]), want, "gather")
+        grads = [(rng.standard_normal(T) * 1e-2).astype(np.float32) for _ in range(R)]
+        if gdt == "bf16":
+            grads = [O.bf16_rne(g) for g in grads]
+        g_d = [to_dev(g) for g in grads]
+        rs_d = torch.empty(R * S, dtype=torch.float32, device=DEV)
+        F.fsdp_reduce_scatter_avg(pg, g_d, rs_d)
+        assert_bitexact(to_host(rs_d).reshape(R, S), O.reduce_scatter_avg(po, grads), "rs")
+        m_d = torch.zeros_like(master_d)
+        v_d = torch.zeros_like(master_d)
+        m_o = np.zeros((R, S), np.float32)
+        v_o = np.zeros((R, S), np.float32)
+        param_d = torch.empty(R * S, dtype=tdt(pdt), device=DEV)
+        for t in (1, 2):
+            F.fsdp_adamw_shard_step(pg, ADAMW, t, g_d, master_d, m_d, v_d, param_d)
+            master_o, m_o, v_o, param_o = O.shard_step(po, grads, master_o, m_o, v_o, t, ADAMW, pdt)
+            assert_adamw_close(to_host(master_d).reshape(R, S), master_o, "master")
+            assert_adamw_close(to_host(m_d).reshape(R, S), m_o, "m")
+            assert_adamw_close(to_host(v_d).reshape(R, S), v_o, "v")
+            if pdt == "bf16":
+                assert_bf16_within_ulp(to_host(param_d).reshape(R, S), param_o, "param")
+
+
+def test_misaligned_base_pointers_take_the_scalar_path():
+    """Views offset by a few elements (not 16-byte aligned) give the same bits."""
+    banner("misaligned pointers")
+    rng = np.random.default_rng(5)
+    shapes = [(37, 11), (5,), (64, 8)]
+    R = 3
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+
+    def off_view(n, dtype, k):
+        base = torch.zeros(n + 16, dtype=dtype, device=DEV)
+        return base[k:k + n]
+
+    master_full = rng.uniform(-1, 1, T).astype(np.float32)
+    full_d = off_view(T, torch.float32, 1)
+    full_d.copy_(to_dev(master_full))
+    master_d = off_view(R * S, torch.float32, 3)
+    F.fsdp_shard_pack(pg, full_d, master_d)
+    master_o = O.shard_pack(po, master_full)
+    assert_bitexact(to_host(master_d).reshape(R, S), master_o, "pack misaligned")
+    grads = [O.bf16_rne((rng.standard_normal(T) * 1e-3).astype(np.float32)) for _ in range(R)]
+    g_d = []
+    for q, g in enumerate(grads):
+        x = off_view(T, torch.bfloat16, q + 1)
+        x.copy_(to_dev(g))
+        g_d.append(x)
+    rs_d = off_view(R * S, torch.float32, 1)
+    F.fsdp_reduce_scatter_avg(pg, g_d, rs_d)
+    assert_bitexact(to_host(rs_d).reshape(R, S), O.reduce_scatter_avg(po, grads), "rs misaligned")
+    m_d = off_view(R * S, torch.float32, 2)
+    v_d = off_view(R * S, torch.float32, 1)
+    p_d = off_view(R * S, torch.bfloat16, 5)
+    F.fsdp_adamw_shard_step(pg, ADAMW, 1, g_d, master_d, m_d, v_d, p_d)
+    mo, mm, vv, po16 = O.shard_step(po, grads, master_o, np.zeros((R, S), np.float32),
+                                     np.zeros((R, S), np.float32), 1, ADAMW, "bf16")
+    assert_adamw_close(to_host(master_d).reshape(R, S), mo, "master misaligned")
+    assert_bf16_within_ulp(to_host(p_d).reshape(R, S), po16, "param misaligned")
+    recv = [off_view(T, torch.bfloat16, r + 1) for r in range(R)]
+    F.fsdp_gather_unflatten(pg, p_d, recv)
+    want, _ = O.gather_unflatten(po, po16)
+    back = off_view(R * S, torch.bfloat16, 7)
+    F.fsdp_shard_pack(pg, recv[R - 1], back)
+    assert torch.equal(back.view(torch.int16), p_d.view(torch.int16))
+    for r in range(R):
+        assert_bf16_within_ulp(to_host(recv[r]), want, "gather misaligned")
+
+
+def test_nan_inf_and_signed_zero_propagate_like_the_oracle():
+    banner("nan/inf")
+    shapes = [(6, 4)]
+    R = 2
+    po = O.plan_layout(shapes, R, O.FLAT)
+    pg = F.Plan(shapes, R, O.FLAT)
+    T, S = po.T, po.S
+    g0 = np.zeros(T, np.float32)
+    g1 = np.zeros(T, np.float32)
+    g0[0], g1[0] = -0.0, -0.0
+    g0[1], g1[1] = -0.0, 0.0
+    g0[2] = np.nan
+    g0[3], g1[3] = np.inf, -np.inf
+    g0[4], g1[4] = np.inf, 1.0
+    g0[5], g1[5] = 3.4e38, 3.4e38
+    grads = [g0, g1]
+    g_d = [to_dev(g) for g in grads]
+    rs_d = torch.empty(R * S, dtype=torch.float32, device=DEV)
+    F.fsdp_reduce_scatter_avg(pg, g_d, rs_d)
+    got = to_host(rs_d).reshape(R, S)
+    want = O.reduce_scatter_avg(po, grads)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert_bitexact(np.where(nan, 0, got), np.where(nan, 0, want), "rs specials")
+    master = np.full((R, S), 0.5, np.float32)
+    master_d = to_dev(master.reshape(-1))
+    m_d = torch.zeros(R * S, device=DEV)
+    v_d = torch.zeros(R * S, device=DEV)
+    p_d = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_adamw_shard_step(pg, ADAMW, 1, g_d, master_d, m_d, v_d, p_d)
+    mo, mm, vv, pp = O.shard_step(po, grads, master, np.zeros_like(master), np.zeros_like(master),
+                                  1, ADAMW, "bf16")
+    assert_adamw_close(to_host(master_d).reshape(R, S), mo, "master specials")
+    assert_bf16_within_ulp(to_host(p_d).reshape(R, S), pp, "param specials")
+
+
+def test_repeat_runs_are_bit_identical():
+    banner("determinism")
+    wl = WORKLOADS["block512_r3"]
+    shapes = shapes_of(wl["units"][0])
+    pg = F.Plan(shapes, 3, "per_param")
+    T, S = pg.T, pg.S
+    grads = [gen.device_grad(wl, 1, 0, r, T, DEV) for r in range(3)]
+    outs = []
+    for _ in range(2):
+        master = gen.device_master(wl, 0, shapes, DEV)
+        md = torch.empty(3 * S, device=DEV)
+        F.fsdp_shard_pack(pg, master, md)
+        m = torch.zeros_like(md)
+        v = torch.zeros_like(md)
+        p = torch.empty(3 * S, dtype=torch.bfloat16, device=DEV)
+        for t in (1, 2, 3):
+            F.fsdp_adamw_shard_step(pg, ADAMW, t, grads, md, m, v, p)
+        outs.append((md, m, v, p.view(torch.int16)))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    banner("errors")
+    pg = F.Plan([(8, 4)], 2, "flat")
+    T, S = pg.T, pg.S
+    buf = torch.zeros(4 * T, device=DEV)
+    g = [buf[:T], buf[T:2 * T]]
+    with pytest.raises(F.FsdpError) as e:     # output overlaps an input
+        F.fsdp_reduce_scatter_avg(pg, g, buf[T // 2:T // 2 + 2 * S])
+    assert e.value.status == -1
+    master = torch.zeros(2 * S, device=DEV)
+    m = torch.zeros(2 * S, device=DEV)
+    p = torch.zeros(2 * S, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(F.FsdpError):          # step must be >= 1
+        F.fsdp_adamw_shard_step(pg, ADAMW, 0, g, master, m, buf[2 * T:2 * T + 2 * S], p)
+    with pytest.raises(F.FsdpError):          # eps must be > 0
+        F.fsdp_adamw_shard_step(pg, dict(ADAMW, eps=0.0), 1, g, master, m,
+                                buf[2 * T:2 * T + 2 * S], p)
+    with pytest.raises(F.FsdpError):          # m aliases master
+        F.fsdp_adamw_shard_step(pg, ADAMW, 1, g, master, master, buf[2 * T:2 * T + 2 * S], p)
+    with pytest.raises(F.FsdpError):          # two receivers are the same buffer
+        r = torch.zeros(T, dtype=torch.bfloat16, device=DEV)
+        F.fsdp_gather_unflatten(pg, p, [r, r])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(master) == 0 and torch.count_nonzero(p.float()) == 0
+
+
+# ------------------------------------------------------- full-size workloads
+def sample_positions(rng, R, S, k):
+    """Shard-space positions: random plus every rank's first/last element."""
+    r = rng.integers(0, R, k)
+    j = rng.integers(0, S, k)
+    edge_r = np.repeat(np.arange(R), 2)
+    edge_j = np.tile(np.array([0, S - 1]), R)
+    return np.concatenate([r, edge_r]), np.concatenate([j, edge_j])
+
+
+def flat_index(po, r, j):
+    """Oracle layout: flat index of shard position (r, j), -1 for padding."""
+    out = np.full(r.shape, -1, np.int64)
+    for rr in range(po.R):
+        sel = r == rr
+        for f0, s0, n in po.pieces(rr):
+            hit = sel & (j >= s0) & (j < s0 + n)
+            out[hit] = f0 + (j[hit] - s0)
+    return out
+
+
+def test_model12_r8_full_step_bench_launch_configuration():
+    """The 12-layer R=8 model, per step: gather(u) then fused(u) per unit,
+    as the benchmark times it; 3 steps.  Units 0 and 11 are checked whole,
+    the others on sampled elements."""
+    wl = WORKLOADS["model12_r8"]
+    R = wl["R"]
+    shapes = shapes_of(wl["units"][0])
+    po = O.plan_layout(shapes, R, wl["layout"])
+    pg = F.Plan(shapes, R, wl["layout"])
+    T, S = po.T, po.S
+    n_units = len(wl["units"])
+    banner(f"model12_r8: {n_units} units, T={T}, S={S}")
+    rng = np.random.default_rng(12)
+    rs_, js_ = sample_positions(rng, R, S, 4096)
+    fi = flat_index(po, rs_, js_)
+    valid = fi >= 0
+    state = []
+    oracle = []
+    for u in range(n_units):
+        full = gen.device_master(wl, u, shapes, DEV)
+        md = torch.empty(R * S, device=DEV)
+        F.fsdp_shard_pack(pg, full, md)
+        pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+        F.fsdp_shard_pack(pg, full, pd)
+        state.append([md, torch.zeros_like(md), torch.zeros_like(md), pd])
+        mo = O.shard_pack(po, to_host(full))
+        oracle.append([mo, np.zeros_like(mo), np.zeros_like(mo), O.bf16_rne(mo)])
+    recv = [torch.empty(T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    for t in range(1, wl["steps"] + 1):
+        for u in range(n_units):
+            md, m, v, pd = state[u]
+            F.fsdp_gather_unflatten(pg, pd, recv)
+            if u in (0, n_units - 1):
+                want, _ = O.gather_unflatten(po, oracle[u][3])
+                got = to_host(recv[3])
+                if t == 1:
+                    assert_bitexact(got, want, f"gather u={u}")
+                else:
+                    assert_bf16_within_ulp(got, want, f"gather u={u}")
+            grads = [gen.device_grad(wl, t, u, r, T, DEV) for r in range(R)]
+            F.fsdp_adamw_shard_step(pg, ADAMW, t, grads, md, m, v, pd)
+            o = oracle[u]
+            if u in (0, n_units - 1):
+                hg = [to_host(g) for g in grads]
+                o[0], o[1], o[2], o[3] = O.shard_step(po, hg, o[0], o[1], o[2], t, ADAMW, "bf16")
+                gm = to_host(md).reshape(R, S)
+                assert_adamw_close(gm, o[0], f"master u={u} t={t}")
+                assert_adamw_close(to_host(m).reshape(R, S), o[1], f"m u={u}")
+                assert_adamw_close(to_host(v).reshape(R, S), o[2], f"v u={u}")
+                gp = to_host(pd).reshape(R, S)
+                assert_bf16_within_ulp(gp, o[3], f"param u={u}")
+                assert_bitexact(gp, O.bf16_rne(gm), "param = RNE(master)")
+            else:
+                # sampled: the oracle steps only the sampled elements
+                gs = [to_host(g[torch.from_numpy(fi[valid]).to(DEV)]) for g in grads]
+                avg = np.zeros(rs_.shape, np.float32)
+                avg[valid] = O.rank_order_mean(gs)
+                p0, m0, v0 = (o[0][rs_, js_], o[1][rs_, js_], o[2][rs_, js_])
+                p1, m1, v1 = O.adamw_step(p0, m0, v0, avg, t, **ADAMW)
+                o[0][rs_, js_], o[1][rs_, js_], o[2][rs_, js_] = p1, m1, v1
+                idx = torch.from_numpy(rs_ * S + js_).to(DEV)
+                assert_adamw_close(to_host(md[idx]), p1, f"master u={u} sampled")
+                assert_adamw_close(to_host(m[idx]), m1, f"m u={u} sampled")
+                assert_adamw_close(to_host(v[idx]), v1, f"v u={u} sampled")
+                assert_bf16_within_ulp(to_host(pd[idx]), O.bf16_rne(p1), f"param u={u} sampled")
+        banner(f"model12_r8 step {t} ok")
+    for r in range(1, R):
+        assert torch.equal(recv[0].view(torch.int16), recv[r].view(torch.int16))
+
+
+def test_group4096_flat_r8_full_size_sampled():
+    """The 4-block hidden-4096 group (872,448,000 parameters) as one FSDP1
+    FlatParameter at R=8, at full size: pack, gather and 3 fused steps,
+    checked on sampled elements against the oracle."""
+    wl = WORKLOADS["group4096_flat_r8"]
+    R = wl["R"]
+    shapes = shapes_of(wl["units"][0])
+    po = O.plan_layout(shapes, R, wl["layout"])
+    pg = F.Plan(shapes, R, wl["layout"])
+    T, S = po.T, po.S
+    banner(f"group4096_flat_r8: T={T} S={S}")
+    rng = np.random.default_rng(4096)
+    rs_, js_ = sample_positions(rng, R, S, 65536)
+    # also the parameter boundaries
+    bnd = np.array([po.flat_off[p] + d for p in range(len(shapes)) for d in (0, -1) if
+                    0 <= po.flat_off[p] + d < T])
+    rs_ = np.concatenate([rs_, bnd // S])
+    js_ = np.concatenate([js_, bnd % S])
+    fi = flat_index(po, rs_, js_)
+    assert np.all(fi >= 0)  # no padding at this size
+    fi_d = torch.from_numpy(fi).to(DEV)
+    idx = torch.from_numpy(rs_ * S + js_).to(DEV)
+
+    full = gen.device_master(wl, 0, shapes, DEV)
+    master_s = to_host(full[fi_d])
+    md = torch.empty(R * S, device=DEV)
+    F.fsdp_shard_pack(pg, full, md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_shard_pack(pg, full, pd)
+    del full
+    assert_bitexact(to_host(md[idx]), master_s, "pack sampled")
+    assert_bitexact(to_host(pd[idx]), O.bf16_rne(master_s), "pack+cast sampled")
+    recv = [torch.empty(T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    F.fsdp_gather_unflatten(pg, pd, recv)
+    for r in range(R):
+        assert_bitexact(to_host(recv[r][fi_d]), O.bf16_rne(master_s), f"gather sampled {r}")
+    for r in range(1, R):
+        assert torch.equal(recv[0].view(torch.int16), recv[r].view(torch.int16))
+    del recv
+    torch.cuda.empty_cache()
+    m = torch.zeros_like(md)
+    v = torch.zeros_like(md)
+    p0 = master_s
+    m0 = np.zeros_like(p0)
+    v0 = np.zeros_like(p0)
+    for t in range(1, wl["steps"] + 1):
+        grads = [gen.device_grad(wl, t, 0, r, T, DEV) for r in range(R)]
+        F.fsdp_adamw_shard_step(pg, ADAMW, t, grads, md, m, v, pd)
+        gs = [to_host(g[fi_d]) for g in grads]
+        del grads
+        p0, m0, v0 = O.adamw_step(p0, m0, v0, O.rank_order_mean(gs), t, **ADAMW)
+        assert_adamw_close(to_host(md[idx]), p0, f"master t={t}")
+        assert_adamw_close(to_host(m[idx]), m0, f"m t={t}")
+        assert_adamw_close(to_host(v[idx]), v0, f"v t={t}")
+        gp = to_host(pd[idx])
+        assert_bf16_within_ulp(gp, O.bf16_rne(p0), f"param t={t}")
+        assert_bitexact(gp, O.bf16_rne(to_host(md[idx])), "param = RNE(master)")
+        banner(f"group4096 step {t} ok")
