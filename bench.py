@@ -16,6 +16,7 @@ launches, and the CPU oracle timed on a bounded sample on the host.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -99,37 +100,40 @@ def main():
             plans[shapes].prepare()
         pl = plans[shapes]
         full = gen.device_master(wl, u, list(shapes), dev)
-        master = torch.empty(R * pl.S, dtype=torch.float32, device=dev)
+        # master, m and v of a unit's shards share one buffer (bases that
+        # differ by large powers of two would alias the same HBM channels)
+        opt = torch.zeros(3, R * pl.S, dtype=torch.float32, device=dev)
+        master, m, v = opt.unbind(0)
         F.fsdp_shard_pack(pl, full, master)
         param = torch.empty(R * pl.S, dtype=pdt, device=dev)
         F.fsdp_shard_pack(pl, full, param)
         del full
-        grads = [gen.device_grad(wl, 1, u, r, pl.T, dev) for r in range(R)]
-        state.append(dict(plan=pl, master=master, m=torch.zeros_like(master),
-                          v=torch.zeros_like(master), param=param, grads=grads))
+        # the R gradient replicas of a unit live in one [R, T] buffer
+        gbuf = torch.empty(R, pl.T, dtype=gdt, device=dev)
+        for r in range(R):
+            gbuf[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
+        grads = list(gbuf.unbind(0))
+        state.append(dict(plan=pl, master=master, m=m, v=v, param=param, grads=grads))
     T_max = max(p.T for p in plans.values())
-    recv = [torch.empty(T_max, dtype=pdt, device=dev) for _ in range(R)]
+    recv = list(torch.empty(R, T_max, dtype=pdt, device=dev).unbind(0))
+    # library calls with their arguments marshalled once (the loop below
+    # only passes the step and the stream)
+    calls = [(F.bind_gather_unflatten(s["plan"], s["param"], recv),
+              F.bind_adamw_shard_step(s["plan"], ADAMW, s["grads"], s["master"], s["m"], s["v"],
+                                      s["param"])) for s in state]
+    hs = ctypes.c_void_p(stream.cuda_stream)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     P = sum(s["plan"].T for s in state)
 
     step_no = [0]
 
-    def step(events=None):
+    def step():
         step_no[0] += 1
         t = step_no[0]
-        for i, s in enumerate(state):
-            pl = s["plan"]
-            outs = [x[:pl.T] for x in recv]
-            if events is not None:
-                events[i][0].record(stream)
-            F.fsdp_gather_unflatten(pl, s["param"], outs)
-            if events is not None:
-                events[i][1].record(stream)
-            F.fsdp_adamw_shard_step(pl, ADAMW, t, s["grads"], s["master"], s["m"], s["v"],
-                                    s["param"])
-            if events is not None:
-                events[i][2].record(stream)
+        for gather, fused in calls:
+            gather(hs)
+            fused(t, hs)
 
     for _ in range(args.warmup):
         step()
@@ -148,18 +152,33 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # ------------------ per-kernel durations: HIP events around every launch
-    n_inst = max(10, min(args.steps, 50))
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in state]
-          for _ in range(n_inst)]
-    torch.cuda.synchronize()
-    for k in range(n_inst):
-        step(ev[k])
-    torch.cuda.synchronize()
-    gather_ms = np.array([[ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(len(state))]
-                          for k in range(n_inst)])
-    fused_ms = np.array([[ev[k][i][1].elapsed_time(ev[k][i][2]) for i in range(len(state))]
-                         for k in range(n_inst)])
+    # ------------- per-kernel durations: HIP events around back-to-back runs
+    # of one kernel over all units (an event between every launch would add
+    # its own few microseconds to each)
+    reps = max(5, args.steps // 4)
+
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * len(calls))
+
+    def fused_pass():
+        step_no[0] += 1
+        for _, fused in calls:
+            fused(step_no[0], hs)
+
+    def gather_pass():
+        for gather, _ in calls:
+            gather(hs)
+
+    fused_avg_ms = timed(fused_pass)
+    gather_avg_ms = timed(gather_pass)
 
     # algorithmic bytes (valid parameters only, padding excluded)
     fused_bytes_unit = [s["plan"].T * (2 * R + 26) if gdt == torch.bfloat16 else
@@ -167,10 +186,8 @@ def main():
     pes = 2 if pdt == torch.bfloat16 else 4
     gather_bytes_unit = [s["plan"].T * (pes + pes * R) for s in state]
     step_bytes = sum(fused_bytes_unit) + sum(gather_bytes_unit)
-    fused_avg_ms = float(fused_ms.mean())
     fused_bytes = float(np.mean(fused_bytes_unit))
     achieved = fused_bytes / (fused_avg_ms * 1e-3) / 1e9
-    gather_avg_ms = float(gather_ms.mean())
     gather_gbps = float(np.mean(gather_bytes_unit)) / (gather_avg_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = load_traffic(args.workload)
@@ -231,7 +248,7 @@ def main():
             "fused_rs_adamw": {"avg_ms": fused_avg_ms, "bytes": fused_bytes, "gbps": achieved},
             "gather_unflatten": {"avg_ms": gather_avg_ms,
                                  "bytes": float(np.mean(gather_bytes_unit)), "gbps": gather_gbps},
-            "event_launches": int(fused_ms.size),
+            "timed_launches_each": reps * len(calls),
         },
         "roofline": {
             "bound": "hbm",
@@ -252,11 +269,14 @@ def main():
 
 def cpu_baseline(state, R, wl, budget_s):
     """The oracle, as it stands, on the same inputs (copied back to the host):
-    per unit, R gathers (one per receiving rank) then the shard step, units
-    in order until about budget_s seconds of CPU work."""
+    per unit, R gathers (one per receiving rank) then the shard step; units in
+    order, step after step, until about budget_s seconds of CPU work."""
+    import platform
+
     import numpy as np
 
     from oracle import fsdp_oracle as O
+    from workloads.configs import ADAMW
 
     def host(t):
         import torch
@@ -264,32 +284,36 @@ def cpu_baseline(state, R, wl, budget_s):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
-    hp = {k: wl_hp for k, wl_hp in __import__("workloads.configs", fromlist=["ADAMW"]).ADAMW.items()}
-    done = 0
-    secs = 0.0
-    units = 0
     plans = {}
-    for i, s in enumerate(state):
+    units = []
+    for s in state:
         pl = s["plan"]
         key = tuple(pl.shapes)
         if key not in plans:
             plans[key] = O.plan_layout(list(pl.shapes), R, wl["layout"])
         po = plans[key]
-        grads = [host(g) for g in s["grads"]]
-        master = host(s["master"]).reshape(R, po.S).copy()
-        m = host(s["m"]).reshape(R, po.S).copy()
-        v = host(s["v"]).reshape(R, po.S).copy()
-        param = host(s["param"]).reshape(R, po.S).copy()
-        t0 = time.perf_counter()
-        for _ in range(R):
-            O.gather_unflatten(po, param)
-        O.shard_step(po, grads, master, m, v, 1, hp, wl["param_dtype"])
-        secs += time.perf_counter() - t0
-        done += po.T
-        units += 1
-        if secs >= budget_s:
-            break
-    import platform
+        units.append(dict(po=po, grads=[host(g) for g in s["grads"]],
+                          master=host(s["master"]).reshape(R, po.S).copy(),
+                          m=np.zeros((R, po.S), np.float32), v=np.zeros((R, po.S), np.float32),
+                          param=host(s["param"]).reshape(R, po.S).copy()))
+    done = 0
+    secs = 0.0
+    unit_steps = 0
+    t = 0
+    while secs < budget_s and t < 1000:
+        t += 1
+        for u in units:
+            po = u["po"]
+            t0 = time.perf_counter()
+            for _ in range(R):
+                O.gather_unflatten(po, u["param"])
+            u["master"], u["m"], u["v"], u["param"] = O.shard_step(
+                po, u["grads"], u["master"], u["m"], u["v"], t, ADAMW, wl["param_dtype"])
+            secs += time.perf_counter() - t0
+            done += po.T
+            unit_steps += 1
+            if secs >= budget_s:
+                break
     cpu_model = platform.processor()
     try:
         with open("/proc/cpuinfo") as f:
@@ -304,9 +328,10 @@ def cpu_baseline(state, R, wl, budget_s):
         "unit": "params/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{units} of {len(state)} units of one step (R={R}: {R} gathers + "
-                  f"reduce-scatter-average + AdamW + recast per unit), {done} params, "
-                  f"{secs:.2f} s; NumPy element-wise on one thread; {cpu_model}",
+        "sample": f"{unit_steps} unit-steps over {t} step(s) of the {len(state)}-unit model "
+                  f"(per unit: {R} gathers + reduce-scatter-average + AdamW + recast), "
+                  f"{done} params in {secs:.2f} s; NumPy element-wise ops, one thread; "
+                  f"{cpu_model}",
     }
 
 

@@ -6,6 +6,7 @@ fsdp_plan_layout, fsdp_shard_pack, fsdp_gather_unflatten,
 fsdp_reduce_scatter_avg, fsdp_adamw_shard_step.
 """
 from .binding import (  # noqa: F401
-    BF16, F32, FLAT, PER_PARAM, FsdpError, Plan, fsdp_adamw_shard_step,
+    BF16, F32, FLAT, PER_PARAM, FsdpError, Plan, bind_adamw_shard_step, bind_gather_unflatten,
+    fsdp_adamw_shard_step,
     fsdp_gather_unflatten, fsdp_plan_layout, fsdp_reduce_scatter_avg, fsdp_shard_pack, lib,
 )

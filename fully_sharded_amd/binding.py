@@ -115,8 +115,12 @@ def _dev(t: torch.Tensor, what: str) -> int:
 
 
 def _stream(stream):
+    """hipStream_t argument: torch's current stream by default; a torch
+    stream, or an already converted ctypes.c_void_p, otherwise."""
     if stream is None:
         stream = torch.cuda.current_stream()
+    if isinstance(stream, ctypes.c_void_p):
+        return stream
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -269,3 +273,66 @@ def fsdp_adamw_shard_step(plan: Plan, hp: dict, step: int, grads, master, m, v, 
                                        int(bool(grads_are_replicas)), _dev(master, "master"),
                                        _dev(m, "m"), _dev(v, "v"), _dev(param_out, "param_out"),
                                        _dtype_code(param_out), _stream(stream)))
+
+
+class BoundCall:
+    """A library call with its pointer arguments marshalled once.
+
+    For hot loops: the tensors are checked and their pointers cached at
+    construction; calling the object only passes the cached arguments (plus
+    the current stream and, for AdamW, the step) to the library."""
+
+    def __init__(self, fn_name, args, keep):
+        self._fn = getattr(lib(), fn_name)
+        self._name = fn_name
+        self._args = args
+        self._keep = keep   # tensors whose memory the cached pointers refer to
+
+    def _run(self, *args):
+        _check(self._name, self._fn(*args))
+
+
+def bind_gather_unflatten(plan: Plan, shards: torch.Tensor, full_out) -> "BoundCall":
+    """fsdp_gather_unflatten with cached arguments; call as f(stream=None)."""
+    if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
+        raise ValueError("size mismatch with the plan")
+    for t in full_out:
+        if t is not None and (t.numel() < plan.T or t.dtype != shards.dtype):
+            raise ValueError("receiver size or dtype mismatch")
+    arr = _ptr_array(full_out, "full_out")
+    call = BoundCall("fsdp_gather_unflatten",
+                     (plan.handle, ctypes.c_void_p(_dev(shards, "shards")),
+                      _dtype_code(shards), arr), (plan, shards, list(full_out)))
+
+    def run(stream=None):
+        call._run(*call._args, _stream(stream))
+    run.call = call
+    return run
+
+
+def bind_adamw_shard_step(plan: Plan, hp: dict, grads, master, m, v, param_out):
+    """fsdp_adamw_shard_step (fused, R gradient replicas) with cached
+    arguments; call as f(step, stream=None)."""
+    n = plan.R * plan.S
+    for t, nm in ((master, "master"), (m, "m"), (v, "v")):
+        if t.numel() != n or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be fp32 with R*S elements")
+    if param_out.numel() != n or len(grads) != plan.R:
+        raise ValueError("size mismatch with the plan")
+    dt = _dtype_code(grads[0])
+    for g in grads:
+        if g.numel() != plan.T or _dtype_code(g) != dt:
+            raise ValueError("gradient size or dtype mismatch")
+    arr = _ptr_array(grads, "grads")
+    h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    head = (plan.handle, ctypes.byref(h))
+    tail = (arr, dt, 1, ctypes.c_void_p(_dev(master, "master")), ctypes.c_void_p(_dev(m, "m")),
+            ctypes.c_void_p(_dev(v, "v")), ctypes.c_void_p(_dev(param_out, "param_out")),
+            _dtype_code(param_out))
+    call = BoundCall("fsdp_adamw_shard_step", None,
+                     (plan, h, list(grads), master, m, v, param_out))
+
+    def run(step, stream=None):
+        call._run(*head, int(step), *tail, _stream(stream))
+    run.call = call
+    return run

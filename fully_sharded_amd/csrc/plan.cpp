@@ -17,13 +17,14 @@
 namespace fsdp {
 namespace {
 
-// Elements one workgroup handles at most.  A workgroup is 256 lanes of 8
-// elements per pass; small units keep one pass per workgroup so that a
-// 3M-element unit still spreads over ~1500 workgroups (>> 256 CUs), large
-// ones give each workgroup up to 16 passes to amortise its start-up.
-int64_t pick_chunk(int64_t total) {
-  int64_t c = 2048;
-  while (c < 32768 && total / c > 4096) c *= 2;
+// Elements one workgroup handles at most: one pass of its 256 lanes
+// (`pass` elements: 1024 for the 4-element lanes of the arithmetic kernels,
+// 2048 for the 16-byte lanes of the bf16 copy) while that still gives a few
+// thousand workgroups (>> 256 CUs), up to 16 passes on large units to
+// amortise workgroup start-up.
+int64_t pick_chunk(int64_t total, int64_t pass) {
+  int64_t c = pass;
+  while (c < 16 * pass && total / c > 4096) c *= 2;
   return c;
 }
 
@@ -126,7 +127,7 @@ fsdp_status build_plan(fsdp_plan* pl) {
       push_run(runs, r * pl->S + pos, -1, pl->S - pos);
     }
   }
-  pl->shard_chunk = pick_chunk(R * pl->S);
+  pl->shard_chunk = pick_chunk(R * pl->S, 1024);
   for (const Work& w : runs) emit(pl->shard_work, w.dst, w.src, w.len, pl->shard_chunk);
 
   // flat-space runs: the same segments ordered by flat offset; they tile
@@ -142,7 +143,7 @@ fsdp_status build_plan(fsdp_plan* pl) {
     expect += s.len;
   }
   if (expect != pl->T) return FSDP_ERR_INVALID_ARG;
-  pl->flat_chunk = pick_chunk(pl->T);
+  pl->flat_chunk = pick_chunk(pl->T, 2048);
   for (const Work& w : runs) emit(pl->flat_work, w.dst, w.src, w.len, pl->flat_chunk);
   return FSDP_OK;
 }
