@@ -41,6 +41,10 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json "
+                         "and exit (no GPU needed)")
     return ap.parse_args()
 
 
@@ -65,8 +69,71 @@ def load_traffic(workload):
     return tr.get("fused_bytes_per_launch")
 
 
+def rows(n_rows, n, dtype, device):
+    """n_rows tensors of n elements carved from one buffer.  The row stride
+    is n rounded up to 256 bytes, plus 256 bytes when it would be a multiple
+    of 4 KiB: rows whose bases differ by large powers of two put the same
+    offsets on the same HBM channels at the same time."""
+    import torch
+    es = torch.empty(0, dtype=dtype).element_size()
+    stride = -(-n * es // 256) * 256
+    if stride % 4096 == 0:
+        stride += 256
+    buf = torch.empty(n_rows * stride // es, dtype=dtype, device=device)
+    return [buf[i * stride // es:i * stride // es + n] for i in range(n_rows)]
+
+
+def summarise_counters(fetch_csv, write_csv, workload):
+    """HBM bytes per fused launch from the FETCH_SIZE and WRITE_SIZE counters
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    1 GiB plain copy of --calibrate-copy (1 GiB read, 1 GiB written)."""
+    import csv
+
+    def load(path, counter):
+        fused, copy = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                if "k_fused" in name:
+                    fused.append(float(r["Counter_Value"]))
+                elif "copy" in name.lower() and "fsdp" not in name:
+                    copy.append(float(r["Counter_Value"]))
+        if not fused or not copy:
+            raise SystemExit(f"{path}: no fused or calibration-copy dispatches for {counter}")
+        return sum(fused) / len(fused), max(copy)
+
+    gib_kib = float(1 << 20)
+    fetch, fetch_copy = load(fetch_csv, "FETCH_SIZE")
+    write, write_copy = load(write_csv, "WRITE_SIZE")
+    fs = gib_kib / fetch_copy
+    ws = gib_kib / write_copy
+    traffic = (fetch * fs + write * ws) * 1024.0
+    out = {
+        "workload": workload,
+        "kernel": "k_fused (fused reduce-scatter-average + AdamW + bf16 recast)",
+        "kernel_src_sha": kernel_src_hash(),
+        "fetch_kib_per_launch": fetch,
+        "write_kib_per_launch": write,
+        "calibration_copy_kib": {"FETCH_SIZE": fetch_copy, "WRITE_SIZE": write_copy,
+                                 "true_kib_each_way": gib_kib},
+        "fetch_scale": fs,
+        "write_scale": ws,
+        "fused_bytes_per_launch": traffic,
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.counters:
+        summarise_counters(args.counters[0], args.counters[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the R ranks are virtual ranks in one GPU's "
               f"memory and this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -102,20 +169,20 @@ def main():
         full = gen.device_master(wl, u, list(shapes), dev)
         # master, m and v of a unit's shards share one buffer (bases that
         # differ by large powers of two would alias the same HBM channels)
-        opt = torch.zeros(3, R * pl.S, dtype=torch.float32, device=dev)
-        master, m, v = opt.unbind(0)
+        master, m, v = rows(3, R * pl.S, torch.float32, dev)
+        m.zero_()
+        v.zero_()
         F.fsdp_shard_pack(pl, full, master)
         param = torch.empty(R * pl.S, dtype=pdt, device=dev)
         F.fsdp_shard_pack(pl, full, param)
         del full
-        # the R gradient replicas of a unit live in one [R, T] buffer
-        gbuf = torch.empty(R, pl.T, dtype=gdt, device=dev)
+        # the R gradient replicas of a unit live in one buffer
+        grads = rows(R, pl.T, gdt, dev)
         for r in range(R):
-            gbuf[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
-        grads = list(gbuf.unbind(0))
+            grads[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
         state.append(dict(plan=pl, master=master, m=m, v=v, param=param, grads=grads))
     T_max = max(p.T for p in plans.values())
-    recv = list(torch.empty(R, T_max, dtype=pdt, device=dev).unbind(0))
+    recv = rows(R, T_max, pdt, dev)
     # library calls with their arguments marshalled once (the loop below
     # only passes the step and the stream)
     calls = [(F.bind_gather_unflatten(s["plan"], s["param"], recv),
@@ -284,6 +351,8 @@ def cpu_baseline(state, R, wl, budget_s):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
+    if max(s["plan"].T for s in state) * R > (1 << 26):
+        return None   # the oracle copies whole units to the host: too large here
     plans = {}
     units = []
     for s in state:

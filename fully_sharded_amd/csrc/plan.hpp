@@ -52,7 +52,7 @@ struct fsdp_plan {
   std::vector<fsdp::Segment> segments;      // ordered by (rank, shard_off)
   std::vector<fsdp::Work> shard_work;       // covers [0, R*S) in order
   std::vector<fsdp::Work> flat_work;        // covers [0, T) in order
-  int64_t shard_chunk = 0;                  // max elements per workgroup
+  int64_t shard_chunk = 0;                  // max elements per work item
   int64_t flat_chunk = 0;
 
   mutable std::mutex mu;
