@@ -36,6 +36,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="model12_r8")
+    ap.add_argument("--schedule", choices=("serial", "prefetch"), default="serial",
+                    help="serial: per unit gather then fused step on one stream; prefetch: "
+                         "gathers on their own stream run ahead of the fused steps, into a "
+                         "double receive buffer")
+    ap.add_argument("--gathers-per-step", type=int, choices=(1, 2), default=1,
+                    help="1: parameters kept from forward to backward "
+                         "(reshard_after_forward=False); 2: freed after forward and "
+                         "gathered again in backward (reshard_after_forward=True)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -144,12 +152,12 @@ def main():
     import torch
 
     import fully_sharded_amd as F
+    from fully_sharded_amd.step import StepRunner, Unit
     from workloads import gen
     from workloads.configs import ADAMW, WORKLOADS, shapes_of
 
     wl = WORKLOADS[args.workload]
     R = wl["R"]
-    units = wl["units"]
     dev = "cuda"
     torch.cuda.init()
     stream = torch.cuda.current_stream()
@@ -158,17 +166,15 @@ def main():
 
     # ---------------------------------------------------------------- set-up
     plans = {}
-    state = []
+    units = []
     t_setup = time.perf_counter()
-    for u, unit in enumerate(units):
+    for u, unit in enumerate(wl["units"]):
         shapes = tuple(shapes_of(unit))
         if shapes not in plans:
             plans[shapes] = F.Plan(list(shapes), R, wl["layout"])
             plans[shapes].prepare()
         pl = plans[shapes]
         full = gen.device_master(wl, u, list(shapes), dev)
-        # master, m and v of a unit's shards share one buffer (bases that
-        # differ by large powers of two would alias the same HBM channels)
         master, m, v = rows(3, R * pl.S, torch.float32, dev)
         m.zero_()
         v.zero_()
@@ -176,31 +182,24 @@ def main():
         param = torch.empty(R * pl.S, dtype=pdt, device=dev)
         F.fsdp_shard_pack(pl, full, param)
         del full
-        # the R gradient replicas of a unit live in one buffer
         grads = rows(R, pl.T, gdt, dev)
         for r in range(R):
             grads[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
-        state.append(dict(plan=pl, master=master, m=m, v=v, param=param, grads=grads))
+        units.append(Unit(pl, master, m, v, param, grads))
     T_max = max(p.T for p in plans.values())
-    recv = rows(R, T_max, pdt, dev)
-    # library calls with their arguments marshalled once (the loop below
-    # only passes the step and the stream)
-    calls = [(F.bind_gather_unflatten(s["plan"], s["param"], recv),
-              F.bind_adamw_shard_step(s["plan"], ADAMW, s["grads"], s["master"], s["m"], s["v"],
-                                      s["param"])) for s in state]
-    hs = ctypes.c_void_p(stream.cuda_stream)
+    n_recv = 2 if args.schedule == "prefetch" else 1
+    recv = [rows(R, T_max, pdt, dev) for _ in range(n_recv)]
+    runner = StepRunner(units, ADAMW, recv, schedule=args.schedule,
+                        gathers_per_step=args.gathers_per_step)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
-    P = sum(s["plan"].T for s in state)
+    P = sum(u.plan.T for u in units)
 
     step_no = [0]
 
     def step():
         step_no[0] += 1
-        t = step_no[0]
-        for gather, fused in calls:
-            gather(hs)
-            fused(t, hs)
+        runner.step(step_no[0])
 
     for _ in range(args.warmup):
         step()
@@ -221,8 +220,9 @@ def main():
 
     # ------------- per-kernel durations: HIP events around back-to-back runs
     # of one kernel over all units (an event between every launch would add
-    # its own few microseconds to each)
+    # its own few microseconds to each), on the stream the kernels run on
     reps = max(5, args.steps // 4)
+    hs = ctypes.c_void_p(stream.cuda_stream)
 
     def timed(fn):
         a = torch.cuda.Event(enable_timing=True)
@@ -233,26 +233,26 @@ def main():
             fn()
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / (reps * len(calls))
+        return a.elapsed_time(b) / (reps * len(units))
 
     def fused_pass():
         step_no[0] += 1
-        for _, fused in calls:
+        for _, fused in runner.calls:
             fused(step_no[0], hs)
 
     def gather_pass():
-        for gather, _ in calls:
+        for gather, _ in runner.calls:
             gather(hs)
 
     fused_avg_ms = timed(fused_pass)
     gather_avg_ms = timed(gather_pass)
 
     # algorithmic bytes (valid parameters only, padding excluded)
-    fused_bytes_unit = [s["plan"].T * (2 * R + 26) if gdt == torch.bfloat16 else
-                        s["plan"].T * (4 * R + 26) for s in state]
+    ges = 2 if gdt == torch.bfloat16 else 4
     pes = 2 if pdt == torch.bfloat16 else 4
-    gather_bytes_unit = [s["plan"].T * (pes + pes * R) for s in state]
-    step_bytes = sum(fused_bytes_unit) + sum(gather_bytes_unit)
+    fused_bytes_unit = [u.plan.T * (ges * R + 24 + pes) for u in units]
+    gather_bytes_unit = [u.plan.T * (pes + pes * R) for u in units]
+    step_bytes = sum(fused_bytes_unit) + args.gathers_per_step * sum(gather_bytes_unit)
     fused_bytes = float(np.mean(fused_bytes_unit))
     achieved = fused_bytes / (fused_avg_ms * 1e-3) / 1e9
     gather_gbps = float(np.mean(gather_bytes_unit)) / (gather_avg_ms * 1e-3) / 1e9
@@ -281,7 +281,7 @@ def main():
     # ------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(state, R, wl, args.cpu_seconds)
+        cpu = cpu_baseline(units, R, wl, args.cpu_seconds)
 
     line = {
         "metric": "shard-step params/s and achieved HBM GB/s (% of peak), 12-layer R=8",
@@ -305,7 +305,9 @@ def main():
             "param_dtype": wl["param_dtype"],
             "grad_dtype": wl["grad_dtype"],
             "state_dtype": "f32",
-            "launches_per_step": 2 * len(units),
+            "schedule": args.schedule,
+            "gathers_per_step": args.gathers_per_step,
+            "launches_per_step": (args.gathers_per_step + 1) * len(units),
             "step": "per unit: gather+unflatten to R receivers, fused RS-avg+AdamW+recast",
         },
         "hbm_gbps": step_gbps,
@@ -315,8 +317,9 @@ def main():
             "fused_rs_adamw": {"avg_ms": fused_avg_ms, "bytes": fused_bytes, "gbps": achieved},
             "gather_unflatten": {"avg_ms": gather_avg_ms,
                                  "bytes": float(np.mean(gather_bytes_unit)), "gbps": gather_gbps},
-            "timed_launches_each": reps * len(calls),
+            "timed_launches_each": reps * len(units),
         },
+        "memory_ledger_per_rank": runner.memory_ledger(pes),
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
@@ -351,20 +354,20 @@ def cpu_baseline(state, R, wl, budget_s):
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
-    if max(s["plan"].T for s in state) * R > (1 << 26):
+    if max(u.plan.T for u in state) * R > (1 << 26):
         return None   # the oracle copies whole units to the host: too large here
     plans = {}
     units = []
     for s in state:
-        pl = s["plan"]
+        pl = s.plan
         key = tuple(pl.shapes)
         if key not in plans:
             plans[key] = O.plan_layout(list(pl.shapes), R, wl["layout"])
         po = plans[key]
-        units.append(dict(po=po, grads=[host(g) for g in s["grads"]],
-                          master=host(s["master"]).reshape(R, po.S).copy(),
+        units.append(dict(po=po, grads=[host(g) for g in s.grads],
+                          master=host(s.master).reshape(R, po.S).copy(),
                           m=np.zeros((R, po.S), np.float32), v=np.zeros((R, po.S), np.float32),
-                          param=host(s["param"]).reshape(R, po.S).copy()))
+                          param=host(s.param).reshape(R, po.S).copy()))
     done = 0
     secs = 0.0
     unit_steps = 0

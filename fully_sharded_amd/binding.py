@@ -74,6 +74,22 @@ _SIGS = {
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_int32, ctypes.c_void_p]),
     "fsdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fsdp_plan_work_items": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                            ctypes.POINTER(ctypes.c_int64)]),
+    "fsdp_reshard_plan": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_void_p)]),
+    "fsdp_reshard_destroy": (None, [ctypes.c_void_p]),
+    "fsdp_reshard_items": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "fsdp_reshard": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int32, ctypes.c_void_p]),
+    "fsdp_grad_accumulate": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.c_int32, ctypes.c_void_p]),
+    "fsdp_allreduce_avg": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.c_int32, ctypes.c_void_p]),
 }
 
 
@@ -186,6 +202,12 @@ class Plan:
     def prepare(self, stream=None):
         _check("fsdp_plan_prepare", lib().fsdp_plan_prepare(self._h, _stream(stream)))
 
+    def work_items(self, space: int):
+        """Host copy of the per-workgroup work items: list of (dst, src, len);
+        space 0 = shard space, 1 = flat space."""
+        return _items(lambda out, cap, n: lib().fsdp_plan_work_items(self._h, space, out, cap, n),
+                      "fsdp_plan_work_items")
+
     def unflatten(self, full: torch.Tensor):
         """Per-parameter views of a full-unit buffer [T] (no copy)."""
         views = []
@@ -193,6 +215,84 @@ class Plan:
             q = self.param(p)
             views.append(full[q["flat_off"]:q["flat_off"] + q["numel"]].view(shape))
         return views
+
+
+def _items(call, name):
+    n = ctypes.c_int64()
+    _check(name, call(None, 0, ctypes.byref(n)))
+    out = (ctypes.c_int64 * (3 * max(1, n.value)))()
+    _check(name, call(out, n.value, ctypes.byref(n)))
+    return [tuple(out[3 * i:3 * i + 3]) for i in range(n.value)]
+
+
+class Resharder:
+    """Re-sharding of one unit from plan `src` to plan `dst` (other R and/or
+    layout, same parameter shapes)."""
+
+    def __init__(self, src: Plan, dst: Plan):
+        h = ctypes.c_void_p()
+        _check("fsdp_reshard_plan", lib().fsdp_reshard_plan(src.handle, dst.handle,
+                                                            ctypes.byref(h)))
+        self._h = h
+        self.src_plan = src
+        self.dst_plan = dst
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.fsdp_reshard_destroy(h)
+            self._h = None
+
+    def work_items(self):
+        return _items(lambda out, cap, n: lib().fsdp_reshard_items(self._h, out, cap, n),
+                      "fsdp_reshard_items")
+
+
+def fsdp_reshard_plan(src: Plan, dst: Plan) -> Resharder:
+    return Resharder(src, dst)
+
+
+def fsdp_reshard(rs: Resharder, src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """src [R_from, S_from] -> dst [R_to, S_to], same dtype, bits copied."""
+    if src.numel() != rs.src_plan.R * rs.src_plan.S or dst.numel() != rs.dst_plan.R * rs.dst_plan.S:
+        raise ValueError("size mismatch with the plans")
+    if _dtype_code(src) != _dtype_code(dst):
+        raise ValueError("src and dst dtypes differ")
+    _check("fsdp_reshard", lib().fsdp_reshard(rs.handle, _dev(src, "src"), _dev(dst, "dst"),
+                                              _dtype_code(src), _stream(stream)))
+
+
+def fsdp_grad_accumulate(plan: Plan, grads, acc, first: bool, stream=None):
+    """acc[r] = grads[r] (first) or acc[r] + grads[r], fp32, over the unit."""
+    if len(grads) != plan.R or len(acc) != plan.R:
+        raise ValueError("need R gradients and R accumulators")
+    dt = _dtype_code(grads[0])
+    for g, a in zip(grads, acc):
+        if g.numel() != plan.T or _dtype_code(g) != dt or a.numel() != plan.T \
+                or a.dtype != torch.float32:
+            raise ValueError("gradient or accumulator size/dtype mismatch")
+    _check("fsdp_grad_accumulate",
+           lib().fsdp_grad_accumulate(plan.handle, _ptr_array(grads, "grads"), dt,
+                                      _ptr_array(acc, "acc"), int(bool(first)), _stream(stream)))
+
+
+def fsdp_allreduce_avg(plan: Plan, grads, out, stream=None):
+    """out[r] = rank-order mean of the R full-unit gradients, for every r."""
+    if len(grads) != plan.R or len(out) != plan.R:
+        raise ValueError("need R gradients and R outputs")
+    dt = _dtype_code(grads[0])
+    odt = _dtype_code(out[0])
+    for g, o in zip(grads, out):
+        if g.numel() != plan.T or _dtype_code(g) != dt or o.numel() != plan.T \
+                or _dtype_code(o) != odt:
+            raise ValueError("gradient or output size/dtype mismatch")
+    _check("fsdp_allreduce_avg",
+           lib().fsdp_allreduce_avg(plan.handle, _ptr_array(grads, "grads"), dt,
+                                    _ptr_array(out, "out"), odt, _stream(stream)))
 
 
 def fsdp_plan_layout(shapes, R: int, layout) -> Plan:

@@ -13,8 +13,8 @@
 #include "plan.hpp"
 
 using fsdp::AdamScalars;
-using fsdp::DeviceTables;
 using fsdp::PtrArray;
+using fsdp::Work;
 
 namespace {
 
@@ -95,11 +95,7 @@ fsdp_status fsdp_plan_layout(int32_t n_params, const int32_t* ndims, const int64
   return FSDP_OK;
 }
 
-void fsdp_plan_destroy(fsdp_plan* plan) {
-  if (!plan) return;
-  for (auto& kv : plan->device) (void)hipFree(kv.second.shard_work);
-  delete plan;
-}
+void fsdp_plan_destroy(fsdp_plan* plan) { delete plan; }
 
 fsdp_status fsdp_plan_get_info(const fsdp_plan* plan, fsdp_plan_info* out) {
   if (!plan || !out) return FSDP_ERR_INVALID_ARG;
@@ -161,11 +157,34 @@ int64_t fsdp_plan_state_bytes_per_rank(const fsdp_plan* plan) {
   return plan ? 16 * plan->S : -1;
 }
 
+namespace {
+fsdp_status copy_items(const std::vector<Work>& items, int64_t* out, int64_t capacity,
+                       int64_t* n) {
+  if (!n) return FSDP_ERR_INVALID_ARG;
+  *n = static_cast<int64_t>(items.size());
+  if (!out) return FSDP_OK;
+  if (capacity < *n) return FSDP_ERR_INVALID_ARG;
+  for (size_t i = 0; i < items.size(); ++i) {
+    out[3 * i + 0] = items[i].dst;
+    out[3 * i + 1] = items[i].src;
+    out[3 * i + 2] = items[i].len;
+  }
+  return FSDP_OK;
+}
+}  // namespace
+
+fsdp_status fsdp_plan_work_items(const fsdp_plan* plan, int32_t space, int64_t* out,
+                                 int64_t capacity, int64_t* n) {
+  if (!plan || (space != 0 && space != 1)) return FSDP_ERR_INVALID_ARG;
+  return copy_items(space == 0 ? plan->shard_work.host : plan->flat_work.host, out, capacity, n);
+}
+
 fsdp_status fsdp_plan_prepare(const fsdp_plan* plan, void* stream) {
   (void)stream;
   if (!plan) return FSDP_ERR_INVALID_ARG;
-  const DeviceTables* t = nullptr;
-  return fsdp::device_tables(plan, &t);
+  const Work* w = nullptr;
+  const fsdp_status st = plan->shard_work.device(&w);
+  return st != FSDP_OK ? st : plan->flat_work.device(&w);
 }
 
 fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t full_dtype,
@@ -177,20 +196,19 @@ fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t ful
   if (overlap(range_of(full, plan->T * dtype_size(full_dtype)),
               range_of(shards, plan->R * plan->S * dtype_size(shard_dtype))))
     return FSDP_ERR_INVALID_ARG;
-  const DeviceTables* t = nullptr;
-  fsdp_status st = fsdp::device_tables(plan, &t);
+  const Work* w = nullptr;
+  const fsdp_status st = plan->shard_work.device(&w);
   if (st != FSDP_OK) return st;
   const bool vec = aligned(full, 16) && aligned(shards, 16);
-  const auto n_work = static_cast<int64_t>(plan->shard_work.size());
+  const auto n_work = static_cast<int64_t>(plan->shard_work.host.size());
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (full_dtype == shard_dtype) {
     PtrArray dst{};
     dst.p[0] = shards;
-    return from_hip(fsdp::launch_copy(t->shard_work, n_work, full, dst, 1,
+    return from_hip(fsdp::launch_copy(w, n_work, full, dst, 1,
                                       static_cast<int>(dtype_size(full_dtype)), vec, s));
   }
-  return from_hip(
-      fsdp::launch_pack_cast(t->shard_work, n_work, full, full_dtype, shards, shard_dtype, vec, s));
+  return from_hip(fsdp::launch_pack_cast(w, n_work, full, full_dtype, shards, shard_dtype, vec, s));
 }
 
 fsdp_status fsdp_gather_unflatten(const fsdp_plan* plan, const void* shards, int32_t dtype,
@@ -213,11 +231,11 @@ fsdp_status fsdp_gather_unflatten(const fsdp_plan* plan, const void* shards, int
   }
   if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
   if (n == 0) return FSDP_OK;
-  const DeviceTables* t = nullptr;
-  fsdp_status st = fsdp::device_tables(plan, &t);
+  const Work* w = nullptr;
+  const fsdp_status st = plan->flat_work.device(&w);
   if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_copy(t->flat_work, static_cast<int64_t>(plan->flat_work.size()),
-                                    shards, dst, plan->R, static_cast<int>(es), vec,
+  return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(plan->flat_work.host.size()), shards,
+                                    dst, plan->R, static_cast<int>(es), vec,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -235,12 +253,12 @@ fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* gr
     vec = vec && aligned(grads[q], 16);
     g.p[q] = grads[q];
   }
-  const DeviceTables* t = nullptr;
-  fsdp_status st = fsdp::device_tables(plan, &t);
+  const Work* w = nullptr;
+  const fsdp_status st = plan->shard_work.device(&w);
   if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_rs_avg(t->shard_work,
-                                      static_cast<int64_t>(plan->shard_work.size()), g, plan->R,
-                                      grad_dtype, out, vec, static_cast<hipStream_t>(stream)));
+  return from_hip(fsdp::launch_rs_avg(w, static_cast<int64_t>(plan->shard_work.host.size()), g,
+                                      plan->R, grad_dtype, out, vec,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
@@ -301,12 +319,111 @@ fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparam
   if (!grads_are_replicas)
     return from_hip(fsdp::launch_adamw(n, static_cast<const float*>(grads[0]), master, m, v,
                                        param_out, param_dtype, sc, vec, s));
-  const DeviceTables* tb = nullptr;
-  fsdp_status st = fsdp::device_tables(plan, &tb);
+  const Work* w = nullptr;
+  const fsdp_status st = plan->shard_work.device(&w);
   if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_fused(tb->shard_work,
-                                     static_cast<int64_t>(plan->shard_work.size()), g, plan->R,
-                                     grad_dtype, master, m, v, param_out, param_dtype, sc, vec, s));
+  return from_hip(fsdp::launch_fused(w, static_cast<int64_t>(plan->shard_work.host.size()), g,
+                                     plan->R, grad_dtype, master, m, v, param_out, param_dtype, sc,
+                                     vec, s));
+}
+
+fsdp_status fsdp_reshard_plan(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder** out) {
+  if (!out) return FSDP_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!from || !to) return FSDP_ERR_INVALID_ARG;
+  fsdp_resharder* rs = new (std::nothrow) fsdp_resharder();
+  if (!rs) return FSDP_ERR_OUT_OF_MEMORY;
+  fsdp_status st;
+  try {
+    st = fsdp::build_reshard(from, to, rs);
+  } catch (const std::bad_alloc&) {
+    st = FSDP_ERR_OUT_OF_MEMORY;
+  }
+  if (st != FSDP_OK) {
+    delete rs;
+    return st;
+  }
+  *out = rs;
+  return FSDP_OK;
+}
+
+void fsdp_reshard_destroy(fsdp_resharder* rs) { delete rs; }
+
+fsdp_status fsdp_reshard_items(const fsdp_resharder* rs, int64_t* out, int64_t capacity,
+                               int64_t* n) {
+  if (!rs) return FSDP_ERR_INVALID_ARG;
+  return copy_items(rs->work.host, out, capacity, n);
+}
+
+fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, int32_t dtype,
+                         void* stream) {
+  if (!rs || !src || !dst || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
+  const int64_t es = dtype_size(dtype);
+  if (!aligned(src, es) || !aligned(dst, es)) return FSDP_ERR_INVALID_ARG;
+  if (overlap(range_of(src, rs->R_from * rs->S_from * es), range_of(dst, rs->R_to * rs->S_to * es)))
+    return FSDP_ERR_INVALID_ARG;
+  const Work* w = nullptr;
+  const fsdp_status st = rs->work.device(&w);
+  if (st != FSDP_OK) return st;
+  PtrArray d{};
+  d.p[0] = dst;
+  return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(rs->work.host.size()), src, d, 1,
+                                    static_cast<int>(es), aligned(src, 16) && aligned(dst, 16),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+fsdp_status fsdp_grad_accumulate(const fsdp_plan* plan, const void* const* grads,
+                                 int32_t grad_dtype, float* const* acc, int32_t first,
+                                 void* stream) {
+  if (!plan || !grads || !acc || !valid_dtype(grad_dtype)) return FSDP_ERR_INVALID_ARG;
+  if (first != 0 && first != 1) return FSDP_ERR_INVALID_ARG;
+  const int64_t ges = dtype_size(grad_dtype);
+  std::vector<Range> outs;
+  std::vector<Range> ins;
+  PtrArray g{}, a{};
+  bool vec = true;
+  for (int r = 0; r < plan->R; ++r) {
+    if (!grads[r] || !acc[r] || !aligned(grads[r], ges) || !aligned(acc[r], 4))
+      return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(grads[r], 16) && aligned(acc[r], 16);
+    ins.push_back(range_of(grads[r], plan->T * ges));
+    outs.push_back(range_of(acc[r], plan->T * 4));
+    g.p[r] = grads[r];
+    a.p[r] = acc[r];
+  }
+  if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return FSDP_ERR_INVALID_ARG;
+  return from_hip(fsdp::launch_accumulate(plan->T, plan->R, g, grad_dtype, a, first != 0, vec,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
+                               int32_t grad_dtype, void* const* out, int32_t out_dtype,
+                               void* stream) {
+  if (!plan || !grads || !out || !valid_dtype(grad_dtype) || !valid_dtype(out_dtype))
+    return FSDP_ERR_INVALID_ARG;
+  const int64_t ges = dtype_size(grad_dtype), oes = dtype_size(out_dtype);
+  std::vector<Range> outs;
+  std::vector<Range> ins;
+  PtrArray g{}, o{};
+  bool vec = true;
+  for (int r = 0; r < plan->R; ++r) {
+    if (!grads[r] || !out[r] || !aligned(grads[r], ges) || !aligned(out[r], oes))
+      return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(grads[r], 16) && aligned(out[r], 16);
+    ins.push_back(range_of(grads[r], plan->T * ges));
+    outs.push_back(range_of(out[r], plan->T * oes));
+    g.p[r] = grads[r];
+    o.p[r] = out[r];
+  }
+  if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
+  for (const Range& x : outs)
+    for (const Range& i : ins)
+      if (overlap(x, i)) return FSDP_ERR_INVALID_ARG;
+  return from_hip(fsdp::launch_allreduce(plan->T, plan->R, g, grad_dtype, o, out_dtype, vec,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 const char* fsdp_status_string(fsdp_status status) {

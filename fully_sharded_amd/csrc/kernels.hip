@@ -417,6 +417,74 @@ __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ wor
   }
 }
 
+// ------------------------------------------------- gradient accumulation
+// acc[r][i] = g[r][i] (first micro-batch) or acc[r][i] + g[r][i], fp32, for
+// every rank r (blockIdx.y) and i < T.  Elementwise: no layout involved.
+struct AccArgs {
+  PtrArray g;
+  PtrArray acc;
+  int64_t T;
+  int first;
+  int vec;
+};
+
+template <typename G>
+__global__ __launch_bounds__(kThreads) void k_accumulate(AccArgs a) {
+  const G* __restrict__ g = static_cast<const G*>(a.g.p[blockIdx.y]);
+  float* __restrict__ acc = static_cast<float*>(const_cast<void*>(a.acc.p[blockIdx.y]));
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * kEPL;
+  if (e0 >= a.T) return;
+  if (a.vec && e0 + kEPL <= a.T) {
+    float x[4];
+    Io<G>::load4(g + e0, true, x);
+    if (!a.first) {
+      float y[4];
+      Io<float>::load4(acc + e0, true, y);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = y[k] + x[k];
+    }
+    Io<float>::store4(acc + e0, true, x);
+  } else {
+    const int64_t hi = e0 + kEPL < a.T ? e0 + kEPL : a.T;
+    for (int64_t e = e0; e < hi; ++e) {
+      const float x = Io<G>::load1(g + e);
+      acc[e] = a.first ? x : acc[e] + x;
+    }
+  }
+}
+
+// ------------------------------------------------------ all-reduce-average
+// out[r][i] = (g_0[i] + ... + g_{R-1}[i]) / R for every receiver r and
+// i < T: DDP's averaged all-reduce, the rank-order mean of the
+// reduce-scatter over the whole unit.
+struct ArArgs {
+  PtrArray g;
+  PtrArray out;
+  int64_t T;
+  int R;
+  int vec;
+};
+
+template <typename G, typename O, int RT>
+__global__ __launch_bounds__(kThreads) void k_allreduce(ArArgs a) {
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * kEPL;
+  if (e0 >= a.T) return;
+  const int R = RT > 0 ? RT : a.R;
+  if (a.vec && e0 + kEPL <= a.T) {
+    float avg[4];
+    grad_avg4<G, RT>(a.g, a.R, e0, true, avg);
+    for (int r = 0; r < R; ++r)
+      Io<O>::store4(static_cast<O*>(const_cast<void*>(a.out.p[r])) + e0, true, avg);
+  } else {
+    const int64_t hi = e0 + kEPL < a.T ? e0 + kEPL : a.T;
+    for (int64_t e = e0; e < hi; ++e) {
+      const float avg = grad_avg1<G, RT>(a.g, a.R, e);
+      for (int r = 0; r < R; ++r)
+        Io<O>::store1(static_cast<O*>(const_cast<void*>(a.out.p[r])) + e, avg);
+    }
+  }
+}
+
 // ----------------------------------------------------------------- launch
 template <typename Args>
 hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a,
@@ -440,6 +508,17 @@ const void* pick_rs(int R) {
     case 7: return reinterpret_cast<const void*>(&k_rs_avg<G, 7>);
     case 8: return reinterpret_cast<const void*>(&k_rs_avg<G, 8>);
     default: return reinterpret_cast<const void*>(&k_rs_avg<G, 0>);
+  }
+}
+
+template <typename G, typename O>
+const void* pick_allreduce(int R) {
+  switch (R) {
+    case 1: return reinterpret_cast<const void*>(&k_allreduce<G, O, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_allreduce<G, O, 2>);
+    case 4: return reinterpret_cast<const void*>(&k_allreduce<G, O, 4>);
+    case 8: return reinterpret_cast<const void*>(&k_allreduce<G, O, 8>);
+    default: return reinterpret_cast<const void*>(&k_allreduce<G, O, 0>);
   }
 }
 
@@ -513,6 +592,35 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
   else
     fn = param_dt == FSDP_BF16 ? pick_fused<float, u16>(R) : pick_fused<float, float>(R);
   return launch_work(fn, work, n_work, a, stream);
+}
+
+hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_dt,
+                             const PtrArray& acc, bool first, bool vec, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  AccArgs a{grads, acc, T, first ? 1 : 0, vec ? 1 : 0};
+  const int64_t blocks = (T + kThreads * kEPL - 1) / (kThreads * kEPL);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const void* fn = grad_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_accumulate<u16>)
+                                        : reinterpret_cast<const void*>(&k_accumulate<float>);
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(R)),
+                         dim3(kThreads), args, 0, stream);
+}
+
+hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt,
+                            const PtrArray& out, int out_dt, bool vec, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  ArArgs a{grads, out, T, R, vec ? 1 : 0};
+  const int64_t blocks = (T + kThreads * kEPL - 1) / (kThreads * kEPL);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const void* fn;
+  if (grad_dt == FSDP_BF16)
+    fn = out_dt == FSDP_BF16 ? pick_allreduce<u16, u16>(R) : pick_allreduce<u16, float>(R);
+  else
+    fn = out_dt == FSDP_BF16 ? pick_allreduce<float, u16>(R) : pick_allreduce<float, float>(R);
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0,
+                         stream);
 }
 
 }  // namespace fsdp

@@ -47,4 +47,13 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
                         int grad_dt, float* master, float* m, float* v, void* param,
                         int param_dt, const AdamScalars& sc, bool vec, hipStream_t stream);
 
+// acc[r] = g[r] (first) or acc[r] + g[r], fp32, for r < R over [0, T).
+hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_dt,
+                             const PtrArray& acc, bool first, bool vec, hipStream_t stream);
+
+// out[r] = rank-order mean of the R gradients, for every receiver r, over
+// [0, T).
+hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt,
+                            const PtrArray& out, int out_dt, bool vec, hipStream_t stream);
+
 }  // namespace fsdp

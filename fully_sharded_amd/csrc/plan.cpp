@@ -1,5 +1,6 @@
 // Host-side planning of one FSDP unit: the shard layout, its contiguous
-// segments and the per-workgroup work tables.
+// segments and the per-workgroup work tables; and the table that re-shards
+// one plan's layout into another's.
 //
 // Layout rules ("Understanding FSDP from source" 2.1; "FSDP Transformer
 // Block Sharding Example", 4-GPU shard layout):
@@ -15,35 +16,7 @@
 #include "plan.hpp"
 
 namespace fsdp {
-namespace {
 
-// Elements per work item (one workgroup): exactly one pass of its 256
-// lanes, at every size -- 1024 for the 4-element lanes of the arithmetic
-// kernels (shard space), 2048 for the 16-byte lanes of the bf16 copy (flat
-// space).  Workgroups are dispatched in order, so the ones in flight then
-// cover one compact window of every stream; giving each workgroup 16
-// consecutive passes spread the in-flight window over ~60 MB per stream and
-// cost 8% on an 872M-element unit (5.27 vs 5.68 TB/s), and even 2 passes
-// cost 7% on a 3M-element one.
-constexpr int64_t kShardChunk = 1024;
-constexpr int64_t kFlatChunk = 2048;
-
-// Append [dst, dst+len) <- [src, src+len) as work items cut at multiples of
-// chunk in the destination index space.
-void emit(std::vector<Work>& out, int64_t dst, int64_t src, int64_t len, int64_t chunk) {
-  while (len > 0) {
-    const int64_t next = (dst / chunk + 1) * chunk;
-    const int64_t n = std::min(len, next - dst);
-    out.push_back(Work{dst, src < 0 ? -1 : src, n});
-    dst += n;
-    if (src >= 0) src += n;
-    len -= n;
-  }
-}
-
-// Append a run to a list of runs, merging it with the previous one when both
-// are contiguous in the destination and (both padding or) contiguous in the
-// source.
 void push_run(std::vector<Work>& runs, int64_t dst, int64_t src, int64_t len) {
   if (len <= 0) return;
   if (!runs.empty()) {
@@ -59,7 +32,55 @@ void push_run(std::vector<Work>& runs, int64_t dst, int64_t src, int64_t len) {
   runs.push_back(Work{dst, src < 0 ? -1 : src, len});
 }
 
-}  // namespace
+void emit_items(const std::vector<Work>& runs, int64_t chunk, std::vector<Work>& out) {
+  for (const Work& w : runs) {
+    int64_t dst = w.dst, src = w.src, len = w.len;
+    while (len > 0) {
+      const int64_t next = (dst / chunk + 1) * chunk;
+      const int64_t n = std::min(len, next - dst);
+      out.push_back(Work{dst, src < 0 ? -1 : src, n});
+      dst += n;
+      if (src >= 0) src += n;
+      len -= n;
+    }
+  }
+}
+
+fsdp_status WorkTable::device(const Work** out) const {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FSDP_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu_);
+  auto it = dev_.find(dev);
+  if (it != dev_.end()) {
+    *out = it->second;
+    return FSDP_OK;
+  }
+  const size_t bytes = std::max<size_t>(1, host.size()) * sizeof(Work);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return FSDP_ERR_OUT_OF_MEMORY;
+  }
+  if (!host.empty() &&
+      hipMemcpy(mem, host.data(), host.size() * sizeof(Work), hipMemcpyHostToDevice) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(mem);
+    return FSDP_ERR_HIP;
+  }
+  dev_.emplace(dev, static_cast<Work*>(mem));
+  *out = static_cast<Work*>(mem);
+  return FSDP_OK;
+}
+
+void WorkTable::release() {
+  std::lock_guard<std::mutex> lock(mu_);
+  for (auto& kv : dev_) (void)hipFree(kv.second);
+  dev_.clear();
+}
 
 fsdp_status build_plan(fsdp_plan* pl) {
   const int64_t R = pl->R;
@@ -113,70 +134,73 @@ fsdp_status build_plan(fsdp_plan* pl) {
   }
 
   // shard-space runs: every position of [0, R*S), pieces and padding
-  std::vector<Work> runs;
   {
     size_t i = 0;
     for (int64_t r = 0; r < R; ++r) {
       int64_t pos = 0;
       for (; i < pl->segments.size() && pl->segments[i].rank == r; ++i) {
         const Segment& s = pl->segments[i];
-        push_run(runs, r * pl->S + pos, -1, s.shard_off - pos);
-        push_run(runs, r * pl->S + s.shard_off, s.flat_off, s.len);
+        push_run(pl->shard_runs, r * pl->S + pos, -1, s.shard_off - pos);
+        push_run(pl->shard_runs, r * pl->S + s.shard_off, s.flat_off, s.len);
         pos = s.shard_off + s.len;
       }
-      push_run(runs, r * pl->S + pos, -1, pl->S - pos);
+      push_run(pl->shard_runs, r * pl->S + pos, -1, pl->S - pos);
     }
   }
-  pl->shard_chunk = kShardChunk;
-  for (const Work& w : runs) emit(pl->shard_work, w.dst, w.src, w.len, pl->shard_chunk);
+  emit_items(pl->shard_runs, kShardChunk, pl->shard_work.host);
 
   // flat-space runs: the same segments ordered by flat offset; they tile
   // [0, T) exactly
   std::vector<Segment> by_flat = pl->segments;
   std::sort(by_flat.begin(), by_flat.end(),
             [](const Segment& a, const Segment& b) { return a.flat_off < b.flat_off; });
-  runs.clear();
   int64_t expect = 0;
   for (const Segment& s : by_flat) {
     if (s.flat_off != expect) return FSDP_ERR_INVALID_ARG;  // cannot happen
-    push_run(runs, s.flat_off, s.rank * pl->S + s.shard_off, s.len);
+    push_run(pl->flat_runs, s.flat_off, s.rank * pl->S + s.shard_off, s.len);
     expect += s.len;
   }
   if (expect != pl->T) return FSDP_ERR_INVALID_ARG;
-  pl->flat_chunk = kFlatChunk;
-  for (const Work& w : runs) emit(pl->flat_work, w.dst, w.src, w.len, pl->flat_chunk);
+  emit_items(pl->flat_runs, kFlatChunk, pl->flat_work.host);
   return FSDP_OK;
 }
 
-fsdp_status device_tables(const fsdp_plan* pl, const DeviceTables** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FSDP_ERR_HIP;
-  std::lock_guard<std::mutex> lock(pl->mu);
-  auto it = pl->device.find(dev);
-  if (it != pl->device.end()) {
-    *out = &it->second;
-    return FSDP_OK;
+fsdp_status build_reshard(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder* rs) {
+  if (from->shapes != to->shapes) return FSDP_ERR_INVALID_ARG;
+  rs->R_from = from->R;
+  rs->R_to = to->R;
+  rs->T = from->T;
+  rs->S_from = from->S;
+  rs->S_to = to->S;
+  // Destination: `to`'s shard space, runs in order (pieces map to flat
+  // offsets, padding has none).  Each piece's flat range is looked up in
+  // `from`'s flat runs (which tile [0, T) in order), split where those runs
+  // end.
+  const std::vector<Work>& fr = from->flat_runs;
+  std::vector<Work> runs;
+  for (const Work& d : to->shard_runs) {
+    if (d.src < 0) {
+      push_run(runs, d.dst, -1, d.len);
+      continue;
+    }
+    int64_t f = d.src, dst = d.dst, left = d.len;
+    // first run of `from` whose flat range ends after f
+    size_t k = static_cast<size_t>(
+        std::upper_bound(fr.begin(), fr.end(), f,
+                         [](int64_t x, const Work& w) { return x < w.dst + w.len; }) -
+        fr.begin());
+    while (left > 0) {
+      if (k >= fr.size()) return FSDP_ERR_INVALID_ARG;  // cannot happen
+      const Work& s = fr[k];
+      const int64_t take = std::min(left, s.dst + s.len - f);
+      push_run(runs, dst, s.src + (f - s.dst), take);
+      dst += take;
+      f += take;
+      left -= take;
+      ++k;
+    }
   }
-  const size_t n_shard = pl->shard_work.size();
-  const size_t n_flat = pl->flat_work.size();
-  void* mem = nullptr;
-  if (hipMalloc(&mem, (n_shard + n_flat) * sizeof(Work)) != hipSuccess) {
-    (void)hipGetLastError();
-    return FSDP_ERR_OUT_OF_MEMORY;
-  }
-  Work* w = static_cast<Work*>(mem);
-  if (hipMemcpy(w, pl->shard_work.data(), n_shard * sizeof(Work), hipMemcpyHostToDevice) !=
-          hipSuccess ||
-      hipMemcpy(w + n_shard, pl->flat_work.data(), n_flat * sizeof(Work),
-                hipMemcpyHostToDevice) != hipSuccess) {
-    (void)hipFree(mem);
-    return FSDP_ERR_HIP;
-  }
-  DeviceTables t;
-  t.shard_work = w;
-  t.flat_work = w + n_shard;
-  auto res = pl->device.emplace(dev, t);
-  *out = &res.first->second;
+  emit_items(runs, kFlatChunk, rs->work.host);
   return FSDP_OK;
 }
 

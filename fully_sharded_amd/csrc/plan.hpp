@@ -1,7 +1,7 @@
-// Internal plan structure of one FSDP unit: shapes, the shard layout, the
-// contiguous (rank, shard range, flat range) segments, and the per-workgroup
-// work tables the kernels consume.  Host-side; the device copies of the work
-// tables are uploaded lazily per device.
+// Internal plan structures: the shard layout of one FSDP unit, its
+// contiguous (rank, shard range, flat range) segments, and the
+// per-workgroup work tables the kernels consume (host copies, and device
+// copies uploaded lazily per device).
 #pragma once
 
 #include <cstdint>
@@ -13,11 +13,10 @@
 
 namespace fsdp {
 
-// One workgroup's contiguous range.  In the shard space (pack,
-// reduce-scatter, AdamW) dst indexes the [R][S] shard buffer linearly and
-// src the full-unit buffer; in the flat space (gather) dst indexes the
-// full-unit buffer and src the shard buffer.  src < 0 marks padding (no
-// source: the destination gets +0 / is left as padding).
+// One workgroup's contiguous range.  dst indexes the destination index space
+// of the operation (the [R][S] shard buffer linearly, or the full-unit
+// buffer), src the source space.  src < 0 marks padding (no source: the
+// destination gets +0).
 struct Work {
   int64_t dst;
   int64_t src;
@@ -35,10 +34,29 @@ struct Param {
   int64_t numel, d0, row, flat_off, k, shard_off;
 };
 
-struct DeviceTables {
-  Work* shard_work = nullptr;  // device copy of shard_work
-  Work* flat_work = nullptr;   // device copy of flat_work
+// A work table: host copy plus one device copy per HIP device.
+class WorkTable {
+ public:
+  std::vector<Work> host;
+  // Device copy for the current device, uploaded on first use (hipMalloc +
+  // hipMemcpy, synchronous).  Returns FSDP_OK and sets *out, or an error.
+  fsdp_status device(const Work** out) const;
+  void release();  // free every device copy
+  ~WorkTable() { release(); }
+
+ private:
+  mutable std::mutex mu_;
+  mutable std::map<int, Work*> dev_;
 };
+
+// Append [dst, dst+len) <- [src, src+len) to a list of runs, merging it with
+// the previous run when both are contiguous in the destination and (both
+// padding or) contiguous in the source.
+void push_run(std::vector<Work>& runs, int64_t dst, int64_t src, int64_t len);
+
+// Cut runs into work items of at most `chunk` elements, at multiples of
+// chunk in the destination space.
+void emit_items(const std::vector<Work>& runs, int64_t chunk, std::vector<Work>& out);
 
 }  // namespace fsdp
 
@@ -49,22 +67,36 @@ struct fsdp_plan {
   int64_t S = 0;
   std::vector<std::vector<int64_t>> shapes;
   std::vector<fsdp::Param> params;
-  std::vector<fsdp::Segment> segments;      // ordered by (rank, shard_off)
-  std::vector<fsdp::Work> shard_work;       // covers [0, R*S) in order
-  std::vector<fsdp::Work> flat_work;        // covers [0, T) in order
-  int64_t shard_chunk = 0;                  // max elements per work item
-  int64_t flat_chunk = 0;
+  std::vector<fsdp::Segment> segments;  // ordered by (rank, shard_off)
+  std::vector<fsdp::Work> shard_runs;   // shard space [0, R*S): pieces and padding
+  std::vector<fsdp::Work> flat_runs;    // flat space [0, T) -> shard space
+  fsdp::WorkTable shard_work;           // shard_runs cut into work items
+  fsdp::WorkTable flat_work;            // flat_runs cut into work items
+};
 
-  mutable std::mutex mu;
-  mutable std::map<int, fsdp::DeviceTables> device;  // by HIP device id
+struct fsdp_resharder {
+  int32_t R_from = 0, R_to = 0;
+  int64_t T = 0, S_from = 0, S_to = 0;
+  fsdp::WorkTable work;  // destination shard space [0, R_to*S_to) <- source shard space
 };
 
 namespace fsdp {
 
+// Elements per work item (one workgroup): exactly one pass of its 256
+// lanes, at every size -- 1024 for the 4-element lanes of the arithmetic
+// kernels (shard space), 2048 for the 16-byte lanes of the bf16 copy.
+// Workgroups are dispatched in order, so the ones in flight then cover one
+// compact window of every stream; giving each workgroup 16 consecutive
+// passes spread the in-flight window over ~60 MB per stream and cost 8% on
+// an 872M-element unit (5.27 vs 5.68 TB/s), and even 2 passes cost 7% on a
+// 3M-element one.
+constexpr int64_t kShardChunk = 1024;
+constexpr int64_t kFlatChunk = 2048;
+
 // Build every host-side table of a plan; returns FSDP_OK or an error.
 fsdp_status build_plan(fsdp_plan* pl);
 
-// Device tables for the current device (uploaded on first use).
-fsdp_status device_tables(const fsdp_plan* pl, const DeviceTables** out);
+// Build the work table that re-shards `from`'s layout into `to`'s.
+fsdp_status build_reshard(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder* rs);
 
 }  // namespace fsdp

@@ -131,6 +131,14 @@ fsdp_status fsdp_plan_comm_ledger(const fsdp_plan* plan, int32_t reshard_after_f
  * v, bf16 grad shard), the 16P/N account of "Understanding FSDP from
  * source" 3.2.  Returns -1 for a NULL plan. */
 int64_t fsdp_plan_state_bytes_per_rank(const fsdp_plan* plan);
+/* The plan's per-workgroup work items (host copy), for inspection and
+ * host-side tests: space 0 = the shard space [0, R*S) used by pack,
+ * reduce-scatter and the AdamW step (src = flat index, -1 for padding),
+ * space 1 = the flat space [0, T) used by the gather (src = linear shard
+ * index).  out[3*i..3*i+2] = {dst, src, len}; with out == NULL only *n is
+ * set; otherwise capacity (rows) must be >= the item count. */
+fsdp_status fsdp_plan_work_items(const fsdp_plan* plan, int32_t space, int64_t* out,
+                                 int64_t capacity, int64_t* n);
 /* Upload the plan's work tables to the current device now (synchronous).
  * Optional: operations do it on first use. */
 fsdp_status fsdp_plan_prepare(const fsdp_plan* plan, void* stream);
@@ -192,6 +200,60 @@ fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparam
                                   int64_t step, const void* const* grads, int32_t grad_dtype,
                                   int32_t grads_are_replicas, float* master, float* m, float* v,
                                   void* param_out, int32_t param_dtype, void* stream);
+
+/* ---- Beyond the per-step path: restore at another world size, gradient
+ * accumulation, and the DDP all-reduce the pages compare FSDP with. ---- */
+
+typedef struct fsdp_resharder fsdp_resharder; /* opaque; immutable once created */
+
+/* Plan the re-sharding of one unit from plan `from` to plan `to`: another R
+ * and/or the other layout, same parameter shapes (else
+ * FSDP_ERR_INVALID_ARG).  Restoring a sharded checkpoint at a different
+ * world size needs each new rank's shard of the same full tensors (zwjcode
+ * FSDP2 page, section 10; "Understanding FSDP from source" 4.5 gathers the
+ * full weights to save and re-shards them to load).  Host only; *out owns a
+ * new object, freed by fsdp_reshard_destroy; the plans may be destroyed
+ * afterwards. */
+fsdp_status fsdp_reshard_plan(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder** out);
+void fsdp_reshard_destroy(fsdp_resharder* rs);
+/* Its work items (host copy), as fsdp_plan_work_items: dst indexes `to`'s
+ * [R_to][S_to], src `from`'s [R_from][S_from] (-1: padding). */
+fsdp_status fsdp_reshard_items(const fsdp_resharder* rs, int64_t* out, int64_t capacity,
+                               int64_t* n);
+
+/* dst = the shards, under `to`, of the unit whose shards under `from` are
+ * src: equal to gathering src with `from` and packing with `to`, without
+ * materialising the full unit; padding +0, bits copied exactly.
+ *   src: [R_from][S_from], dst: [R_to][S_to], both of dtype, disjoint.  Use
+ *   it for the bf16 parameter and the fp32 master, m and v alike.  The
+ *   first call on a device uploads the work table (as for a plan). */
+fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, int32_t dtype,
+                         void* stream);
+
+/* Gradient accumulation over micro-batches: acc[r][i] = g[r][i] when first
+ * != 0, else acc[r][i] + g[r][i], in fp32, for every rank r < R and i < T
+ * (zwjcode FSDP2 page, section 08: every micro-batch runs forward and
+ * backward and the gradients add up before one update).  The accumulators
+ * then feed fsdp_adamw_shard_step as FSDP_F32 replicas (or
+ * fsdp_reduce_scatter_avg).
+ *   grads: R device pointers, [T] each, of grad_dtype; acc: R device
+ *   pointers, fp32 [T] each, pairwise disjoint and disjoint from the grads;
+ *   first is 0 or 1 (first = 1 copies, so a -0 gradient stays -0). */
+fsdp_status fsdp_grad_accumulate(const fsdp_plan* plan, const void* const* grads,
+                                 int32_t grad_dtype, float* const* acc, int32_t first,
+                                 void* stream);
+
+/* DDP's averaged all-reduce: out[r][i] = (sum over q = 0..R-1 of
+ * grads[q][i]) / R for every receiver r and i < T, with the same fp32
+ * rank-order sum and division as fsdp_reduce_scatter_avg ("FSDP Training
+ * Step Walkthrough", comparison with DDP; zwjcode FSDP2 page, section 09:
+ * the all-reduce gives every card the whole averaged gradient).  out_dtype
+ * FSDP_BF16 rounds the fp32 mean to nearest even.
+ *   grads: R device pointers, [T] each; out: R device pointers, [T] each of
+ *   out_dtype, pairwise disjoint and disjoint from the grads. */
+fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
+                               int32_t grad_dtype, void* const* out, int32_t out_dtype,
+                               void* stream);
 
 /* Static, human-readable name of a status. */
 const char* fsdp_status_string(fsdp_status status);

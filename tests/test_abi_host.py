@@ -160,3 +160,70 @@ def test_product_code_never_imports_the_oracle():
             if fn.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in src.lower(), fn
+
+
+# --------------------------------------------------- work tables, host side
+def expand(items, size):
+    """Items (dst, src, len) -> per-destination source index (-1 padding),
+    checking that they tile [0, size) in order."""
+    m = np.full(size, -2, np.int64)
+    pos = 0
+    for dst, src, n in items:
+        assert dst == pos and n > 0
+        m[dst:dst + n] = -1 if src < 0 else np.arange(src, src + n)
+        pos += n
+    assert pos == size
+    return m
+
+
+def oracle_shard_map(po):
+    """Oracle layout as a map: shard position r*S+j -> flat index (-1 pad)."""
+    m = np.full(po.R * po.S, -1, np.int64)
+    for r in range(po.R):
+        for f0, s0, n in po.pieces(r):
+            m[r * po.S + s0:r * po.S + s0 + n] = np.arange(f0, f0 + n)
+    return m
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8])
+def test_work_items_tile_both_spaces_like_the_oracle(R):
+    rng = np.random.default_rng(40 + R)
+    for trial in range(15):
+        shapes = [(int(rng.integers(1, 3 * R + 3)),) + tuple(int(x) for x in rng.integers(1, 300, int(rng.integers(0, 2))))
+                  for _ in range(int(rng.integers(1, 5)))]
+        layout = O.FLAT if trial % 2 else O.PER_PARAM
+        po = O.plan_layout(shapes, R, layout)
+        pg = F.Plan(shapes, R, layout)
+        shard = expand(pg.work_items(0), R * po.S)
+        want = oracle_shard_map(po)
+        np.testing.assert_array_equal(shard, want)
+        assert all(n <= 1024 for _, _, n in pg.work_items(0))
+        flat = expand(pg.work_items(1), po.T)
+        inv = np.full(po.T, -1, np.int64)
+        valid = want >= 0
+        inv[want[valid]] = np.flatnonzero(valid)
+        np.testing.assert_array_equal(flat, inv)
+        assert all(n <= 2048 for _, _, n in pg.work_items(1))
+
+
+@pytest.mark.parametrize("Ra,Rb", [(8, 4), (4, 8), (3, 5), (1, 2), (6, 6)])
+def test_resharder_items_match_the_oracle_reshard(Ra, Rb):
+    rng = np.random.default_rng(Ra * 100 + Rb)
+    for trial in range(10):
+        shapes = [(int(rng.integers(1, 3 * max(Ra, Rb) + 3)),) + tuple(int(x) for x in rng.integers(1, 50, int(rng.integers(0, 3))))
+                  for _ in range(int(rng.integers(1, 5)))]
+        la = O.FLAT if trial % 2 else O.PER_PARAM
+        lb = O.PER_PARAM if trial % 3 else O.FLAT
+        pa, pb = O.plan_layout(shapes, Ra, la), O.plan_layout(shapes, Rb, lb)
+        rs = F.Resharder(F.Plan(shapes, Ra, la), F.Plan(shapes, Rb, lb))
+        got = expand(rs.work_items(), Rb * pb.S)
+        # the oracle re-shards the source positions' own indices (+1; 0 = pad)
+        idx = (np.arange(Ra * pa.S, dtype=np.int64) + 1).reshape(Ra, pa.S)
+        idx[O.shard_pack(pa, np.ones(pa.T, np.int64)) == 0] = 0
+        want = O.reshard(pa, pb, idx).reshape(-1) - 1
+        np.testing.assert_array_equal(got, want)
+
+
+def test_resharder_rejects_different_units():
+    with pytest.raises(F.FsdpError):
+        F.Resharder(F.Plan([(4, 2)], 2, "flat"), F.Plan([(4, 3)], 2, "flat"))

@@ -485,3 +485,82 @@ def test_oracle_is_independent_of_the_library():
         if fn.endswith(".py"):
             src = open(os.path.join(here, fn)).read()
             assert "fully_sharded_amd" not in src and "ctypes" not in src
+
+
+# ------------------------------------------------------------ next rows
+def test_reshard_block_r4_to_r2_matches_the_page_row_table():
+    """[BLOCK] 4-GPU table: W_Q rows 128k..128k+127 on GPU k.  At 2 ranks
+    rank 0 must hold rows 0..255, i.e. what GPUs 0 and 1 held, in order."""
+    shapes = shapes_of(BLOCK_512)
+    p4 = O.plan_layout(shapes, 4, O.PER_PARAM)
+    p2 = O.plan_layout(shapes, 2, O.PER_PARAM)
+    full = np.zeros(p4.T, np.float32)
+    full[:512 * 512] = np.repeat(np.arange(512, dtype=np.float32), 512)
+    s2 = O.reshard(p4, p2, O.shard_pack(p4, full))
+    rows0 = s2[0, :256 * 512].reshape(256, 512)[:, 0]
+    rows1 = s2[1, :256 * 512].reshape(256, 512)[:, 0]
+    np.testing.assert_array_equal(rows0, np.arange(256))
+    np.testing.assert_array_equal(rows1, np.arange(256, 512))
+
+
+@pytest.mark.parametrize("Ra,Rb", [(1, 3), (2, 8), (3, 2), (5, 4), (8, 8)])
+def test_reshard_brute_force_roundtrip_and_layout_change(Ra, Rb):
+    rng = np.random.default_rng(Ra * 10 + Rb)
+    for trial in range(12):
+        shapes = random_shapes(rng, max(Ra, Rb))
+        la = O.FLAT if trial % 2 else O.PER_PARAM
+        lb = O.PER_PARAM if trial % 3 else O.FLAT
+        pa = O.plan_layout(shapes, Ra, la)
+        pb = O.plan_layout(shapes, Rb, lb)
+        x = rng.integers(1, 2**31, pa.T).astype(np.uint32)
+        sa = O.shard_pack(pa, x)
+        sb = O.reshard(pa, pb, sa)
+        # brute force: each destination element found through the two owner maps
+        own_a, _ = brute_owner(shapes, Ra, la)
+        own_b, Sb = brute_owner(shapes, Rb, lb)
+        want = np.zeros((Rb, Sb), np.uint32)
+        for i in range(pa.T):
+            ra, ja = own_a[i]
+            rb, jb = own_b[i]
+            want[rb, jb] = sa[ra, ja]
+        np.testing.assert_array_equal(sb, want)
+        np.testing.assert_array_equal(O.reshard(pb, pa, sb), sa)      # round trip
+        np.testing.assert_array_equal(O.reshard(pa, pa, sa), sa)      # identity
+
+
+def test_grad_accumulate_order_and_single_micro_batch():
+    rng = np.random.default_rng(2)
+    g = [(rng.standard_normal(1000) * 10.0 ** rng.integers(-6, 3)).astype(np.float32)
+         for _ in range(5)]
+    acc = O.grad_accumulate(g)
+    want = g[0].copy()
+    for k in range(1, 5):
+        for i in range(1000):
+            want[i] = np.float32(want[i] + g[k][i])
+    np.testing.assert_array_equal(acc.view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(O.grad_accumulate([g[0]]), g[0])
+    # integers below 2^20: the fp32 sum is exact
+    ints = [rng.integers(-2**20, 2**20, 64).astype(np.float32) for _ in range(7)]
+    np.testing.assert_array_equal(O.grad_accumulate(ints),
+                                  np.sum(np.stack(ints).astype(np.int64), 0).astype(np.float32))
+    z = np.array([-0.0], np.float32)
+    assert np.signbit(O.grad_accumulate([z, z])[0])
+    b16 = [O.bf16_rne(x) for x in g[:2]]
+    np.testing.assert_array_equal(O.grad_accumulate(b16),
+                                  O.bf16_to_f32(b16[0]) + O.bf16_to_f32(b16[1]))
+
+
+def test_allreduce_is_gather_of_reduce_scatter_and_ddp_volume():
+    rng = np.random.default_rng(4)
+    shapes = [(7, 3), (10,), (3, 2, 2)]
+    for R in (1, 2, 3, 8):
+        for layout in (O.PER_PARAM, O.FLAT):
+            pl = O.plan_layout(shapes, R, layout)
+            g = [rng.standard_normal(pl.T).astype(np.float32) for _ in range(R)]
+            ar = O.allreduce_avg(g)
+            gathered, _ = O.gather_unflatten(pl, O.reduce_scatter_avg(pl, g))
+            for r in range(R):
+                np.testing.assert_array_equal(ar[r], gathered)
+    # the walkthrough's DDP comparison: 2(N-1)/N x 8 = 8 elements at N = 2
+    gd = golden("walkthrough_2rank_toy.json")
+    assert O.ddp_allreduce_elems(8, 2) == gd["comm_per_rank_elements"]["ddp_allreduce"]
