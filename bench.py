@@ -49,6 +49,13 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--mode", choices=("step", "reshard", "accum", "ddp"), default="step",
+                    help="step: the training step (default, the headline); reshard: restore "
+                         "the model's sharded state at another world size; accum: a step "
+                         "with --micro micro-batches accumulated in fp32; ddp: the DDP "
+                         "comparator (all-reduce + AdamW on every rank's full replica)")
+    ap.add_argument("--micro", type=int, default=4, help="micro-batches for --mode accum")
+    ap.add_argument("--to-ranks", type=int, default=4, help="new world size for --mode reshard")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json "
@@ -137,6 +144,43 @@ def summarise_counters(fetch_csv, write_csv, workload):
     print(json.dumps(out))
 
 
+def setup_units(wl, dev):
+    """Plans and device buffers of every unit, inputs drawn on the GPU:
+    sharded fp32 master (m = v = 0), bf16 parameter, R gradient replicas."""
+    import torch
+
+    import fully_sharded_amd as F
+    from fully_sharded_amd.step import Unit
+    from workloads import gen
+    from workloads.configs import shapes_of
+
+    R = wl["R"]
+    gdt = torch.bfloat16 if wl["grad_dtype"] == "bf16" else torch.float32
+    pdt = torch.bfloat16 if wl["param_dtype"] == "bf16" else torch.float32
+    plans = {}
+    units = []
+    for u, unit in enumerate(wl["units"]):
+        shapes = tuple(shapes_of(unit))
+        if shapes not in plans:
+            plans[shapes] = F.Plan(list(shapes), R, wl["layout"])
+            plans[shapes].prepare()
+        pl = plans[shapes]
+        full = gen.device_master(wl, u, list(shapes), dev)
+        master, m, v = rows(3, R * pl.S, torch.float32, dev)
+        m.zero_()
+        v.zero_()
+        F.fsdp_shard_pack(pl, full, master)
+        param = torch.empty(R * pl.S, dtype=pdt, device=dev)
+        F.fsdp_shard_pack(pl, full, param)
+        del full
+        grads = rows(R, pl.T, gdt, dev)
+        for r in range(R):
+            grads[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
+        units.append(Unit(pl, master, m, v, param, grads))
+    torch.cuda.synchronize()
+    return plans, units
+
+
 def main():
     args = parse()
     if args.counters:
@@ -165,27 +209,10 @@ def main():
     pdt = torch.bfloat16 if wl["param_dtype"] == "bf16" else torch.float32
 
     # ---------------------------------------------------------------- set-up
-    plans = {}
-    units = []
     t_setup = time.perf_counter()
-    for u, unit in enumerate(wl["units"]):
-        shapes = tuple(shapes_of(unit))
-        if shapes not in plans:
-            plans[shapes] = F.Plan(list(shapes), R, wl["layout"])
-            plans[shapes].prepare()
-        pl = plans[shapes]
-        full = gen.device_master(wl, u, list(shapes), dev)
-        master, m, v = rows(3, R * pl.S, torch.float32, dev)
-        m.zero_()
-        v.zero_()
-        F.fsdp_shard_pack(pl, full, master)
-        param = torch.empty(R * pl.S, dtype=pdt, device=dev)
-        F.fsdp_shard_pack(pl, full, param)
-        del full
-        grads = rows(R, pl.T, gdt, dev)
-        for r in range(R):
-            grads[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
-        units.append(Unit(pl, master, m, v, param, grads))
+    plans, units = setup_units(wl, dev)
+    if args.mode != "step":
+        return run_mode(args, wl, plans, units)
     T_max = max(p.T for p in plans.values())
     n_recv = 2 if args.schedule == "prefetch" else 1
     recv = [rows(R, T_max, pdt, dev) for _ in range(n_recv)]
@@ -335,6 +362,269 @@ def main():
     if copy_info:
         line["copy_calibration"] = copy_info
     print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------------ other modes
+def _timed(fn, reps):
+    """ms per call of fn over reps back-to-back calls, HIP events on the
+    current stream (the stream every call below launches on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _host(t):
+    import numpy as np
+    import torch
+    t = t.detach().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _cpu_loop(work, budget_s):
+    """Run work() (returns params processed) until ~budget_s of CPU time."""
+    done = 0
+    secs = 0.0
+    calls = 0
+    while secs < budget_s and calls < 1000:
+        t0 = time.perf_counter()
+        done += work()
+        secs += time.perf_counter() - t0
+        calls += 1
+    return done, secs, calls
+
+
+def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
+    d = {
+        "metric": metric, "value": value, "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": dict({"workload": args.workload, "units": len(wl["units"]), "R": wl["R"],
+                        "layout": wl["layout"], "mode": args.mode}, **cfg),
+        "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    if extra:
+        d.update(extra)
+    print(json.dumps(d), flush=True)
+
+
+def _roof(bytes_per_launch, ms):
+    gbps = bytes_per_launch / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": gbps / PEAK_HBM_GBPS, "traffic": None}
+
+
+def run_mode(args, wl, plans, units):
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import fully_sharded_amd as F
+    from oracle import fsdp_oracle as O
+    from workloads.configs import ADAMW
+
+    R = wl["R"]
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    P = sum(u.plan.T for u in units)
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+
+    if args.mode == "reshard":
+        # restore the whole model's sharded state (bf16 parameter, fp32
+        # master, m, v) at world size --to-ranks, same layout
+        R2 = args.to_ranks
+        dst_plans = {k: F.Plan(list(k), R2, wl["layout"]) for k in plans}
+        rsh = {k: F.Resharder(plans[k], dst_plans[k]) for k in plans}
+        jobs = []
+        for u in units:
+            k = tuple(u.plan.shapes)
+            S2 = dst_plans[k].S
+            p2 = torch.empty(R2 * S2, dtype=u.param.dtype, device=dev)
+            st2 = rows(3, R2 * S2, torch.float32, dev)
+            jobs.append([(rsh[k], u.param, p2)] + [(rsh[k], a, b) for a, b in
+                                                    zip((u.master, u.m, u.v), st2)])
+
+        def restore():
+            for job in jobs:
+                for rs, a, b in job:
+                    F.fsdp_reshard(rs, a, b, hs)
+
+        for _ in range(args.warmup):
+            restore()
+        ms = _timed(restore, args.steps)
+        fp32_pass = lambda: [F.fsdp_reshard(job[1][0], job[1][1], job[1][2], hs) for job in jobs]
+        ms_launch = _timed(fp32_pass, max(5, args.steps)) / len(jobs)
+        bytes_launch = float(np.mean([u.plan.T for u in units])) * 8
+        u0 = units[0]
+        po = O.plan_layout(list(u0.plan.shapes), R, wl["layout"])
+        po2 = O.plan_layout(list(u0.plan.shapes), R2, wl["layout"])
+        hosts = [_host(x).reshape(R, po.S) for x in (u0.param, u0.master, u0.m, u0.v)]
+        def cpu_work():
+            for h in hosts:
+                O.reshard(po, po2, h)
+            return po.T
+        done, secs, calls = _cpu_loop(cpu_work, budget) if budget else (0, 0, 0)
+        cpu = None if not budget else {
+            "value": done / secs, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} restores of unit 0 (parameter, master, m, v; "
+                      f"R={R} -> {R2}), {done} params in {secs:.2f} s, one thread"}
+        _line(args, wl, f"reshard (restore at R={R2}) params/s and HBM GB/s, {R}->{R2}",
+              P / (ms * 1e-3), ms, {"to_ranks": R2, "params": P,
+                                     "bytes_per_param": 28},
+              {"reshard_fp32": {"avg_ms": ms_launch, "bytes": bytes_launch,
+                                "gbps": bytes_launch / (ms_launch * 1e-3) / 1e9}},
+              _roof(bytes_launch, ms_launch), cpu,
+              {"hbm_gbps": P * 28 / (ms * 1e-3) / 1e9})
+        return
+
+    if args.mode == "accum":
+        K = args.micro
+        if K < 1:
+            raise SystemExit("--micro must be >= 1")
+        T_max = max(p.T for p in plans.values())
+        recv = rows(R, T_max, units[0].param.dtype, dev)
+        accs = [rows(R, u.plan.T, torch.float32, dev) for u in units]
+        calls = [(F.bind_grad_accumulate(u.plan, u.grads, a),
+                  F.bind_gather_unflatten(u.plan, u.param, recv),
+                  F.bind_adamw_shard_step(u.plan, ADAMW, a, u.master, u.m, u.v, u.param))
+                 for u, a in zip(units, accs)]
+        step_no = [0]
+
+        def step():
+            step_no[0] += 1
+            for acc, gather, fused in calls:
+                for k in range(K):
+                    acc(k == 0, hs)
+                gather(hs)
+                fused(step_no[0], hs)
+
+        for _ in range(args.warmup):
+            step()
+        ms = _timed(step, args.steps)
+        ms_acc = _timed(lambda: [c[0](False, hs) for c in calls], max(5, args.steps)) / len(calls)
+        Tm = float(np.mean([u.plan.T for u in units]))
+        acc_bytes = Tm * R * (2 + 4 + 4)
+        step_bytes = P * (R * 6 + (K - 1) * R * 10 + (2 + 2 * R) + (4 * R + 26))
+        u0 = units[0]
+        po = O.plan_layout(list(u0.plan.shapes), R, wl["layout"])
+        hg = [_host(g) for g in u0.grads]
+        st = [_host(x).reshape(R, po.S) for x in (u0.master, u0.m, u0.v)]
+
+        def cpu_work():
+            accs_h = [O.grad_accumulate([hg[r]] * K) for r in range(R)]
+            O.shard_step(po, accs_h, st[0], st[1], st[2], 1, ADAMW, wl["param_dtype"])
+            return po.T
+        done, secs, ncalls = _cpu_loop(cpu_work, budget) if budget else (0, 0, 0)
+        cpu = None if not budget else {
+            "value": done / secs, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ncalls} accumulated steps of unit 0 (K={K}, R={R}), {done} params in "
+                      f"{secs:.2f} s, one thread"}
+        _line(args, wl, f"accumulated-step params/s and HBM GB/s, K={K} micro-batches",
+              P / (ms * 1e-3), ms, {"micro_batches": K, "params": P},
+              {"accumulate": {"avg_ms": ms_acc, "bytes": acc_bytes,
+                              "gbps": acc_bytes / (ms_acc * 1e-3) / 1e9}},
+              _roof(acc_bytes, ms_acc), cpu,
+              {"hbm_gbps": step_bytes / (ms * 1e-3) / 1e9, "step_bytes": step_bytes})
+        return
+
+    if args.mode == "ddp":
+        # every rank holds the full model: R full replicas of parameter,
+        # master, m and v; the gradient all-reduce-average gives every rank
+        # the whole averaged gradient; every rank runs AdamW on all of it.
+        from fully_sharded_amd.step import StepRunner
+        from workloads import gen
+        jobs = []
+        for i, u in enumerate(units):
+            T = u.plan.T
+            rep = F.Plan([(R * T,)], 1, "flat")      # R replicas as one flat array
+            avg = torch.empty(R * T, dtype=torch.float32, device=dev)
+            full = gen.device_master(wl, i, list(u.plan.shapes), dev)
+            master, m, v = rows(3, R * T, torch.float32, dev)
+            master.view(R, T).copy_(full.expand(R, T))
+            m.zero_()
+            v.zero_()
+            param = torch.empty(R * T, dtype=u.param.dtype, device=dev)
+            param.view(R, T).copy_(full.expand(R, T))
+            outs = list(avg.view(R, T).unbind(0))
+            jobs.append((u, rep, avg, outs, (rep, master, m, v, param)))
+        step_no = [0]
+
+        def step():
+            step_no[0] += 1
+            for u, rep, avg, outs, (rp, master, m, v, param) in jobs:
+                F.fsdp_allreduce_avg(u.plan, u.grads, outs, hs)
+                F.fsdp_adamw_shard_step(rp, ADAMW, step_no[0], avg, master, m, v, param,
+                                        grads_are_replicas=False, stream=hs)
+
+        for _ in range(args.warmup):
+            step()
+        ms = _timed(step, args.steps)
+        ms_ar = _timed(lambda: [F.fsdp_allreduce_avg(j[0].plan, j[0].grads, j[3], hs)
+                                for j in jobs], max(5, args.steps)) / len(jobs)
+        Tm = float(np.mean([u.plan.T for u in units]))
+        ar_bytes = Tm * (2 * R + 4 * R)
+        step_bytes = P * (6 * R + 30 * R)
+        # the FSDP step on the same model, same run, for the comparison
+        recv = rows(R, max(p.T for p in plans.values()), units[0].param.dtype, dev)
+        runner = StepRunner(units, ADAMW, [recv])
+        fs = [0]
+
+        def fstep():
+            fs[0] += 1
+            runner.step(fs[0])
+        for _ in range(args.warmup):
+            fstep()
+        ms_fsdp = _timed(fstep, args.steps)
+        S_tot = sum(u.plan.S for u in units)
+        ledger = {
+            "state_bytes_per_rank": {"ddp": 16 * P, "fsdp": 16 * S_tot},
+            "comm_elems_per_rank_per_step": {
+                "ddp_allreduce": 2.0 * (R - 1) / R * P,
+                "fsdp_reshard_after_forward": sum(u.plan.comm_ledger(True)["total"]
+                                                  for u in units),
+                "fsdp_keep_after_forward": sum(u.plan.comm_ledger(False)["total"]
+                                               for u in units)},
+            "hbm_bytes_per_step": {"ddp": step_bytes,
+                                   "fsdp": P * (4 * R + 28)},
+        }
+        u0 = units[0]
+        hg = [_host(g) for g in u0.grads]
+        T0 = u0.plan.T
+        z = np.zeros(T0, np.float32)
+        m0 = _host(jobs[0][4][1])[:T0].copy()
+
+        def cpu_work():
+            avg = O.allreduce_avg(hg)
+            for r in range(R):
+                O.adamw_step(m0, z, z, avg[r], 1, **ADAMW)
+            return T0
+        done, secs, ncalls = _cpu_loop(cpu_work, budget) if budget else (0, 0, 0)
+        cpu = None if not budget else {
+            "value": done / secs, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ncalls} DDP steps of unit 0 (all-reduce + AdamW on {R} replicas), "
+                      f"{done} params in {secs:.2f} s, one thread"}
+        _line(args, wl, "DDP-comparator step params/s (all-reduce + AdamW on every replica)",
+              P / (ms * 1e-3), ms, {"params": P},
+              {"allreduce_avg": {"avg_ms": ms_ar, "bytes": ar_bytes,
+                                 "gbps": ar_bytes / (ms_ar * 1e-3) / 1e9}},
+              _roof(ar_bytes, ms_ar), cpu,
+              {"hbm_gbps": step_bytes / (ms * 1e-3) / 1e9, "step_bytes": step_bytes,
+               "fsdp_ms_per_step_same_run": ms_fsdp, "ddp_over_fsdp_time": ms / ms_fsdp,
+               "ledger": ledger})
+        return
+    raise SystemExit(f"unknown mode {args.mode}")
 
 
 def cpu_baseline(state, R, wl, budget_s):

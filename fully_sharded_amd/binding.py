@@ -436,3 +436,22 @@ def bind_adamw_shard_step(plan: Plan, hp: dict, grads, master, m, v, param_out):
         call._run(*head, int(step), *tail, _stream(stream))
     run.call = call
     return run
+
+
+def bind_grad_accumulate(plan: Plan, grads, acc):
+    """fsdp_grad_accumulate with cached arguments; call as f(first, stream=None)."""
+    if len(grads) != plan.R or len(acc) != plan.R:
+        raise ValueError("need R gradients and R accumulators")
+    dt = _dtype_code(grads[0])
+    for g, a in zip(grads, acc):
+        if g.numel() != plan.T or _dtype_code(g) != dt or a.numel() != plan.T \
+                or a.dtype != torch.float32:
+            raise ValueError("gradient or accumulator size/dtype mismatch")
+    ga = _ptr_array(grads, "grads")
+    aa = _ptr_array(acc, "acc")
+    call = BoundCall("fsdp_grad_accumulate", None, (plan, list(grads), list(acc)))
+
+    def run(first, stream=None):
+        call._run(plan.handle, ga, dt, aa, int(bool(first)), _stream(stream))
+    run.call = call
+    return run
