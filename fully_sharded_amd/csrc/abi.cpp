@@ -206,7 +206,7 @@ fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t ful
     PtrArray dst{};
     dst.p[0] = shards;
     return from_hip(fsdp::launch_copy(w, n_work, full, dst, 1,
-                                      static_cast<int>(dtype_size(full_dtype)), vec, s));
+                                      static_cast<int>(dtype_size(full_dtype)), 16, vec, s));
   }
   return from_hip(fsdp::launch_pack_cast(w, n_work, full, full_dtype, shards, shard_dtype, vec, s));
 }
@@ -235,8 +235,8 @@ fsdp_status fsdp_gather_unflatten(const fsdp_plan* plan, const void* shards, int
   const fsdp_status st = plan->flat_work.device(&w);
   if (st != FSDP_OK) return st;
   return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(plan->flat_work.host.size()), shards,
-                                    dst, plan->R, static_cast<int>(es), vec,
-                                    static_cast<hipStream_t>(stream)));
+                                    dst, plan->R, static_cast<int>(es), plan->gather_lane_bytes,
+                                    vec, static_cast<hipStream_t>(stream)));
 }
 
 fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* grads,
@@ -368,7 +368,7 @@ fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, i
   PtrArray d{};
   d.p[0] = dst;
   return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(rs->work.host.size()), src, d, 1,
-                                    static_cast<int>(es), aligned(src, 16) && aligned(dst, 16),
+                                    static_cast<int>(es), 16, aligned(src, 16) && aligned(dst, 16),
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -24,10 +24,11 @@ struct AdamScalars {
   double lr, eps;
 };
 
-// Copy along work items; es = element size in bytes (2 or 4).  dst holds
-// n_dst pointers (NULL entries are skipped); padding items write zeros.
+// Copy along work items; es = element size in bytes (2 or 4), lane_bytes
+// = 8 or 16 bytes per lane.  dst holds n_dst pointers (NULL entries are
+// skipped); padding items write zeros.
 hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const PtrArray& dst,
-                       int n_dst, int es, bool vec, hipStream_t stream);
+                       int n_dst, int es, int lane_bytes, bool vec, hipStream_t stream);
 
 // Pack with a dtype change (F32 -> BF16 round to nearest even, BF16 -> F32).
 hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, int src_dt,

@@ -161,7 +161,9 @@ fsdp_status build_plan(fsdp_plan* pl) {
     expect += s.len;
   }
   if (expect != pl->T) return FSDP_ERR_INVALID_ARG;
-  emit_items(pl->flat_runs, kFlatChunk, pl->flat_work.host);
+  pl->gather_lane_bytes = pl->T <= kWideGatherMax ? 16 : 8;
+  emit_items(pl->flat_runs, pl->gather_lane_bytes == 16 ? kFlatChunk : kFlatChunk / 2,
+             pl->flat_work.host);
   return FSDP_OK;
 }
 

@@ -72,6 +72,7 @@ struct fsdp_plan {
   std::vector<fsdp::Work> flat_runs;    // flat space [0, T) -> shard space
   fsdp::WorkTable shard_work;           // shard_runs cut into work items
   fsdp::WorkTable flat_work;            // flat_runs cut into work items
+  int32_t gather_lane_bytes = 16;       // bytes per lane of the gather copy
 };
 
 struct fsdp_resharder {
@@ -92,6 +93,13 @@ namespace fsdp {
 // 3M-element one.
 constexpr int64_t kShardChunk = 1024;
 constexpr int64_t kFlatChunk = 2048;
+
+// The gather copies 16 bytes per lane up to this many elements per unit and
+// 8 bytes per lane (1024-element work items) above it.  Measured on MI355X
+// (bf16, 8 receivers): 16-byte lanes lead at 3M and 6M elements (5.40 vs
+// 5.15, 5.60 vs 5.05 TB/s), tie at 12.6M, and trail from 25M on (4.67 vs
+// 5.26 TB/s at 25M, 4.96 vs 5.68 at 100M).
+constexpr int64_t kWideGatherMax = 12582912;
 
 // Build every host-side table of a plan; returns FSDP_OK or an error.
 fsdp_status build_plan(fsdp_plan* pl);
