@@ -227,3 +227,25 @@ def test_resharder_items_match_the_oracle_reshard(Ra, Rb):
 def test_resharder_rejects_different_units():
     with pytest.raises(F.FsdpError):
         F.Resharder(F.Plan([(4, 2)], 2, "flat"), F.Plan([(4, 3)], 2, "flat"))
+
+
+def test_header_compiles_as_c99_and_plans_from_plain_c(tmp_path):
+    """A plain C99 program includes include/fsdp_hip.h, links the library and
+    plans the TransformerBlock FlatParameter of the 4-GPU example."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(F.binding.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_check.c"), "-o", str(exe),
+                    "-L", libdir, "-l:libfsdp_hip.so", "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    assert out[0] == "T 3145728 S 786432 R 4 segments 4"
+    assert out[1:5] == ["offset 0", "offset 786432", "offset 1572864", "offset 2359296"]
+    assert out[5] == "all_gather 2359296"
+    assert out[6] == f"state_bytes {16 * 786432}"
+    assert out[7] == "R=0 -> invalid argument, out NULL"
