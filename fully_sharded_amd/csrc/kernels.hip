@@ -12,9 +12,10 @@
 //   * every streaming access is nontemporal: the data is touched once, and
 //     keeping it out of the caches raised the fused kernel from 4.8 to
 //     5.6 TB/s in isolation;
-//   * lanes whose chunk is cut by the ends of the range, and work items
-//     whose source is misaligned relative to the destination, take an
-//     element-by-element path with the same arithmetic.
+//   * work items whose source is misaligned relative to the destination
+//     funnel each lane's window out of two aligned vector loads; lanes
+//     whose chunk is cut by the ends of the range take an element-by-element
+//     path with the same arithmetic.
 //
 // Reductions are fp32, in rank order 0..R-1 starting from rank 0's value,
 // then one correctly rounded division by R: one lane owns an element and
@@ -46,6 +47,55 @@ __device__ __forceinline__ void st_nt8(void* p, u32x2 x) {
 }
 __device__ __forceinline__ void st_nt16(void* p, u32x4 x) {
   __builtin_nontemporal_store(x, static_cast<u32x4*>(p));
+}
+
+// Misaligned source windows.  A work item whose source offset is not a
+// multiple of the lane's element count relative to its destination still
+// takes vector loads: the W bytes a lane needs start k elements past an
+// aligned W-byte word, so it loads that word and the next one and funnels
+// the wanted bytes out of the pair (v_alignbit).  Both words hold at least
+// one element the lane needs, so nothing outside them is read and no extra
+// page is touched.
+template <int NW, int Q>
+__device__ __forceinline__ void funnel_words(const uint32_t (&w)[2 * NW], uint32_t shift,
+                                             uint32_t (&r)[NW]) {
+#pragma unroll
+  for (int j = 0; j < NW; ++j) r[j] = __builtin_amdgcn_alignbit(w[j + Q + 1], w[j + Q], shift);
+}
+
+// Words [byte, byte + 4*NW) of the 2*NW-word window w (byte uniform).
+template <int NW>
+__device__ __forceinline__ void funnel(const uint32_t (&w)[2 * NW], int byte, uint32_t (&r)[NW]) {
+  const uint32_t shift = static_cast<uint32_t>(byte & 3) * 8u;
+  switch (byte >> 2) {
+    case 0: funnel_words<NW, 0>(w, shift, r); break;
+    case 1: funnel_words<NW, 1>(w, shift, r); break;
+    default:
+      if constexpr (NW == 4) {
+        if ((byte >> 2) == 2)
+          funnel_words<NW, 2>(w, shift, r);
+        else
+          funnel_words<NW, 3>(w, shift, r);
+      }
+      break;
+  }
+}
+
+// 8 or 16 bytes starting `byte` bytes (0 < byte < W, element-aligned) past
+// the W-aligned address p.
+__device__ __forceinline__ u32x2 ld_nt8_shifted(const char* p, int byte) {
+  const u32x2 a = ld_nt8(p), b = ld_nt8(p + 8);
+  const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+  uint32_t r[2];
+  funnel<2>(w, byte, r);
+  return u32x2{r[0], r[1]};
+}
+__device__ __forceinline__ u32x4 ld_nt16_shifted(const char* p, int byte) {
+  const u32x4 a = ld_nt16(p), b = ld_nt16(p + 16);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t r[4];
+  funnel<4>(w, byte, r);
+  return u32x4{r[0], r[1], r[2], r[3]};
 }
 
 // ------------------------------------------------------------- conversions
@@ -87,6 +137,12 @@ struct Io<float> {
       for (int k = 0; k < 4; ++k) p[k] = x[k];
     }
   }
+  // elements [s, s+4) with s % 4 == k != 0
+  __device__ __forceinline__ static void load4s(const float* p, int64_t s, int k, float (&x)[4]) {
+    const u32x4 u = ld_nt16_shifted(reinterpret_cast<const char*>(p + (s - k)), 4 * k);
+    x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+  }
   __device__ __forceinline__ static float load1(const float* p) { return *p; }
   __device__ __forceinline__ static void store1(float* p, float x) { *p = x; }
 };
@@ -114,6 +170,12 @@ struct Io<u16> {
       for (int k = 0; k < 4; ++k) p[k] = static_cast<u16>(f32_to_bf16(x[k]));
     }
   }
+  // elements [s, s+4) with s % 4 == k != 0
+  __device__ __forceinline__ static void load4s(const u16* p, int64_t s, int k, float (&x)[4]) {
+    const u32x2 u = ld_nt8_shifted(reinterpret_cast<const char*>(p + (s - k)), 2 * k);
+    x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+    x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
   __device__ __forceinline__ static float load1(const u16* p) { return bf16_to_f32(*p); }
   __device__ __forceinline__ static void store1(u16* p, float x) {
     *p = static_cast<u16>(f32_to_bf16(x));
@@ -124,13 +186,24 @@ struct Io<u16> {
 // avg[k] = (g_0[s+k] + g_1[s+k] + ... + g_{R-1}[s+k]) / R, fp32, left to
 // right.  RT > 0: R known at compile time (all R loads issued before the
 // adds); RT == 0: any R.
-template <typename G, int RT>
-__device__ __forceinline__ void grad_avg4(const PtrArray& g, int R, int64_t s, bool vec,
+template <typename G, int RT, bool SHIFT = false>
+__device__ __forceinline__ void grad_load4(const PtrArray& g, int q, int64_t s, int k,
+                                           float (&x)[4]) {
+  const G* p = static_cast<const G*>(g.p[q]);
+  if constexpr (SHIFT)
+    Io<G>::load4s(p, s, k, x);
+  else
+    Io<G>::load4(p + s, true, x);
+}
+
+// SHIFT: s % 4 == k != 0 (misaligned source, funnelled vector loads).
+template <typename G, int RT, bool SHIFT = false>
+__device__ __forceinline__ void grad_avg4(const PtrArray& g, int R, int64_t s, int k,
                                           float (&avg)[4]) {
   if constexpr (RT > 0) {
     float x[RT][4];
 #pragma unroll
-    for (int q = 0; q < RT; ++q) Io<G>::load4(static_cast<const G*>(g.p[q]) + s, vec, x[q]);
+    for (int q = 0; q < RT; ++q) grad_load4<G, RT, SHIFT>(g, q, s, k, x[q]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float acc = x[0][k];
@@ -139,10 +212,10 @@ __device__ __forceinline__ void grad_avg4(const PtrArray& g, int R, int64_t s, b
       avg[k] = acc / static_cast<float>(RT);
     }
   } else {
-    Io<G>::load4(static_cast<const G*>(g.p[0]) + s, vec, avg);
+    grad_load4<G, RT, SHIFT>(g, 0, s, k, avg);
     for (int q = 1; q < R; ++q) {
       float x[4];
-      Io<G>::load4(static_cast<const G*>(g.p[q]) + s, vec, x);
+      grad_load4<G, RT, SHIFT>(g, q, s, k, x);
 #pragma unroll
       for (int k = 0; k < 4; ++k) avg[k] = avg[k] + x[k];
     }
@@ -232,14 +305,26 @@ __global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work
   const E* __restrict__ src = static_cast<const E*>(a.src);
   const bool pad = w.src < 0;
   const int64_t delta = w.src - w.dst;
-  const bool vec = a.vec && (pad || (delta % N) == 0);
+  const int k = static_cast<int>(((delta % N) + N) % N);  // source misalignment
+  const bool vec = a.vec != 0;
   const int64_t end = w.dst + w.len;
   const int first = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.n_dst));
   for (int64_t c = w.dst / N + threadIdx.x; c * N < end; c += kThreads) {
     const int64_t e0 = c * N;
     if (vec && e0 >= w.dst && e0 + N <= end) {
       V v = {};
-      if (!pad) v = Lane<W>::load(src + e0 + delta);
+      if (!pad) {
+        const E* sp = src + e0 + delta;
+        if (k == 0) {
+          v = Lane<W>::load(sp);
+        } else {
+          const char* al = reinterpret_cast<const char*>(sp - k);
+          if constexpr (W == 8)
+            v = ld_nt8_shifted(al, k * ES);
+          else
+            v = ld_nt16_shifted(al, k * ES);
+        }
+      }
       for (int k = 0, r = first; k < a.n_dst; ++k, r = r + 1 == a.n_dst ? 0 : r + 1) {
         E* d = static_cast<E*>(const_cast<void*>(a.dst.p[r]));
         if (d) Lane<W>::store(d + e0, v);
@@ -291,13 +376,17 @@ __global__ __launch_bounds__(kThreads) void k_pack_cast(const Work* __restrict__
   D* __restrict__ dst = static_cast<D*>(a.dst);
   const bool pad = w.src < 0;
   const int64_t delta = w.src - w.dst;
-  // a source misaligned relative to the destination takes the element path
-  const bool vec = a.vec != 0 && (pad || (delta % kEPL) == 0);
+  const int k = static_cast<int>(((delta % kEPL) + kEPL) % kEPL);  // source misalignment
   for_chunks(
-      w, vec,
+      w, a.vec != 0,
       [&](int64_t e0) {
         float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (!pad) Io<S>::load4(src + e0 + delta, true, x);
+        if (!pad) {
+          if (k == 0)
+            Io<S>::load4(src + e0 + delta, true, x);
+          else
+            Io<S>::load4s(src, e0 + delta, k, x);
+        }
         Io<D>::store4(dst + e0, true, x);
       },
       [&](int64_t e) { Io<D>::store1(dst + e, pad ? 0.0f : Io<S>::load1(src + e + delta)); });
@@ -311,14 +400,14 @@ struct RsArgs {
   int vec;
 };
 
-template <typename G, int RT, bool PAD>
-__device__ __forceinline__ void rs_item(const Work& w, const RsArgs& a, bool vec) {
+template <typename G, int RT, bool PAD, bool SHIFT>
+__device__ __forceinline__ void rs_item(const Work& w, const RsArgs& a, int k) {
   const int64_t delta = w.src - w.dst;
   for_chunks(
-      w, vec,
+      w, a.vec != 0,
       [&](int64_t e0) {
         float avg[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (!PAD) grad_avg4<G, RT>(a.g, a.R, e0 + delta, true, avg);
+        if constexpr (!PAD) grad_avg4<G, RT, SHIFT>(a.g, a.R, e0 + delta, k, avg);
         Io<float>::store4(a.out + e0, true, avg);
       },
       [&](int64_t e) { a.out[e] = PAD ? 0.0f : grad_avg1<G, RT>(a.g, a.R, e + delta); });
@@ -327,12 +416,13 @@ __device__ __forceinline__ void rs_item(const Work& w, const RsArgs& a, bool vec
 template <typename G, int RT>
 __global__ __launch_bounds__(kThreads) void k_rs_avg(const Work* __restrict__ work, RsArgs a) {
   const Work w = work[blockIdx.x];
-  if (w.src < 0) {
-    rs_item<G, RT, true>(w, a, a.vec != 0);
-  } else {
-    // a source misaligned relative to the destination takes the element path
-    rs_item<G, RT, false>(w, a, a.vec != 0 && ((w.src - w.dst) % kEPL) == 0);
-  }
+  const int k = static_cast<int>((((w.src - w.dst) % kEPL) + kEPL) % kEPL);
+  if (w.src < 0)
+    rs_item<G, RT, true, false>(w, a, 0);
+  else if (k == 0)
+    rs_item<G, RT, false, false>(w, a, 0);
+  else
+    rs_item<G, RT, false, true>(w, a, k);
 }
 
 // ------------------------------------------------------------------ AdamW
@@ -395,19 +485,19 @@ struct FusedArgs {
 // One work item of the fused step.  In a whole chunk every load (master, m,
 // v, then the R gradient replicas) is issued before any of them is used, so
 // a wave waits for memory once per chunk.  PAD: padding, no gradient (g = 0).
-template <typename G, typename P, int RT, bool PAD>
-__device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, bool vec) {
+template <typename G, typename P, int RT, bool PAD, bool SHIFT>
+__device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, int k) {
   P* __restrict__ param = static_cast<P*>(a.param);
   const int64_t delta = w.src - w.dst;
   for_chunks(
-      w, vec,
+      w, a.vec != 0,
       [&](int64_t e0) {
         float p[4], m[4], v[4];
         Io<float>::load4(a.master + e0, true, p);
         Io<float>::load4(a.m + e0, true, m);
         Io<float>::load4(a.v + e0, true, v);
         float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (!PAD) grad_avg4<G, RT>(a.g, a.R, e0 + delta, true, g);
+        if constexpr (!PAD) grad_avg4<G, RT, SHIFT>(a.g, a.R, e0 + delta, k, g);
 #pragma unroll
         for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], a.sc);
         Io<float>::store4(a.master + e0, true, p);
@@ -429,12 +519,13 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, bo
 template <typename G, typename P, int RT>
 __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work, FusedArgs a) {
   const Work w = work[blockIdx.x];
-  if (w.src < 0) {
-    fused_item<G, P, RT, true>(w, a, a.vec != 0);
-  } else {
-    // a source misaligned relative to the destination takes the element path
-    fused_item<G, P, RT, false>(w, a, a.vec != 0 && ((w.src - w.dst) % kEPL) == 0);
-  }
+  const int k = static_cast<int>((((w.src - w.dst) % kEPL) + kEPL) % kEPL);
+  if (w.src < 0)
+    fused_item<G, P, RT, true, false>(w, a, 0);
+  else if (k == 0)
+    fused_item<G, P, RT, false, false>(w, a, 0);
+  else
+    fused_item<G, P, RT, false, true>(w, a, k);
 }
 
 // ------------------------------------------------- gradient accumulation
@@ -492,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void k_allreduce(ArArgs a) {
   const int R = RT > 0 ? RT : a.R;
   if (a.vec && e0 + kEPL <= a.T) {
     float avg[4];
-    grad_avg4<G, RT>(a.g, a.R, e0, true, avg);
+    grad_avg4<G, RT>(a.g, a.R, e0, 0, avg);
     for (int r = 0; r < R; ++r)
       Io<O>::store4(static_cast<O*>(const_cast<void*>(a.out.p[r])) + e0, true, avg);
   } else {
