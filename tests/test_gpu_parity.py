@@ -473,3 +473,33 @@ def test_group4096_flat_r8_full_size_sampled():
         assert_bf16_within_ulp(gp, O.bf16_rne(p0), f"param t={t}")
         assert_bitexact(gp, O.bf16_rne(to_host(md[idx])), "param = RNE(master)")
         banner(f"group4096 step {t} ok")
+
+
+@pytest.mark.parametrize("layout", ["per_param", "flat"])
+def test_wide_unit_gather_with_misaligned_ranks(layout):
+    """A unit above 12.6M elements (the gather's 8-byte-lane regime); per
+    parameter at R=3 its shard length is odd, so ranks 1 and 2 read
+    misaligned sources.  Gather and pack bit-exact, bf16 and fp32."""
+    shapes = [(4099, 4099), (10,)]
+    R = 3
+    po = O.plan_layout(shapes, R, layout)
+    pg = F.Plan(shapes, R, layout)
+    assert po.T > 12582912
+    if layout == "per_param":
+        assert po.S % 4 != 0      # ranks 1 and 2 misaligned for 4-element lanes
+    banner(f"wide gather {layout}: T={po.T} S={po.S}")
+    rng = np.random.default_rng(99)
+    for dt in ("bf16", "f32"):
+        full = rng.standard_normal(po.T).astype(np.float32)
+        if dt == "bf16":
+            full = O.bf16_rne(full)
+        sh = torch.empty(R * po.S, dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                         device=DEV)
+        F.fsdp_shard_pack(pg, to_dev(full), sh)
+        sh_o = O.shard_pack(po, full)
+        assert_bitexact(to_host(sh).reshape(R, po.S), sh_o, f"pack {dt}")
+        recv = [torch.empty(po.T, dtype=sh.dtype, device=DEV) for _ in range(R)]
+        F.fsdp_gather_unflatten(pg, sh, recv)
+        want, _ = O.gather_unflatten(po, sh_o)
+        for r in range(R):
+            assert_bitexact(to_host(recv[r]), want, f"gather {dt} receiver {r}")
