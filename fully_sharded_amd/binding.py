@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 
 import torch
 
@@ -169,8 +170,9 @@ class Plan:
         return self._h
 
     def __del__(self):
+        # at interpreter exit the HIP runtime may already be gone: leak then
         h = getattr(self, "_h", None)
-        if h is not None and _lib is not None:
+        if h is not None and _lib is not None and not sys.is_finalizing():
             _lib.fsdp_plan_destroy(h)
             self._h = None
 
@@ -243,7 +245,7 @@ class Resharder:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and _lib is not None:
+        if h is not None and _lib is not None and not sys.is_finalizing():
             _lib.fsdp_reshard_destroy(h)
             self._h = None
 

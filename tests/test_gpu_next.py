@@ -170,3 +170,23 @@ def test_allreduce_avg_bit_exact(R, gdt, odt):
     for r in range(R):
         w = O.bf16_rne(want[r]) if odt == "bf16" else want[r]
         assert_bitexact(to_host(out[r]), w, f"allreduce rank {r}")
+
+
+def test_new_ops_reject_bad_arguments_before_launch():
+    pg = F.Plan([(16, 4)], 2, "flat")
+    other = F.Plan([(16, 4)], 4, "per_param")
+    rs = F.Resharder(pg, other)
+    buf = torch.zeros(2 * pg.S + 4 * other.S, device=DEV)
+    src = buf[:2 * pg.S]
+    with pytest.raises(F.FsdpError):        # source and destination overlap
+        F.fsdp_reshard(rs, src, buf[1:1 + 4 * other.S])
+    g = [torch.zeros(pg.T, device=DEV) for _ in range(2)]
+    with pytest.raises(F.FsdpError):        # an output aliases a gradient
+        F.fsdp_allreduce_avg(pg, g, [g[0], torch.zeros(pg.T, device=DEV)])
+    o = torch.zeros(pg.T, device=DEV)
+    with pytest.raises(F.FsdpError):        # two outputs are one buffer
+        F.fsdp_allreduce_avg(pg, g, [o, o])
+    with pytest.raises(ValueError):         # dtype mismatch, caught by the binding
+        F.fsdp_reshard(rs, src, torch.zeros(4 * other.S, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(buf) == 0
