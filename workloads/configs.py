@@ -96,6 +96,16 @@ WORKLOADS = {
         cid=6, units=[BLOCK_512] * 12, R=8, layout=FLAT,
         grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3,
         master_init="fan_in"),
+    # the same 12-layer model wrapped at other granularities (the FSDP unit
+    # decides what one all-gather covers): the whole model as one unit, and
+    # one unit per parameter
+    "model12_whole_r8": dict(
+        cid=8, units=[[(f"l{i}.{n}", s) for i in range(12) for n, s in BLOCK_512]], R=8,
+        layout=PER_PARAM, grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3,
+        master_init="fan_in"),
+    "model12_perparam_r8": dict(
+        cid=9, units=[[p] for _ in range(12) for p in BLOCK_512], R=8, layout=PER_PARAM,
+        grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3, master_init="fan_in"),
     "group4096_flat_r8": dict(
         cid=7, units=[GROUP_4096], R=8, layout=FLAT,
         grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3,
