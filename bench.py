@@ -468,18 +468,34 @@ def run_mode(args, wl, plans, units):
             st2 = rows(3, R2 * S2, torch.float32, dev)
             jobs.append([(rsh[k], u.param, p2)] + [(rsh[k], a, b) for a, b in
                                                     zip((u.master, u.m, u.v), st2)])
+        # one launch per resharder and dtype: the bf16 parameters of every
+        # unit, then the fp32 master, m and v of every unit
+        batches = []
+        for k, rs in rsh.items():
+            pairs = [pr for job in jobs for pr in job if pr[0] is rs]
+            for want in (units[0].param.dtype, torch.float32):
+                sel = [pr for pr in pairs if pr[1].dtype == want]
+                for i in range(0, len(sel), 64):
+                    batches.append((rs, [pr[1] for pr in sel[i:i + 64]],
+                                    [pr[2] for pr in sel[i:i + 64]]))
 
         def restore():
-            for job in jobs:
-                for rs, a, b in job:
-                    F.fsdp_reshard(rs, a, b, hs)
+            for rs, srcs, dsts in batches:
+                F.fsdp_reshard_batch(rs, srcs, dsts, hs)
 
         for _ in range(args.warmup):
             restore()
         ms = _timed(restore, args.steps)
-        fp32_pass = lambda: [F.fsdp_reshard(job[1][0], job[1][1], job[1][2], hs) for job in jobs]
-        ms_launch = _timed(fp32_pass, max(5, args.steps)) / len(jobs)
-        bytes_launch = float(np.mean([u.plan.T for u in units])) * 8
+        # the dominant launch: the largest fp32 batch (master, m, v of every
+        # unit), T*4 bytes read and T*4 written per array
+        big = max((b for b in batches if b[1][0].dtype == torch.float32),
+                  key=lambda b: len(b[1]))
+        # timed alternating with a second copy of its buffers, so the 256 MB
+        # last-level cache cannot serve what the previous launch touched
+        big2 = (big[0], [a.clone() for a in big[1]], [torch.empty_like(b) for b in big[2]])
+        ms_launch = _timed(lambda: [F.fsdp_reshard_batch(b[0], b[1], b[2], hs)
+                                    for b in (big, big2)], max(5, args.steps)) / 2
+        bytes_launch = float(big[0].src_plan.T * 8 * len(big[1]))
         u0 = units[0]
         po = O.plan_layout(list(u0.plan.shapes), R, wl["layout"])
         po2 = O.plan_layout(list(u0.plan.shapes), R2, wl["layout"])
@@ -495,8 +511,9 @@ def run_mode(args, wl, plans, units):
                       f"R={R} -> {R2}), {done} params in {secs:.2f} s, one thread"}
         _line(args, wl, f"reshard (restore at R={R2}) params/s and HBM GB/s, {R}->{R2}",
               P / (ms * 1e-3), ms, {"to_ranks": R2, "params": P,
-                                     "bytes_per_param": 28},
-              {"reshard_fp32": {"avg_ms": ms_launch, "bytes": bytes_launch,
+                                     "bytes_per_param": 28, "launches": len(batches)},
+              {"reshard_fp32_batch": {"avg_ms": ms_launch, "bytes": bytes_launch,
+                                      "arrays": len(big[1]),
                                 "gbps": bytes_launch / (ms_launch * 1e-3) / 1e9}},
               _roof(bytes_launch, ms_launch), cpu,
               {"hbm_gbps": P * 28 / (ms * 1e-3) / 1e9})

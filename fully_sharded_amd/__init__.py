@@ -10,6 +10,6 @@ fsdp_grad_accumulate and fsdp_allreduce_avg (the DDP comparator).
 from .binding import (  # noqa: F401
     BF16, F32, FLAT, PER_PARAM, FsdpError, Plan, Resharder, bind_adamw_shard_step,
     bind_gather_unflatten, bind_grad_accumulate, fsdp_adamw_shard_step, fsdp_allreduce_avg, fsdp_grad_accumulate,
-    fsdp_reshard, fsdp_reshard_plan,
+    fsdp_reshard, fsdp_reshard_batch, fsdp_reshard_plan,
     fsdp_gather_unflatten, fsdp_plan_layout, fsdp_reduce_scatter_avg, fsdp_shard_pack, lib,
 )

@@ -85,6 +85,10 @@ _SIGS = {
                                           ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "fsdp_reshard": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int32, ctypes.c_void_p]),
+    "fsdp_reshard_batch": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
+                                          ctypes.c_void_p]),
     "fsdp_grad_accumulate": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
                                             ctypes.c_int32, ctypes.c_void_p]),
@@ -266,6 +270,21 @@ def fsdp_reshard(rs: Resharder, src: torch.Tensor, dst: torch.Tensor, stream=Non
         raise ValueError("src and dst dtypes differ")
     _check("fsdp_reshard", lib().fsdp_reshard(rs.handle, _dev(src, "src"), _dev(dst, "dst"),
                                               _dtype_code(src), _stream(stream)))
+
+
+def fsdp_reshard_batch(rs: Resharder, srcs, dsts, stream=None):
+    """dsts[i] = reshard of srcs[i] for up to 64 same-dtype arrays, one launch."""
+    if len(srcs) != len(dsts) or not srcs:
+        raise ValueError("need as many destinations as sources")
+    dt = _dtype_code(srcs[0])
+    for a, b in zip(srcs, dsts):
+        if a.numel() != rs.src_plan.R * rs.src_plan.S or b.numel() != rs.dst_plan.R * rs.dst_plan.S:
+            raise ValueError("size mismatch with the plans")
+        if _dtype_code(a) != dt or _dtype_code(b) != dt:
+            raise ValueError("all arrays must have one dtype")
+    _check("fsdp_reshard_batch",
+           lib().fsdp_reshard_batch(rs.handle, len(srcs), _ptr_array(srcs, "srcs"),
+                                    _ptr_array(dsts, "dsts"), dt, _stream(stream)))
 
 
 def fsdp_grad_accumulate(plan: Plan, grads, acc, first: bool, stream=None):

@@ -372,6 +372,35 @@ fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, i
                                     static_cast<hipStream_t>(stream)));
 }
 
+fsdp_status fsdp_reshard_batch(const fsdp_resharder* rs, int32_t n, const void* const* srcs,
+                               void* const* dsts, int32_t dtype, void* stream) {
+  if (!rs || !srcs || !dsts || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
+  if (n < 1 || n > FSDP_MAX_RANKS) return n < 1 ? FSDP_ERR_INVALID_ARG : FSDP_ERR_UNSUPPORTED;
+  const int64_t es = dtype_size(dtype);
+  std::vector<Range> ins, outs;
+  PtrArray s{}, d{};
+  bool vec = true;
+  for (int i = 0; i < n; ++i) {
+    if (!srcs[i] || !dsts[i] || !aligned(srcs[i], es) || !aligned(dsts[i], es))
+      return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(srcs[i], 16) && aligned(dsts[i], 16);
+    ins.push_back(range_of(srcs[i], rs->R_from * rs->S_from * es));
+    outs.push_back(range_of(dsts[i], rs->R_to * rs->S_to * es));
+    s.p[i] = srcs[i];
+    d.p[i] = dsts[i];
+  }
+  if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
+  for (const Range& o : outs)
+    for (const Range& x : ins)
+      if (overlap(o, x)) return FSDP_ERR_INVALID_ARG;
+  const Work* w = nullptr;
+  const fsdp_status st = rs->work.device(&w);
+  if (st != FSDP_OK) return st;
+  return from_hip(fsdp::launch_copy_pairs(w, static_cast<int64_t>(rs->work.host.size()), s, d, n,
+                                          static_cast<int>(es), vec,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 fsdp_status fsdp_grad_accumulate(const fsdp_plan* plan, const void* const* grads,
                                  int32_t grad_dtype, float* const* acc, int32_t first,
                                  void* stream) {

@@ -343,6 +343,43 @@ __global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work
   }
 }
 
+// The same copy for up to 64 independent (source, destination) pairs that
+// share one work table: blockIdx.y picks the pair.
+struct PairArgs {
+  PtrArray src;
+  PtrArray dst;
+  int vec;
+};
+
+template <int ES>
+__global__ __launch_bounds__(kThreads) void k_copy_pairs(const Work* __restrict__ work,
+                                                         PairArgs a) {
+  using E = typename Raw<ES>::E;
+  constexpr int N = 16 / ES;
+  const Work w = work[blockIdx.x];
+  const E* __restrict__ src = static_cast<const E*>(a.src.p[blockIdx.y]);
+  E* __restrict__ dst = static_cast<E*>(const_cast<void*>(a.dst.p[blockIdx.y]));
+  const bool pad = w.src < 0;
+  const int64_t delta = w.src - w.dst;
+  const int k = static_cast<int>(((delta % N) + N) % N);
+  const int64_t end = w.dst + w.len;
+  for (int64_t c = w.dst / N + threadIdx.x; c * N < end; c += kThreads) {
+    const int64_t e0 = c * N;
+    if (a.vec && e0 >= w.dst && e0 + N <= end) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (!pad) {
+        const E* sp = src + e0 + delta;
+        v = k == 0 ? ld_nt16(sp) : ld_nt16_shifted(reinterpret_cast<const char*>(sp - k), k * ES);
+      }
+      st_nt16(dst + e0, v);
+    } else {
+      const int64_t lo = e0 > w.dst ? e0 : w.dst;
+      const int64_t hi = e0 + N < end ? e0 + N : end;
+      for (int64_t e = lo; e < hi; ++e) dst[e] = pad ? E(0) : src[e + delta];
+    }
+  }
+}
+
 // Loop of the arithmetic kernels over one work item: lane chunks of kEPL
 // elements aligned in the destination index space.  body4(e0) handles a
 // whole aligned chunk, body1(e) one element.
@@ -738,6 +775,19 @@ hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt
   void* args[] = {&a};
   return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0,
                          stream);
+}
+
+hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& src,
+                             const PtrArray& dst, int n_pairs, int es, bool vec,
+                             hipStream_t stream) {
+  if (n_work <= 0 || n_pairs <= 0) return hipSuccess;
+  if (n_work > 0x7fffffff || n_pairs > FSDP_MAX_RANKS) return hipErrorInvalidValue;
+  PairArgs a{src, dst, vec ? 1 : 0};
+  const void* fn = es == 2 ? reinterpret_cast<const void*>(&k_copy_pairs<2>)
+                           : reinterpret_cast<const void*>(&k_copy_pairs<4>);
+  void* args[] = {const_cast<Work**>(&work), &a};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(n_work), static_cast<unsigned>(n_pairs)),
+                         dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace fsdp

@@ -57,4 +57,10 @@ hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_d
 hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt,
                             const PtrArray& out, int out_dt, bool vec, hipStream_t stream);
 
+// The copy for n_pairs (source, destination) pairs sharing one work table
+// (one destination each), 16 bytes per lane.
+hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& src,
+                             const PtrArray& dst, int n_pairs, int es, bool vec,
+                             hipStream_t stream);
+
 }  // namespace fsdp

@@ -230,6 +230,13 @@ fsdp_status fsdp_reshard_items(const fsdp_resharder* rs, int64_t* out, int64_t c
 fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, int32_t dtype,
                          void* stream);
 
+/* fsdp_reshard for n independent arrays of one dtype in one launch (e.g.
+ * master, m and v of every unit sharing the plans): dst[i] = reshard of
+ * src[i].  1 <= n <= 64 (larger n: FSDP_ERR_UNSUPPORTED); destinations
+ * pairwise disjoint and disjoint from every source. */
+fsdp_status fsdp_reshard_batch(const fsdp_resharder* rs, int32_t n, const void* const* srcs,
+                               void* const* dsts, int32_t dtype, void* stream);
+
 /* Gradient accumulation over micro-batches: acc[r][i] = g[r][i] when first
  * != 0, else acc[r][i] + g[r][i], in fp32, for every rank r < R and i < T
  * (zwjcode FSDP2 page, section 08: every micro-batch runs forward and

@@ -190,3 +190,18 @@ def test_new_ops_reject_bad_arguments_before_launch():
         F.fsdp_reshard(rs, src, torch.zeros(4 * other.S, dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
     assert torch.count_nonzero(buf) == 0
+
+
+def test_reshard_batch_moves_many_arrays_in_one_launch():
+    shapes = shapes_of(BLOCK_512)
+    pa, pb = O.plan_layout(shapes, 8, "per_param"), O.plan_layout(shapes, 3, "flat")
+    rs = F.Resharder(F.Plan(shapes, 8, "per_param"), F.Plan(shapes, 3, "flat"))
+    rng = np.random.default_rng(77)
+    hs = [O.shard_pack(pa, rng.standard_normal(pa.T).astype(np.float32)) for _ in range(5)]
+    srcs = [to_dev(h.reshape(-1)) for h in hs]
+    dsts = [torch.full((3 * pb.S,), 5.0, device=DEV) for _ in hs]
+    F.fsdp_reshard_batch(rs, srcs, dsts)
+    for h, d in zip(hs, dsts):
+        assert_bitexact(to_host(d).reshape(3, pb.S), O.reshard(pa, pb, h), "reshard batch")
+    with pytest.raises(F.FsdpError):          # two destinations are one buffer
+        F.fsdp_reshard_batch(rs, srcs[:2], [dsts[0], dsts[0]])
