@@ -36,10 +36,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="model12_r8")
-    ap.add_argument("--schedule", choices=("serial", "prefetch"), default="serial",
+    ap.add_argument("--schedule", choices=("serial", "prefetch", "graph"), default="serial",
                     help="serial: per unit gather then fused step on one stream; prefetch: "
                          "gathers on their own stream run ahead of the fused steps, into a "
-                         "double receive buffer")
+                         "double receive buffer; graph: the serial sequence replayed as one "
+                         "HIP graph per step")
     ap.add_argument("--gathers-per-step", type=int, choices=(1, 2), default=1,
                     help="1: parameters kept from forward to backward "
                          "(reshard_after_forward=False); 2: freed after forward and "
@@ -347,6 +348,8 @@ def main():
             "schedule": args.schedule,
             "gathers_per_step": args.gathers_per_step,
             "launches_per_step": (args.gathers_per_step + 1) * len(units),
+            "host_calls_per_step": 2 if args.schedule == "graph"
+            else (args.gathers_per_step + 1) * len(units),
             "buffer_copies": len(runners),
             "step": "per unit: gather+unflatten to R receivers, fused RS-avg+AdamW+recast",
         },

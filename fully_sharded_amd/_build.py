@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfsdp_hip.so")
-SOURCES = ["plan.cpp", "kernels.hip", "abi.cpp"]
+SOURCES = ["plan.cpp", "kernels.hip", "abi.cpp", "graph.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -89,6 +89,20 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_void_p),
                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                           ctypes.c_void_p]),
+    "fsdp_step_graph_create": (ctypes.c_int, [ctypes.POINTER(AdamWHParams),
+                                              ctypes.POINTER(ctypes.c_void_p)]),
+    "fsdp_step_graph_destroy": (None, [ctypes.c_void_p]),
+    "fsdp_step_graph_add_gather": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_int32,
+                                                  ctypes.POINTER(ctypes.c_void_p)]),
+    "fsdp_step_graph_add_adamw": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_int32]),
+    "fsdp_step_graph_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                            ctypes.POINTER(ctypes.c_int64)]),
+    "fsdp_step_graph_launch": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
     "fsdp_grad_accumulate": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
                                             ctypes.c_int32, ctypes.c_void_p]),
@@ -476,3 +490,76 @@ def bind_grad_accumulate(plan: Plan, grads, acc):
         call._run(plan.handle, ga, dt, aa, int(bool(first)), _stream(stream))
     run.call = call
     return run
+
+
+class StepGraph:
+    """fsdp_step_graph_*: a unit loop's gathers and AdamW steps recorded once
+    and replayed per training step with one graph launch.
+
+    The graph keeps the device pointers of every tensor added; this object
+    holds references to them (and to the plans) so they stay alive."""
+
+    def __init__(self, hp: dict):
+        self._h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                               hp["weight_decay"])
+        h = ctypes.c_void_p()
+        _check("fsdp_step_graph_create", lib().fsdp_step_graph_create(ctypes.byref(self._h),
+                                                                       ctypes.byref(h)))
+        self._handle = h
+        self._keep = []
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h and h.value and _lib is not None and not sys.is_finalizing():
+            _lib.fsdp_step_graph_destroy(h)
+            self._handle = None
+
+    def add_gather(self, plan: Plan, shards: torch.Tensor, full_out):
+        """Record fsdp_gather_unflatten(plan, shards, full_out)."""
+        if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
+            raise ValueError("size mismatch with the plan")
+        for t in full_out:
+            if t is not None and (t.numel() < plan.T or t.dtype != shards.dtype):
+                raise ValueError("receiver size or dtype mismatch")
+        _check("fsdp_step_graph_add_gather",
+               lib().fsdp_step_graph_add_gather(self._handle, plan.handle,
+                                                ctypes.c_void_p(_dev(shards, "shards")),
+                                                _dtype_code(shards),
+                                                _ptr_array(full_out, "full_out")))
+        self._keep.append((plan, shards, list(full_out)))
+
+    def add_adamw(self, plan: Plan, grads, master, m, v, param_out):
+        """Record the fused fsdp_adamw_shard_step over R gradient replicas."""
+        n = plan.R * plan.S
+        for t, nm in ((master, "master"), (m, "m"), (v, "v")):
+            if t.numel() != n or t.dtype != torch.float32:
+                raise ValueError(f"{nm} must be fp32 with R*S elements")
+        if param_out.numel() != n or len(grads) != plan.R:
+            raise ValueError("size mismatch with the plan")
+        dt = _dtype_code(grads[0])
+        for g in grads:
+            if g.numel() != plan.T or _dtype_code(g) != dt:
+                raise ValueError("gradient size or dtype mismatch")
+        _check("fsdp_step_graph_add_adamw",
+               lib().fsdp_step_graph_add_adamw(
+                   self._handle, plan.handle, _ptr_array(grads, "grads"), dt, 1,
+                   ctypes.c_void_p(_dev(master, "master")), ctypes.c_void_p(_dev(m, "m")),
+                   ctypes.c_void_p(_dev(v, "v")), ctypes.c_void_p(_dev(param_out, "param_out")),
+                   _dtype_code(param_out)))
+        self._keep.append((plan, list(grads), master, m, v, param_out))
+
+    def info(self):
+        """(kernel nodes, AdamW nodes) recorded so far."""
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        _check("fsdp_step_graph_info",
+               lib().fsdp_step_graph_info(self._handle, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def launch(self, step: int, stream=None):
+        """Replay every recorded call with AdamW step counter `step`."""
+        _check("fsdp_step_graph_launch",
+               lib().fsdp_step_graph_launch(self._handle, int(step), _stream(stream)))

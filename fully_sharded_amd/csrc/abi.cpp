@@ -10,6 +10,7 @@
 
 #include "fsdp_hip.h"
 #include "kernels.hpp"
+#include "ops.hpp"
 #include "plan.hpp"
 
 using fsdp::AdamScalars;
@@ -41,13 +42,120 @@ bool any_overlap(const std::vector<Range>& rs) {
   return false;
 }
 
-fsdp_status from_hip(hipError_t e) {
+fsdp_status from_hip(hipError_t e) { return fsdp::status_of(e); }
+
+}  // namespace
+
+namespace fsdp {
+
+fsdp_status status_of(hipError_t e) {
   if (e == hipSuccess) return FSDP_OK;
   (void)hipGetLastError();
   return e == hipErrorOutOfMemory ? FSDP_ERR_OUT_OF_MEMORY : FSDP_ERR_HIP;
 }
 
-}  // namespace
+fsdp_status check_hparams(const fsdp_adamw_hparams* hp) {
+  if (!hp) return FSDP_ERR_INVALID_ARG;
+  const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps,
+               wd = hp->weight_decay;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || lr < 0 ||
+      !(b1 >= 0 && b1 < 1) || !(b2 >= 0 && b2 < 1) || !(eps > 0) || wd < 0)
+    return FSDP_ERR_INVALID_ARG;
+  return FSDP_OK;
+}
+
+fsdp_status adam_scalars(const fsdp_adamw_hparams* hp, int64_t step, AdamScalars* sc) {
+  const fsdp_status st = check_hparams(hp);
+  if (st != FSDP_OK) return st;
+  if (step < 1) return FSDP_ERR_INVALID_ARG;
+  const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps,
+               wd = hp->weight_decay;
+  const double t = static_cast<double>(step);
+  sc->decay = 1.0 - lr * wd;
+  sc->beta1 = b1;
+  sc->omb1 = 1.0 - b1;
+  sc->beta2 = b2;
+  sc->omb2 = 1.0 - b2;
+  sc->bc1 = 1.0 - std::pow(b1, t);
+  sc->bc2 = 1.0 - std::pow(b2, t);
+  sc->lr = lr;
+  sc->eps = eps;
+  if (!(sc->bc1 > 0) || !(sc->bc2 > 0)) return FSDP_ERR_INVALID_ARG;
+  return FSDP_OK;
+}
+
+fsdp_status gather_impl(const fsdp_plan* plan, const void* shards, int32_t dtype,
+                        void* const* full_out, const Sink& sink) {
+  if (!plan || !shards || !full_out || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
+  const int64_t es = dtype_size(dtype);
+  if (!aligned(shards, es)) return FSDP_ERR_INVALID_ARG;
+  std::vector<Range> ranges{range_of(shards, plan->R * plan->S * es)};
+  PtrArray dst{};
+  bool vec = aligned(shards, 16);
+  int n = 0;
+  for (int r = 0; r < plan->R; ++r) {
+    void* d = full_out[r];
+    dst.p[r] = d;
+    if (!d) continue;
+    if (!aligned(d, es)) return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(d, 16);
+    ranges.push_back(range_of(d, plan->T * es));
+    ++n;
+  }
+  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
+  if (n == 0) return FSDP_OK;
+  const Work* w = nullptr;
+  const fsdp_status st = plan->flat_work.device(&w);
+  if (st != FSDP_OK) return st;
+  return status_of(launch_copy(w, static_cast<int64_t>(plan->flat_work.host.size()), shards, dst,
+                               plan->R, static_cast<int>(es), plan->gather_lane_bytes, vec, sink));
+}
+
+fsdp_status adamw_impl(const fsdp_plan* plan, const AdamScalars& sc, const AdamScalars* scp,
+                       const void* const* grads, int32_t grad_dtype, int32_t grads_are_replicas,
+                       float* master, float* m, float* v, void* param_out, int32_t param_dtype,
+                       const Sink& sink) {
+  if (!plan || !grads || !master || !m || !v || !param_out) return FSDP_ERR_INVALID_ARG;
+  if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype)) return FSDP_ERR_INVALID_ARG;
+  if (grads_are_replicas != 0 && grads_are_replicas != 1) return FSDP_ERR_INVALID_ARG;
+  const int64_t n = plan->R * plan->S;
+  const int64_t pes = dtype_size(param_dtype);
+  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(param_out, pes))
+    return FSDP_ERR_INVALID_ARG;
+  std::vector<Range> ranges{range_of(master, n * 4), range_of(m, n * 4), range_of(v, n * 4),
+                            range_of(param_out, n * pes)};
+  bool vec = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) && aligned(param_out, 16);
+  PtrArray g{};
+  if (grads_are_replicas) {
+    const int64_t ges = dtype_size(grad_dtype);
+    for (int q = 0; q < plan->R; ++q) {
+      if (!grads[q] || !aligned(grads[q], ges)) return FSDP_ERR_INVALID_ARG;
+      const Range gr = range_of(grads[q], plan->T * ges);
+      for (const Range& o : ranges)
+        if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
+      vec = vec && aligned(grads[q], 16);
+      g.p[q] = grads[q];
+    }
+  } else {
+    if (grad_dtype != FSDP_F32 || !grads[0] || !aligned(grads[0], 4)) return FSDP_ERR_INVALID_ARG;
+    const Range gr = range_of(grads[0], n * 4);
+    for (const Range& o : ranges)
+      if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
+    vec = vec && aligned(grads[0], 16);
+  }
+  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
+  if (!grads_are_replicas)
+    return status_of(launch_adamw(n, static_cast<const float*>(grads[0]), master, m, v, param_out,
+                                  param_dtype, sc, scp, vec, sink));
+  const Work* w = nullptr;
+  const fsdp_status st = plan->shard_work.device(&w);
+  if (st != FSDP_OK) return st;
+  return status_of(launch_fused(w, static_cast<int64_t>(plan->shard_work.host.size()), g, plan->R,
+                                grad_dtype, master, m, v, param_out, param_dtype, sc, scp, vec,
+                                sink));
+}
+
+}  // namespace fsdp
 
 extern "C" {
 
@@ -201,7 +309,7 @@ fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t ful
   if (st != FSDP_OK) return st;
   const bool vec = aligned(full, 16) && aligned(shards, 16);
   const auto n_work = static_cast<int64_t>(plan->shard_work.host.size());
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fsdp::StreamSink s(stream);
   if (full_dtype == shard_dtype) {
     PtrArray dst{};
     dst.p[0] = shards;
@@ -213,30 +321,7 @@ fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t ful
 
 fsdp_status fsdp_gather_unflatten(const fsdp_plan* plan, const void* shards, int32_t dtype,
                                   void* const* full_out, void* stream) {
-  if (!plan || !shards || !full_out || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
-  const int64_t es = dtype_size(dtype);
-  if (!aligned(shards, es)) return FSDP_ERR_INVALID_ARG;
-  std::vector<Range> ranges{range_of(shards, plan->R * plan->S * es)};
-  PtrArray dst{};
-  bool vec = aligned(shards, 16);
-  int n = 0;
-  for (int r = 0; r < plan->R; ++r) {
-    void* d = full_out[r];
-    dst.p[r] = d;
-    if (!d) continue;
-    if (!aligned(d, es)) return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(d, 16);
-    ranges.push_back(range_of(d, plan->T * es));
-    ++n;
-  }
-  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
-  if (n == 0) return FSDP_OK;
-  const Work* w = nullptr;
-  const fsdp_status st = plan->flat_work.device(&w);
-  if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(plan->flat_work.host.size()), shards,
-                                    dst, plan->R, static_cast<int>(es), plan->gather_lane_bytes,
-                                    vec, static_cast<hipStream_t>(stream)));
+  return fsdp::gather_impl(plan, shards, dtype, full_out, fsdp::StreamSink(stream));
 }
 
 fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* grads,
@@ -258,73 +343,19 @@ fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* gr
   if (st != FSDP_OK) return st;
   return from_hip(fsdp::launch_rs_avg(w, static_cast<int64_t>(plan->shard_work.host.size()), g,
                                       plan->R, grad_dtype, out, vec,
-                                      static_cast<hipStream_t>(stream)));
+                                      fsdp::StreamSink(stream)));
 }
 
 fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
                                   int64_t step, const void* const* grads, int32_t grad_dtype,
                                   int32_t grads_are_replicas, float* master, float* m, float* v,
                                   void* param_out, int32_t param_dtype, void* stream) {
-  if (!plan || !hp || !grads || !master || !m || !v || !param_out) return FSDP_ERR_INVALID_ARG;
-  if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype)) return FSDP_ERR_INVALID_ARG;
-  if (step < 1) return FSDP_ERR_INVALID_ARG;
-  if (grads_are_replicas != 0 && grads_are_replicas != 1) return FSDP_ERR_INVALID_ARG;
-  const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, eps = hp->eps,
-               wd = hp->weight_decay;
-  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || lr < 0 ||
-      !(b1 >= 0 && b1 < 1) || !(b2 >= 0 && b2 < 1) || !(eps > 0) || wd < 0)
-    return FSDP_ERR_INVALID_ARG;
-
-  const int64_t n = plan->R * plan->S;
-  const int64_t pes = dtype_size(param_dtype);
-  if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(param_out, pes))
-    return FSDP_ERR_INVALID_ARG;
-  std::vector<Range> ranges{range_of(master, n * 4), range_of(m, n * 4), range_of(v, n * 4),
-                            range_of(param_out, n * pes)};
-  bool vec = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) && aligned(param_out, 16);
-  PtrArray g{};
-  if (grads_are_replicas) {
-    const int64_t ges = dtype_size(grad_dtype);
-    for (int q = 0; q < plan->R; ++q) {
-      if (!grads[q] || !aligned(grads[q], ges)) return FSDP_ERR_INVALID_ARG;
-      const Range gr = range_of(grads[q], plan->T * ges);
-      for (const Range& o : ranges)
-        if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
-      vec = vec && aligned(grads[q], 16);
-      g.p[q] = grads[q];
-    }
-  } else {
-    if (grad_dtype != FSDP_F32 || !grads[0] || !aligned(grads[0], 4)) return FSDP_ERR_INVALID_ARG;
-    const Range gr = range_of(grads[0], n * 4);
-    for (const Range& o : ranges)
-      if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(grads[0], 16);
-  }
-  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
-
+  if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
   AdamScalars sc;
-  const double t = static_cast<double>(step);
-  sc.decay = 1.0 - lr * wd;
-  sc.beta1 = b1;
-  sc.omb1 = 1.0 - b1;
-  sc.beta2 = b2;
-  sc.omb2 = 1.0 - b2;
-  sc.bc1 = 1.0 - std::pow(b1, t);
-  sc.bc2 = 1.0 - std::pow(b2, t);
-  sc.lr = lr;
-  sc.eps = eps;
-  if (!(sc.bc1 > 0) || !(sc.bc2 > 0)) return FSDP_ERR_INVALID_ARG;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!grads_are_replicas)
-    return from_hip(fsdp::launch_adamw(n, static_cast<const float*>(grads[0]), master, m, v,
-                                       param_out, param_dtype, sc, vec, s));
-  const Work* w = nullptr;
-  const fsdp_status st = plan->shard_work.device(&w);
+  const fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
   if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_fused(w, static_cast<int64_t>(plan->shard_work.host.size()), g,
-                                     plan->R, grad_dtype, master, m, v, param_out, param_dtype, sc,
-                                     vec, s));
+  return fsdp::adamw_impl(plan, sc, nullptr, grads, grad_dtype, grads_are_replicas, master, m, v,
+                          param_out, param_dtype, fsdp::StreamSink(stream));
 }
 
 fsdp_status fsdp_reshard_plan(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder** out) {
@@ -369,7 +400,7 @@ fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, i
   d.p[0] = dst;
   return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(rs->work.host.size()), src, d, 1,
                                     static_cast<int>(es), 16, aligned(src, 16) && aligned(dst, 16),
-                                    static_cast<hipStream_t>(stream)));
+                                    fsdp::StreamSink(stream)));
 }
 
 fsdp_status fsdp_reshard_batch(const fsdp_resharder* rs, int32_t n, const void* const* srcs,
@@ -398,7 +429,7 @@ fsdp_status fsdp_reshard_batch(const fsdp_resharder* rs, int32_t n, const void* 
   if (st != FSDP_OK) return st;
   return from_hip(fsdp::launch_copy_pairs(w, static_cast<int64_t>(rs->work.host.size()), s, d, n,
                                           static_cast<int>(es), vec,
-                                          static_cast<hipStream_t>(stream)));
+                                          fsdp::StreamSink(stream)));
 }
 
 fsdp_status fsdp_grad_accumulate(const fsdp_plan* plan, const void* const* grads,
@@ -425,7 +456,7 @@ fsdp_status fsdp_grad_accumulate(const fsdp_plan* plan, const void* const* grads
     for (const Range& i : ins)
       if (overlap(o, i)) return FSDP_ERR_INVALID_ARG;
   return from_hip(fsdp::launch_accumulate(plan->T, plan->R, g, grad_dtype, a, first != 0, vec,
-                                          static_cast<hipStream_t>(stream)));
+                                          fsdp::StreamSink(stream)));
 }
 
 fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
@@ -452,7 +483,7 @@ fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
     for (const Range& i : ins)
       if (overlap(x, i)) return FSDP_ERR_INVALID_ARG;
   return from_hip(fsdp::launch_allreduce(plan->T, plan->R, g, grad_dtype, o, out_dtype, vec,
-                                         static_cast<hipStream_t>(stream)));
+                                         fsdp::StreamSink(stream)));
 }
 
 const char* fsdp_status_string(fsdp_status status) {

@@ -470,6 +470,7 @@ struct AdamArgs {
   float* v;
   void* param;
   AdamScalars sc;
+  const AdamScalars* scp;  // non-null: take the scalars from device memory
   int64_t n;
   int vec;
 };
@@ -477,6 +478,7 @@ struct AdamArgs {
 template <typename P>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
   P* __restrict__ param = static_cast<P*>(a.param);
+  const AdamScalars sc = a.scp ? *a.scp : a.sc;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c * kEPL < a.n;
        c += stride) {
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
       Io<float>::load4(a.m + e0, true, m);
       Io<float>::load4(a.v + e0, true, v);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], a.sc);
+      for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], sc);
       Io<float>::store4(a.master + e0, true, p);
       Io<float>::store4(a.m + e0, true, m);
       Io<float>::store4(a.v + e0, true, v);
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
       const int64_t hi = e0 + kEPL < a.n ? e0 + kEPL : a.n;
       for (int64_t e = e0; e < hi; ++e) {
         float p = a.master[e], m = a.m[e], v = a.v[e];
-        adamw1(a.g[e], p, m, v, a.sc);
+        adamw1(a.g[e], p, m, v, sc);
         a.master[e] = p;
         a.m[e] = m;
         a.v[e] = v;
@@ -515,6 +517,7 @@ struct FusedArgs {
   float* v;
   void* param;
   AdamScalars sc;
+  const AdamScalars* scp;  // non-null: take the scalars from device memory
   int R;
   int vec;
 };
@@ -523,7 +526,8 @@ struct FusedArgs {
 // v, then the R gradient replicas) is issued before any of them is used, so
 // a wave waits for memory once per chunk.  PAD: padding, no gradient (g = 0).
 template <typename G, typename P, int RT, bool PAD, bool SHIFT>
-__device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, int k) {
+__device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a,
+                                           const AdamScalars& sc, int k) {
   P* __restrict__ param = static_cast<P*>(a.param);
   const int64_t delta = w.src - w.dst;
   for_chunks(
@@ -536,7 +540,7 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, in
         float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (!PAD) grad_avg4<G, RT, SHIFT>(a.g, a.R, e0 + delta, k, g);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], a.sc);
+        for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], sc);
         Io<float>::store4(a.master + e0, true, p);
         Io<float>::store4(a.m + e0, true, m);
         Io<float>::store4(a.v + e0, true, v);
@@ -545,7 +549,7 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, in
       [&](int64_t e) {
         const float g = PAD ? 0.0f : grad_avg1<G, RT>(a.g, a.R, e + delta);
         float p = a.master[e], m = a.m[e], v = a.v[e];
-        adamw1(g, p, m, v, a.sc);
+        adamw1(g, p, m, v, sc);
         a.master[e] = p;
         a.m[e] = m;
         a.v[e] = v;
@@ -556,13 +560,14 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a, in
 template <typename G, typename P, int RT>
 __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work, FusedArgs a) {
   const Work w = work[blockIdx.x];
+  const AdamScalars sc = a.scp ? *a.scp : a.sc;
   const int k = static_cast<int>((((w.src - w.dst) % kEPL) + kEPL) % kEPL);
   if (w.src < 0)
-    fused_item<G, P, RT, true, false>(w, a, 0);
+    fused_item<G, P, RT, true, false>(w, a, sc, 0);
   else if (k == 0)
-    fused_item<G, P, RT, false, false>(w, a, 0);
+    fused_item<G, P, RT, false, false>(w, a, sc, 0);
   else
-    fused_item<G, P, RT, false, true>(w, a, k);
+    fused_item<G, P, RT, false, true>(w, a, sc, k);
 }
 
 // ------------------------------------------------- gradient accumulation
@@ -633,15 +638,21 @@ __global__ __launch_bounds__(kThreads) void k_allreduce(ArArgs a) {
   }
 }
 
+// -------------------------------------------- AdamW scalars into memory
+// One lane writes the step's scalar record, for kernels that read it from
+// device memory (a step graph replays the same kernel arguments every step).
+__global__ __launch_bounds__(64) void k_set_scalars(AdamScalars* __restrict__ dst,
+                                                    AdamScalars sc) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *dst = sc;
+}
+
 // ----------------------------------------------------------------- launch
 template <typename Args>
-hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a,
-                       hipStream_t stream) {
+hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a, const Sink& sink) {
   if (n_work <= 0) return hipSuccess;
   if (n_work > 0x7fffffff) return hipErrorInvalidValue;
   void* args[] = {const_cast<Work**>(&work), &a};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(n_work)), dim3(kThreads), args, 0,
-                         stream);
+  return sink.launch(fn, dim3(static_cast<unsigned>(n_work)), dim3(kThreads), args);
 }
 
 template <typename G>
@@ -688,7 +699,7 @@ const void* pick_fused(int R) {
 }  // namespace
 
 hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const PtrArray& dst,
-                       int n_dst, int es, int lane_bytes, bool vec, hipStream_t stream) {
+                       int n_dst, int es, int lane_bytes, bool vec, const Sink& stream) {
   if (n_dst < 1) return hipErrorInvalidValue;
   CopyArgs a{src, dst, n_dst, vec ? 1 : 0};
   const void* fn;
@@ -702,7 +713,7 @@ hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const 
 }
 
 hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, int src_dt,
-                            void* dst, int dst_dt, bool vec, hipStream_t stream) {
+                            void* dst, int dst_dt, bool vec, const Sink& stream) {
   CastArgs a{src, dst, vec ? 1 : 0};
   const void* fn = nullptr;
   if (src_dt == FSDP_F32 && dst_dt == FSDP_BF16)
@@ -715,31 +726,31 @@ hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, i
 }
 
 hipError_t launch_rs_avg(const Work* work, int64_t n_work, const PtrArray& grads, int R,
-                         int grad_dt, float* out, bool vec, hipStream_t stream) {
+                         int grad_dt, float* out, bool vec, const Sink& stream) {
   RsArgs a{grads, out, R, vec ? 1 : 0};
   const void* fn = grad_dt == FSDP_BF16 ? pick_rs<u16>(R) : pick_rs<float>(R);
   return launch_work(fn, work, n_work, a, stream);
 }
 
 hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, float* v,
-                        void* param, int param_dt, const AdamScalars& sc, bool vec,
-                        hipStream_t stream) {
+                        void* param, int param_dt, const AdamScalars& sc,
+                        const AdamScalars* scp, bool vec, const Sink& stream) {
   if (n <= 0) return hipSuccess;
-  AdamArgs a{g, master, m, v, param, sc, n, vec ? 1 : 0};
+  AdamArgs a{g, master, m, v, param, sc, scp, n, vec ? 1 : 0};
   const int64_t chunks = (n + kEPL - 1) / kEPL;
   int64_t blocks = (chunks + kThreads - 1) / kThreads;
   if (blocks > 65536) blocks = 65536;
   const void* fn = param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16>)
                                          : reinterpret_cast<const void*>(&k_adamw<float>);
   void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0,
-                         stream);
+  return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args);
 }
 
 hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads, int R,
                         int grad_dt, float* master, float* m, float* v, void* param,
-                        int param_dt, const AdamScalars& sc, bool vec, hipStream_t stream) {
-  FusedArgs a{grads, master, m, v, param, sc, R, vec ? 1 : 0};
+                        int param_dt, const AdamScalars& sc, const AdamScalars* scp,
+                        bool vec, const Sink& stream) {
+  FusedArgs a{grads, master, m, v, param, sc, scp, R, vec ? 1 : 0};
   const void* fn;
   if (grad_dt == FSDP_BF16)
     fn = param_dt == FSDP_BF16 ? pick_fused<u16, u16>(R) : pick_fused<u16, float>(R);
@@ -749,7 +760,7 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
 }
 
 hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_dt,
-                             const PtrArray& acc, bool first, bool vec, hipStream_t stream) {
+                             const PtrArray& acc, bool first, bool vec, const Sink& stream) {
   if (T <= 0) return hipSuccess;
   AccArgs a{grads, acc, T, first ? 1 : 0, vec ? 1 : 0};
   const int64_t blocks = (T + kThreads * kEPL - 1) / (kThreads * kEPL);
@@ -757,12 +768,12 @@ hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_d
   const void* fn = grad_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_accumulate<u16>)
                                         : reinterpret_cast<const void*>(&k_accumulate<float>);
   void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(R)),
-                         dim3(kThreads), args, 0, stream);
+  return stream.launch(fn, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(R)),
+                       dim3(kThreads), args);
 }
 
 hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt,
-                            const PtrArray& out, int out_dt, bool vec, hipStream_t stream) {
+                            const PtrArray& out, int out_dt, bool vec, const Sink& stream) {
   if (T <= 0) return hipSuccess;
   ArArgs a{grads, out, T, R, vec ? 1 : 0};
   const int64_t blocks = (T + kThreads * kEPL - 1) / (kThreads * kEPL);
@@ -773,21 +784,30 @@ hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt
   else
     fn = out_dt == FSDP_BF16 ? pick_allreduce<float, u16>(R) : pick_allreduce<float, float>(R);
   void* args[] = {&a};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0,
-                         stream);
+  return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args);
 }
 
 hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& src,
                              const PtrArray& dst, int n_pairs, int es, bool vec,
-                             hipStream_t stream) {
+                             const Sink& stream) {
   if (n_work <= 0 || n_pairs <= 0) return hipSuccess;
   if (n_work > 0x7fffffff || n_pairs > FSDP_MAX_RANKS) return hipErrorInvalidValue;
   PairArgs a{src, dst, vec ? 1 : 0};
   const void* fn = es == 2 ? reinterpret_cast<const void*>(&k_copy_pairs<2>)
                            : reinterpret_cast<const void*>(&k_copy_pairs<4>);
   void* args[] = {const_cast<Work**>(&work), &a};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(n_work), static_cast<unsigned>(n_pairs)),
-                         dim3(kThreads), args, 0, stream);
+  return stream.launch(fn, dim3(static_cast<unsigned>(n_work), static_cast<unsigned>(n_pairs)),
+                       dim3(kThreads), args);
+}
+
+hipError_t launch_set_scalars(AdamScalars* dst, const AdamScalars& sc, const Sink& stream) {
+  AdamScalars v = sc;
+  void* args[] = {&dst, &v};
+  return stream.launch(reinterpret_cast<const void*>(&k_set_scalars), dim3(1), dim3(64), args);
+}
+
+hipError_t StreamSink::launch(const void* fn, dim3 grid, dim3 block, void** args) const {
+  return hipLaunchKernel(fn, grid, block, args, 0, stream_);
 }
 
 }  // namespace fsdp

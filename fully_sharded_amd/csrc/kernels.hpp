@@ -24,43 +24,69 @@ struct AdamScalars {
   double lr, eps;
 };
 
+// Where a launcher sends its kernel: enqueued on a stream, or appended to a
+// graph under construction.  args follows hipLaunchKernel: one pointer per
+// kernel argument, read before launch() returns.
+class Sink {
+ public:
+  virtual ~Sink() = default;
+  virtual hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args) const = 0;
+};
+
+class StreamSink final : public Sink {
+ public:
+  explicit StreamSink(hipStream_t s) : stream_(s) {}
+  explicit StreamSink(void* s) : stream_(static_cast<hipStream_t>(s)) {}
+  hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args) const override;
+
+ private:
+  hipStream_t stream_;
+};
+
 // Copy along work items; es = element size in bytes (2 or 4), lane_bytes
 // = 8 or 16 bytes per lane.  dst holds n_dst pointers (NULL entries are
 // skipped); padding items write zeros.
 hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const PtrArray& dst,
-                       int n_dst, int es, int lane_bytes, bool vec, hipStream_t stream);
+                       int n_dst, int es, int lane_bytes, bool vec, const Sink& stream);
 
 // Pack with a dtype change (F32 -> BF16 round to nearest even, BF16 -> F32).
 hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, int src_dt,
-                            void* dst, int dst_dt, bool vec, hipStream_t stream);
+                            void* dst, int dst_dt, bool vec, const Sink& stream);
 
 // Reduce-scatter-average over shard-space work items.
 hipError_t launch_rs_avg(const Work* work, int64_t n_work, const PtrArray& grads, int R,
-                         int grad_dt, float* out, bool vec, hipStream_t stream);
+                         int grad_dt, float* out, bool vec, const Sink& stream);
+
+// The AdamW launchers take the step's scalars by value (sc), or, when scp is
+// non-null, read them from that device record when they run.
 
 // AdamW on n contiguous elements with an fp32 gradient of the same indexing.
 hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, float* v,
-                        void* param, int param_dt, const AdamScalars& sc, bool vec,
-                        hipStream_t stream);
+                        void* param, int param_dt, const AdamScalars& sc,
+                        const AdamScalars* scp, bool vec, const Sink& stream);
 
 // Fused reduce-scatter-average + AdamW + recast over shard-space work items.
 hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads, int R,
                         int grad_dt, float* master, float* m, float* v, void* param,
-                        int param_dt, const AdamScalars& sc, bool vec, hipStream_t stream);
+                        int param_dt, const AdamScalars& sc, const AdamScalars* scp,
+                        bool vec, const Sink& stream);
 
 // acc[r] = g[r] (first) or acc[r] + g[r], fp32, for r < R over [0, T).
 hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_dt,
-                             const PtrArray& acc, bool first, bool vec, hipStream_t stream);
+                             const PtrArray& acc, bool first, bool vec, const Sink& stream);
 
 // out[r] = rank-order mean of the R gradients, for every receiver r, over
 // [0, T).
 hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt,
-                            const PtrArray& out, int out_dt, bool vec, hipStream_t stream);
+                            const PtrArray& out, int out_dt, bool vec, const Sink& stream);
 
 // The copy for n_pairs (source, destination) pairs sharing one work table
 // (one destination each), 16 bytes per lane.
 hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& src,
                              const PtrArray& dst, int n_pairs, int es, bool vec,
-                             hipStream_t stream);
+                             const Sink& stream);
+
+// Write sc to the device record dst (one single-lane kernel).
+hipError_t launch_set_scalars(AdamScalars* dst, const AdamScalars& sc, const Sink& stream);
 
 }  // namespace fsdp

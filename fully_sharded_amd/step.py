@@ -3,8 +3,10 @@
 AdamW + recast of its gradients ("FSDP Training Step Walkthrough", steps 1-6;
 zwjcode FSDP2 page, section 05: one communication group per block).
 
-Two schedules, same kernels and same results bit for bit:
+Three schedules, same kernels and same results bit for bit:
   serial    one stream: gather(u), step(u), gather(u+1), ...
+  graph     the serial sequence recorded once as a HIP graph (StepGraph) and
+            replayed each step with one launch
   prefetch  gathers on their own stream run ahead of the steps, into two
             alternating receive buffers (zwjcode FSDP2 page, section 07:
             all-gather block k+1 while block k computes, at the price of a
@@ -22,7 +24,7 @@ import ctypes
 
 import torch
 
-from .binding import Plan, bind_adamw_shard_step, bind_gather_unflatten
+from .binding import Plan, StepGraph, bind_adamw_shard_step, bind_gather_unflatten
 
 
 class Unit:
@@ -48,7 +50,7 @@ class StepRunner:
 
     def __init__(self, units, hp: dict, receivers, schedule: str = "serial",
                  gathers_per_step: int = 1):
-        if schedule not in ("serial", "prefetch"):
+        if schedule not in ("serial", "prefetch", "graph"):
             raise ValueError(schedule)
         if schedule == "prefetch" and len(receivers) < 2:
             raise ValueError("the prefetch schedule needs two receive buffers")
@@ -63,6 +65,12 @@ class StepRunner:
                       for i, u in enumerate(self.units)]
         self.stream = torch.cuda.current_stream()
         self._hs = ctypes.c_void_p(self.stream.cuda_stream)
+        if schedule == "graph":
+            self.graph = StepGraph(hp)
+            for u in self.units:
+                for _ in range(gathers_per_step):
+                    self.graph.add_gather(u.plan, u.param, receivers[0])
+                self.graph.add_adamw(u.plan, u.grads, u.master, u.m, u.v, u.param)
         if schedule == "prefetch":
             self.s_gather = torch.cuda.Stream()   # default priority
             self.s_step = torch.cuda.Stream()
@@ -77,6 +85,9 @@ class StepRunner:
         """One training step with AdamW step counter t (>= 1), enqueued on
         the current stream (the prefetch schedule joins its streams back to
         it before returning)."""
+        if self.schedule == "graph":
+            self.graph.launch(t, self._hs)
+            return
         if self.schedule == "serial":
             for gather, fused in self.calls:
                 for _ in range(self.gathers_per_step):

@@ -262,6 +262,60 @@ fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
                                int32_t grad_dtype, void* const* out, int32_t out_dtype,
                                void* stream);
 
+/* ---------------------------------------------------------------------
+ * Step graph: a unit loop recorded once and replayed every step.
+ *
+ * The per-unit sequence of one training step ("FSDP Training Step
+ * Walkthrough", steps 1-6: per unit, gather, then reduce-scatter and the
+ * local AdamW step) is the same launches every step; only AdamW's step
+ * counter changes.  A step graph records those launches once, as a HIP graph
+ * of kernel nodes executed in the order they were added, and
+ * fsdp_step_graph_launch replays it for step t with one graph launch.  Each
+ * replay computes exactly what the stream calls compute, bit for bit.
+ *
+ * The graph owns a small device record of AdamW scalars (allocated by
+ * fsdp_step_graph_create); every launch first writes step t's record with a
+ * one-lane kernel on `stream`, then launches the graph on the same stream.
+ * The graph keeps the device pointers it was given: the buffers and plans
+ * must stay alive, at the same addresses, until it is destroyed.
+ * Operations on one graph must not overlap: launches of one graph go to one
+ * stream (or are ordered by the caller), and fsdp_step_graph_destroy
+ * requires that no launch of it is still running.
+ * --------------------------------------------------------------------- */
+typedef struct fsdp_step_graph fsdp_step_graph; /* opaque */
+
+/* An empty step graph on the current device whose AdamW nodes use hp
+ * (checked as fsdp_adamw_shard_step checks it).  Allocates the scalar
+ * record (FSDP_ERR_OUT_OF_MEMORY if that fails). */
+fsdp_status fsdp_step_graph_create(const fsdp_adamw_hparams* hp, fsdp_step_graph** out);
+
+/* Destroys the graph and frees its record.  NULL is ignored. */
+void fsdp_step_graph_destroy(fsdp_step_graph* graph);
+
+/* Appends the gather that fsdp_gather_unflatten would enqueue with these
+ * arguments (same checks, same errors).  Uploads the plan's work tables
+ * if needed.  After the graph's first launch, or on another device than
+ * the graph's: FSDP_ERR_INVALID_ARG. */
+fsdp_status fsdp_step_graph_add_gather(fsdp_step_graph* graph, const fsdp_plan* plan,
+                                       const void* shards, int32_t dtype, void* const* full_out);
+
+/* Appends the AdamW shard step that fsdp_adamw_shard_step would enqueue with
+ * these arguments (same checks, same errors), taking its hyper-parameters
+ * from the graph and its step counter from each launch. */
+fsdp_status fsdp_step_graph_add_adamw(fsdp_step_graph* graph, const fsdp_plan* plan,
+                                      const void* const* grads, int32_t grad_dtype,
+                                      int32_t grads_are_replicas, float* master, float* m,
+                                      float* v, void* param_out, int32_t param_dtype);
+
+/* Kernel nodes recorded so far, and how many of them are AdamW steps. */
+fsdp_status fsdp_step_graph_info(const fsdp_step_graph* graph, int64_t* n_nodes,
+                                 int64_t* n_adamw);
+
+/* Runs every recorded operation, in order, with AdamW step counter `step`
+ * (>= 1), on `stream`.  The first launch instantiates the graph and seals
+ * it (no more nodes).  Must be called on the graph's device. */
+fsdp_status fsdp_step_graph_launch(fsdp_step_graph* graph, int64_t step, void* stream);
+
 /* Static, human-readable name of a status. */
 const char* fsdp_status_string(fsdp_status status);
 

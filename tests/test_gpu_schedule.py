@@ -1,6 +1,7 @@
 """The unit loop's schedules give the same state bit for bit: the prefetch
-schedule (gathers on their own stream, double receive buffer) and two
-gathers per step change ordering and traffic, not results."""
+schedule (gathers on their own stream, double receive buffer), two gathers
+per step, and the step graph (the serial sequence replayed as one HIP graph)
+change ordering, traffic or launch count, not results."""
 
 import pytest
 import torch
@@ -19,24 +20,28 @@ def build(wl_name, n_units=None):
     R = wl["R"]
     shapes = shapes_of(wl["units"][0])
     pl = F.Plan(shapes, R, wl["layout"])
+    pdt = torch.bfloat16 if wl["param_dtype"] == "bf16" else torch.float32
     units = []
     for u in range(n_units or len(wl["units"])):
         full = gen.device_master(wl, u, shapes, DEV)
         master = torch.empty(R * pl.S, device=DEV)
         F.fsdp_shard_pack(pl, full, master)
-        param = torch.empty(R * pl.S, dtype=torch.bfloat16, device=DEV)
+        param = torch.empty(R * pl.S, dtype=pdt, device=DEV)
         F.fsdp_shard_pack(pl, full, param)
         grads = [gen.device_grad(wl, 1, u, r, pl.T, DEV) for r in range(R)]
         units.append(Unit(pl, master, torch.zeros_like(master), torch.zeros_like(master),
                           param, grads))
-    recv = [[torch.empty(pl.T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    recv = [[torch.empty(pl.T, dtype=pdt, device=DEV) for _ in range(R)]
             for _ in range(2)]
     return units, recv
 
 
 def state_of(units):
-    return [(u.master.clone(), u.m.clone(), u.v.clone(), u.param.view(torch.int16).clone())
-            for u in units]
+    return [(u.master.clone(), u.m.clone(), u.v.clone(), bits(u.param)) for u in units]
+
+
+def bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).clone()
 
 
 @pytest.mark.parametrize("schedule,gathers", [("prefetch", 1), ("serial", 2), ("prefetch", 2)])
@@ -69,3 +74,66 @@ def test_memory_ledger_counts_the_prefetch_buffer():
     assert serial["largest_unsharded_group"] == 2 * T and serial["prefetch"] == 0
     assert pre["prefetch"] == 2 * T
     assert pre["peak_lower_bound"] == serial["peak_lower_bound"] + 2 * T
+
+
+@pytest.mark.parametrize("wl_name,gathers", [("model12_r8", 1), ("model12_r8", 2),
+                                             ("block512_r3", 1), ("block512_flat_r3", 1),
+                                             ("toy_2layer_r2", 1)])
+def test_step_graph_replays_match_the_stream_calls(wl_name, gathers):
+    """Every replay of the step graph, with unrelated eager work and a
+    synchronisation between replays, leaves the state and the receive buffer
+    bit-identical to the same step made with stream calls."""
+    print(f"[gpu] step graph {wl_name} gathers={gathers}", flush=True)
+    ref_units, ref_recv = build(wl_name)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial", gathers)
+    units, recv = build(wl_name)
+    run = StepRunner(units, ADAMW, recv, "graph", gathers)
+    n_nodes, n_adamw = run.graph.info()
+    assert n_adamw == len(units) and n_nodes == len(units) * (gathers + 1)
+    scratch = torch.randn(1 << 20, device=DEV)
+    for t in (1, 2, 3, 4):
+        run.step(t)
+        scratch.mul_(1.0001).add_(1.0)            # the program's own eager work
+        ref.step(t)
+        torch.cuda.synchronize()
+        for a, b in zip(state_of(ref_units), state_of(units)):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), f"step {t}"
+        for r in range(len(recv[0])):
+            assert torch.equal(bits(recv[0][r]), bits(ref_recv[0][r])), f"step {t}"
+
+
+def test_step_graph_steps_need_not_be_consecutive():
+    """The step counter comes from each launch: replaying t = 5 after t = 1
+    matches the stream calls made with t = 1 then t = 5."""
+    ref_units, ref_recv = build("block512_r4")
+    units, recv = build("block512_r4")
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial")
+    run = StepRunner(units, ADAMW, recv, "graph")
+    for t in (1, 5, 2):
+        ref.step(t)
+        run.step(t)
+    torch.cuda.synchronize()
+    for a, b in zip(state_of(ref_units), state_of(units)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_step_graph_errors():
+    units, recv = build("block512_r4")
+    u = units[0]
+    with pytest.raises(F.FsdpError):            # eps must be > 0
+        F.StepGraph(dict(ADAMW, eps=0.0))
+    g = F.StepGraph(ADAMW)
+    g.launch(1)                                  # empty: nothing to run
+    with pytest.raises(F.FsdpError):            # the parameter overlaps the master
+        g.add_adamw(u.plan, u.grads, u.master, u.m, u.v, u.master.view(torch.bfloat16)[: u.param.numel()])
+    g.add_gather(u.plan, u.param, recv[0])
+    g.add_adamw(u.plan, u.grads, u.master, u.m, u.v, u.param)
+    with pytest.raises(F.FsdpError):            # step counter starts at 1
+        g.launch(0)
+    g.launch(1)
+    with pytest.raises(F.FsdpError):            # sealed by its first launch
+        g.add_gather(u.plan, u.param, recv[1])
+    torch.cuda.synchronize()
+    assert g.info() == (2, 1)
