@@ -35,12 +35,13 @@ namespace {
 class GraphSink final : public fsdp::Sink {
  public:
   explicit GraphSink(fsdp_step_graph* g) : g_(g) {}
-  hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args) const override {
+  hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args,
+                    unsigned lds) const override {
     hipKernelNodeParams p{};
     p.func = const_cast<void*>(fn);
     p.gridDim = grid;
     p.blockDim = block;
-    p.sharedMemBytes = 0;
+    p.sharedMemBytes = lds;
     p.kernelParams = args;
     p.extra = nullptr;
     hipGraphNode_t node = nullptr;

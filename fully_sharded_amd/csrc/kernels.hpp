@@ -26,18 +26,21 @@ struct AdamScalars {
 
 // Where a launcher sends its kernel: enqueued on a stream, or appended to a
 // graph under construction.  args follows hipLaunchKernel: one pointer per
-// kernel argument, read before launch() returns.
+// kernel argument, read before launch() returns; lds is the dynamic LDS
+// (shared memory) bytes per workgroup.
 class Sink {
  public:
   virtual ~Sink() = default;
-  virtual hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args) const = 0;
+  virtual hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args,
+                            unsigned lds) const = 0;
 };
 
 class StreamSink final : public Sink {
  public:
   explicit StreamSink(hipStream_t s) : stream_(s) {}
   explicit StreamSink(void* s) : stream_(static_cast<hipStream_t>(s)) {}
-  hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args) const override;
+  hipError_t launch(const void* fn, dim3 grid, dim3 block, void** args,
+                    unsigned lds) const override;
 
  private:
   hipStream_t stream_;
