@@ -3,13 +3,16 @@
 One step = for every FSDP unit of the model, in order: all-gather +
 unflatten its bf16 shards into R full-unit receivers, then the fused
 reduce-scatter-average of the R bf16 gradient replicas + AdamW on the fp32
-master/m/v shards + bf16 recast.  Default workload: the 12-layer model of
-TransformerBlocks (hidden 512, ffn 2048), one FSDP2 per-parameter unit per
-block, R = 8 virtual ranks in one GPU's memory (37,761,024 parameters).
-Inputs are synthetic, seeded and resident in HBM before timing starts.
+master/m/v shards + bf16 recast.  Default schedule "overlap": each unit's
+fused step is enqueued together with the next unit's gather (FSDP's
+prefetch; one launch per unit for units this size), into two alternating
+receive buffers.  Default workload: the 12-layer model of TransformerBlocks
+(hidden 512, ffn 2048), one FSDP2 per-parameter unit per block, R = 8
+virtual ranks in one GPU's memory (37,761,024 parameters).  Inputs are
+synthetic, seeded and resident in HBM before timing starts.
 
 Prints one JSON line: params/s of the whole step, achieved algorithmic HBM
-GB/s, the roofline of the dominant (fused) kernel from HIP events around its
+GB/s, the roofline of the step's dominant kernel from HIP events around its
 launches, and the CPU oracle timed on a bounded sample on the host.
 """
 
@@ -36,11 +39,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="model12_r8")
-    ap.add_argument("--schedule", choices=("serial", "prefetch", "graph"), default="serial",
-                    help="serial: per unit gather then fused step on one stream; prefetch: "
+    ap.add_argument("--schedule", choices=("serial", "prefetch", "graph", "overlap"),
+                    default=None,
+                    help="default overlap (serial with --gathers-per-step 2); "
+                         "serial: per unit gather then fused step on one stream; prefetch: "
                          "gathers on their own stream run ahead of the fused steps, into a "
                          "double receive buffer; graph: the serial sequence replayed as one "
-                         "HIP graph per step")
+                         "HIP graph per step; overlap: each unit's fused step shares its "
+                         "launch with the next unit's gather (double receive buffer)")
     ap.add_argument("--gathers-per-step", type=int, choices=(1, 2), default=1,
                     help="1: parameters kept from forward to backward "
                          "(reshard_after_forward=False); 2: freed after forward and "
@@ -61,7 +67,10 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibrate-copy` into profiles/traffic_<workload>.json "
                          "and exit (no GPU needed)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.schedule is None:
+        args.schedule = "overlap" if args.gathers_per_step == 1 else "serial"
+    return args
 
 
 def kernel_src_hash():
@@ -72,17 +81,31 @@ def kernel_src_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """Counter-measured HBM bytes per fused launch, if taken on the current
-    kernel sources (profiles/traffic_<workload>.json), else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+# Kernels whose traffic the counter runs summarise: key -> the kernel-name
+# fragment that selects their dispatches in a rocprofv3 counter CSV.
+TRAFFIC_KERNELS = {
+    "fused": ("::k_fused<", "k_fused (fused reduce-scatter-average + AdamW + bf16 recast)"),
+    "fused_gather": ("::k_fused_gather<", "k_fused_gather (one unit's fused step, then the "
+                                          "next unit's gather, in one launch)"),
+}
+
+
+def traffic_path(workload, key):
+    name = f"traffic_{workload}.json" if key == "fused" else f"traffic_{workload}_{key}.json"
+    return os.path.join(ROOT, "profiles", name)
+
+
+def load_traffic(workload, key="fused"):
+    """Counter-measured HBM bytes per launch of a kernel, if taken on the
+    current kernel sources, else None."""
+    path = traffic_path(workload, key)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tr = json.load(f)
     if tr.get("kernel_src_sha") != kernel_src_hash():
         return None
-    return tr.get("fused_bytes_per_launch")
+    return tr.get("bytes_per_launch", tr.get("fused_bytes_per_launch"))
 
 
 def rows(n_rows, n, dtype, device):
@@ -100,49 +123,64 @@ def rows(n_rows, n, dtype, device):
 
 
 def summarise_counters(fetch_csv, write_csv, workload):
-    """HBM bytes per fused launch from the FETCH_SIZE and WRITE_SIZE counters
-    (KiB per dispatch), each scaled by what the same counter reads for the
-    1 GiB plain copy of --calibrate-copy (1 GiB read, 1 GiB written)."""
+    """HBM bytes per launch of each kernel in TRAFFIC_KERNELS that the runs
+    dispatched, from the FETCH_SIZE and WRITE_SIZE counters (KiB per
+    dispatch), each scaled by what the same counter reads for the 1 GiB
+    plain copy of --calibrate-copy (1 GiB read, 1 GiB written)."""
     import csv
 
-    def load(path, counter):
-        fused, copy = [], []
+    def load(path, counter, frag):
+        sel, copy = [], []
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                if "k_fused" in name:
-                    fused.append(float(r["Counter_Value"]))
+                if frag in name:
+                    sel.append(float(r["Counter_Value"]))
                 elif "copy" in name.lower() and "fsdp" not in name:
                     copy.append(float(r["Counter_Value"]))
-        if not fused or not copy:
-            raise SystemExit(f"{path}: no fused or calibration-copy dispatches for {counter}")
-        return sum(fused) / len(fused), max(copy)
+        if not copy:
+            raise SystemExit(f"{path}: no calibration-copy dispatches for {counter}")
+        return (sum(sel) / len(sel) if sel else None), max(copy), len(sel)
 
     gib_kib = float(1 << 20)
-    fetch, fetch_copy = load(fetch_csv, "FETCH_SIZE")
-    write, write_copy = load(write_csv, "WRITE_SIZE")
-    fs = gib_kib / fetch_copy
-    ws = gib_kib / write_copy
-    traffic = (fetch * fs + write * ws) * 1024.0
-    out = {
-        "workload": workload,
-        "kernel": "k_fused (fused reduce-scatter-average + AdamW + bf16 recast)",
-        "kernel_src_sha": kernel_src_hash(),
-        "fetch_kib_per_launch": fetch,
-        "write_kib_per_launch": write,
-        "calibration_copy_kib": {"FETCH_SIZE": fetch_copy, "WRITE_SIZE": write_copy,
-                                 "true_kib_each_way": gib_kib},
-        "fetch_scale": fs,
-        "write_scale": ws,
-        "fused_bytes_per_launch": traffic,
-    }
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    print(json.dumps(out))
+    for key, (frag, desc) in TRAFFIC_KERNELS.items():
+        fetch, fetch_copy, nf = load(fetch_csv, "FETCH_SIZE", frag)
+        write, write_copy, nw = load(write_csv, "WRITE_SIZE", frag)
+        if fetch is None or write is None:
+            continue
+        fs = gib_kib / fetch_copy
+        ws = gib_kib / write_copy
+        out = {
+            "workload": workload,
+            "kernel": desc,
+            "kernel_src_sha": kernel_src_hash(),
+            "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
+            "fetch_kib_per_launch": fetch,
+            "write_kib_per_launch": write,
+            "calibration_copy_kib": {"FETCH_SIZE": fetch_copy, "WRITE_SIZE": write_copy,
+                                     "true_kib_each_way": gib_kib},
+            "fetch_scale": fs,
+            "write_scale": ws,
+            "bytes_per_launch": (fetch * fs + write * ws) * 1024.0,
+        }
+        with open(traffic_path(workload, key), "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        print(json.dumps(out))
+
+
+def launches_per_step(args, units):
+    """Kernel launches of one step (the graph schedule adds its one-lane
+    scalar kernel)."""
+    n = len(units)
+    if args.schedule == "overlap":
+        # a unit's step shares its launch with the next gather when it has
+        # at most 4,096 work items
+        big = sum(1 for u in units[:-1] if len(u.plan.work_items(0)) > 4096)
+        return 1 + (n - 1) + big + 1
+    return (args.gathers_per_step + 1) * n + (1 if args.schedule == "graph" else 0)
 
 
 def setup_units(wl, dev):
@@ -221,7 +259,7 @@ def main():
     n_copies = 1 if ws >= (1 << 30) else min(16, -(-(1 << 30) // ws))
     copies = [units] + [setup_units(wl, dev)[1] for _ in range(n_copies - 1)]
     T_max = max(p.T for p in plans.values())
-    n_recv = 2 if args.schedule == "prefetch" else 1
+    n_recv = 2 if args.schedule in ("prefetch", "overlap") else 1
     runners = []
     for cu in copies:
         recv = [rows(R, T_max, pdt, dev) for _ in range(n_recv)]
@@ -286,6 +324,16 @@ def main():
 
     fused_avg_ms = timed(fused_pass)
     gather_avg_ms = timed(gather_pass)
+    pair_avg_ms = None
+    if args.schedule == "overlap" and len(units) > 1:
+        pp = [0]
+
+        def pair_pass():
+            pp[0] += 1
+            step_no[0] += 1
+            for pair in runners[pp[0] % len(runners)].pairs:
+                pair(step_no[0], hs)
+        pair_avg_ms = timed(pair_pass) * len(units) / (len(units) - 1)
 
     # algorithmic bytes (valid parameters only, padding excluded)
     ges = 2 if gdt == torch.bfloat16 else 4
@@ -294,10 +342,32 @@ def main():
     gather_bytes_unit = [u.plan.T * (pes + pes * R) for u in units]
     step_bytes = sum(fused_bytes_unit) + args.gathers_per_step * sum(gather_bytes_unit)
     fused_bytes = float(np.mean(fused_bytes_unit))
-    achieved = fused_bytes / (fused_avg_ms * 1e-3) / 1e9
+    fused_gbps = fused_bytes / (fused_avg_ms * 1e-3) / 1e9
     gather_gbps = float(np.mean(gather_bytes_unit)) / (gather_avg_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+    kernels = {
+        "fused_rs_adamw": {"avg_ms": fused_avg_ms, "bytes": fused_bytes, "gbps": fused_gbps},
+        "gather_unflatten": {"avg_ms": gather_avg_ms,
+                             "bytes": float(np.mean(gather_bytes_unit)), "gbps": gather_gbps},
+        "timed_launches_each": reps * len(units),
+    }
+    # the dominant kernel of the step as scheduled: the fused step, or, in
+    # the overlap schedule with short steps, the launch that holds one
+    # unit's fused step and the next unit's gather
+    dominant = ("fused", fused_bytes, fused_avg_ms)
+    if pair_avg_ms is not None:
+        pair_bytes = float(np.mean([fused_bytes_unit[i] + gather_bytes_unit[i + 1]
+                                    for i in range(len(units) - 1)]))
+        one_launch = launches_per_step(args, units) == len(units) + 1
+        kernels["fused_then_gather"] = {
+            "avg_ms": pair_avg_ms, "bytes": pair_bytes,
+            "gbps": pair_bytes / (pair_avg_ms * 1e-3) / 1e9,
+            "launches": 1 if one_launch else 2}
+        if one_launch:
+            dominant = ("fused_gather", pair_bytes, pair_avg_ms)
+    dom_key, dom_bytes, dom_ms = dominant
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, dom_key)
 
     copy_info = None
     if args.calibrate_copy:
@@ -347,23 +417,23 @@ def main():
             "state_dtype": "f32",
             "schedule": args.schedule,
             "gathers_per_step": args.gathers_per_step,
-            "launches_per_step": (args.gathers_per_step + 1) * len(units),
+            "launches_per_step": launches_per_step(args, units),
             "host_calls_per_step": 2 if args.schedule == "graph"
+            else len(units) + 1 if args.schedule == "overlap"
             else (args.gathers_per_step + 1) * len(units),
             "buffer_copies": len(runners),
-            "step": "per unit: gather+unflatten to R receivers, fused RS-avg+AdamW+recast",
+            "step": "per unit: gather+unflatten to R receivers, fused RS-avg+AdamW+recast "
+                    "(overlap: unit u's fused step shares its launch with unit u+1's gather)",
         },
         "hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / PEAK_HBM_GBPS,
         "step_bytes": step_bytes,
-        "kernels": {
-            "fused_rs_adamw": {"avg_ms": fused_avg_ms, "bytes": fused_bytes, "gbps": achieved},
-            "gather_unflatten": {"avg_ms": gather_avg_ms,
-                                 "bytes": float(np.mean(gather_bytes_unit)), "gbps": gather_gbps},
-            "timed_launches_each": reps * len(units),
-        },
+        "kernels": kernels,
         "memory_ledger_per_rank": runner.memory_ledger(pes),
         "roofline": {
+            "kernel": TRAFFIC_KERNELS[dom_key][1],
+            "bytes_per_launch": dom_bytes,
+            "avg_ms": dom_ms,
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,

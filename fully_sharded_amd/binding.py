@@ -89,6 +89,14 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_void_p),
                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                           ctypes.c_void_p]),
+    "fsdp_adamw_step_then_gather": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(AdamWHParams),
+                                                   ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.c_int32, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_int32,
+                                                   ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.c_void_p]),
     "fsdp_step_graph_create": (ctypes.c_int, [ctypes.POINTER(AdamWHParams),
                                               ctypes.POINTER(ctypes.c_void_p)]),
     "fsdp_step_graph_destroy": (None, [ctypes.c_void_p]),
@@ -466,6 +474,61 @@ def bind_adamw_shard_step(plan: Plan, hp: dict, grads, master, m, v, param_out):
             _dtype_code(param_out))
     call = BoundCall("fsdp_adamw_shard_step", None,
                      (plan, h, list(grads), master, m, v, param_out))
+
+    def run(step, stream=None):
+        call._run(*head, int(step), *tail, _stream(stream))
+    run.call = call
+    return run
+
+
+def _check_step_args(plan: Plan, grads, master, m, v, param_out):
+    n = plan.R * plan.S
+    for t, nm in ((master, "master"), (m, "m"), (v, "v")):
+        if t.numel() != n or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be fp32 with R*S elements")
+    if param_out.numel() != n or len(grads) != plan.R:
+        raise ValueError("size mismatch with the plan")
+    dt = _dtype_code(grads[0])
+    for g in grads:
+        if g.numel() != plan.T or _dtype_code(g) != dt:
+            raise ValueError("gradient size or dtype mismatch")
+    return dt
+
+
+def _check_gather_args(plan: Plan, shards, full_out):
+    if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
+        raise ValueError("size mismatch with the plan")
+    for t in full_out:
+        if t is not None and (t.numel() < plan.T or t.dtype != shards.dtype):
+            raise ValueError("receiver size or dtype mismatch")
+
+
+def fsdp_adamw_step_then_gather(plan: Plan, hp: dict, step: int, grads, master, m, v, param_out,
+                                next_plan: Plan, next_shards, full_out, stream=None):
+    """The fused AdamW step of one unit, then the gather of the next unit's
+    shards into full_out (one launch for short steps)."""
+    bind_adamw_step_then_gather(plan, hp, grads, master, m, v, param_out, next_plan,
+                                next_shards, full_out)(step, stream)
+
+
+def bind_adamw_step_then_gather(plan: Plan, hp: dict, grads, master, m, v, param_out,
+                                next_plan: Plan, next_shards, full_out):
+    """fsdp_adamw_step_then_gather with cached arguments; call as
+    f(step, stream=None)."""
+    dt = _check_step_args(plan, grads, master, m, v, param_out)
+    _check_gather_args(next_plan, next_shards, full_out)
+    if next_shards.dtype != param_out.dtype:
+        raise ValueError("the next unit's shards must have the parameter dtype")
+    h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    head = (plan.handle, ctypes.byref(h))
+    tail = (_ptr_array(grads, "grads"), dt, ctypes.c_void_p(_dev(master, "master")),
+            ctypes.c_void_p(_dev(m, "m")), ctypes.c_void_p(_dev(v, "v")),
+            ctypes.c_void_p(_dev(param_out, "param_out")), _dtype_code(param_out),
+            next_plan.handle, ctypes.c_void_p(_dev(next_shards, "next_shards")),
+            _ptr_array(full_out, "full_out"))
+    call = BoundCall("fsdp_adamw_step_then_gather", None,
+                     (plan, h, list(grads), master, m, v, param_out, next_plan, next_shards,
+                      list(full_out)))
 
     def run(step, stream=None):
         call._run(*head, int(step), *tail, _stream(stream))

@@ -84,37 +84,72 @@ fsdp_status adam_scalars(const fsdp_adamw_hparams* hp, int64_t step, AdamScalars
   return FSDP_OK;
 }
 
-fsdp_status gather_impl(const fsdp_plan* plan, const void* shards, int32_t dtype,
-                        void* const* full_out, const Sink& sink) {
+namespace {
+
+// A checked gather: its launch arguments and the memory it reads and writes.
+struct GatherCall {
+  const Work* w = nullptr;
+  int64_t n_work = 0;
+  const void* src = nullptr;
+  PtrArray dst{};
+  int n_dst = 0;  // destinations given (NULL ones are skipped)
+  int es = 0;
+  int lane_bytes = 16;
+  bool vec = false;
+  std::vector<Range> reads, writes;
+};
+
+fsdp_status prep_gather(const fsdp_plan* plan, const void* shards, int32_t dtype,
+                        void* const* full_out, GatherCall* c) {
   if (!plan || !shards || !full_out || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
   const int64_t es = dtype_size(dtype);
   if (!aligned(shards, es)) return FSDP_ERR_INVALID_ARG;
-  std::vector<Range> ranges{range_of(shards, plan->R * plan->S * es)};
-  PtrArray dst{};
-  bool vec = aligned(shards, 16);
-  int n = 0;
+  c->reads.push_back(range_of(shards, plan->R * plan->S * es));
+  c->vec = aligned(shards, 16);
   for (int r = 0; r < plan->R; ++r) {
     void* d = full_out[r];
-    dst.p[r] = d;
+    c->dst.p[r] = d;
     if (!d) continue;
     if (!aligned(d, es)) return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(d, 16);
-    ranges.push_back(range_of(d, plan->T * es));
-    ++n;
+    c->vec = c->vec && aligned(d, 16);
+    c->writes.push_back(range_of(d, plan->T * es));
+    ++c->n_dst;
   }
-  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
-  if (n == 0) return FSDP_OK;
-  const Work* w = nullptr;
-  const fsdp_status st = plan->flat_work.device(&w);
+  std::vector<Range> all = c->writes;
+  all.push_back(c->reads[0]);
+  if (any_overlap(all)) return FSDP_ERR_INVALID_ARG;
+  if (c->n_dst == 0) return FSDP_OK;
+  const fsdp_status st = plan->flat_work.device(&c->w);
   if (st != FSDP_OK) return st;
-  return status_of(launch_copy(w, static_cast<int64_t>(plan->flat_work.host.size()), shards, dst,
-                               plan->R, static_cast<int>(es), plan->gather_lane_bytes, vec, sink));
+  c->n_work = static_cast<int64_t>(plan->flat_work.host.size());
+  c->src = shards;
+  c->es = static_cast<int>(es);
+  c->lane_bytes = plan->gather_lane_bytes;
+  return FSDP_OK;
 }
 
-fsdp_status adamw_impl(const fsdp_plan* plan, const AdamScalars& sc, const AdamScalars* scp,
-                       const void* const* grads, int32_t grad_dtype, int32_t grads_are_replicas,
-                       float* master, float* m, float* v, void* param_out, int32_t param_dtype,
-                       const Sink& sink) {
+fsdp_status launch(const GatherCall& c, int R, const Sink& sink) {
+  if (c.n_dst == 0) return FSDP_OK;
+  return status_of(launch_copy(c.w, c.n_work, c.src, c.dst, R, c.es, c.lane_bytes, c.vec, sink));
+}
+
+// A checked AdamW shard step.
+struct AdamCall {
+  const fsdp_plan* plan = nullptr;
+  bool replicas = true;
+  PtrArray g{};
+  int32_t grad_dt = 0, param_dt = 0;
+  float *master = nullptr, *m = nullptr, *v = nullptr;
+  void* param = nullptr;
+  bool vec = false;
+  const Work* w = nullptr;
+  int64_t n_work = 0;
+  std::vector<Range> reads, writes;
+};
+
+fsdp_status prep_adamw(const fsdp_plan* plan, const void* const* grads, int32_t grad_dtype,
+                       int32_t grads_are_replicas, float* master, float* m, float* v,
+                       void* param_out, int32_t param_dtype, AdamCall* c) {
   if (!plan || !grads || !master || !m || !v || !param_out) return FSDP_ERR_INVALID_ARG;
   if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype)) return FSDP_ERR_INVALID_ARG;
   if (grads_are_replicas != 0 && grads_are_replicas != 1) return FSDP_ERR_INVALID_ARG;
@@ -122,37 +157,101 @@ fsdp_status adamw_impl(const fsdp_plan* plan, const AdamScalars& sc, const AdamS
   const int64_t pes = dtype_size(param_dtype);
   if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(param_out, pes))
     return FSDP_ERR_INVALID_ARG;
-  std::vector<Range> ranges{range_of(master, n * 4), range_of(m, n * 4), range_of(v, n * 4),
-                            range_of(param_out, n * pes)};
-  bool vec = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) && aligned(param_out, 16);
-  PtrArray g{};
+  c->writes = {range_of(master, n * 4), range_of(m, n * 4), range_of(v, n * 4),
+               range_of(param_out, n * pes)};
+  c->vec = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) && aligned(param_out, 16);
   if (grads_are_replicas) {
     const int64_t ges = dtype_size(grad_dtype);
     for (int q = 0; q < plan->R; ++q) {
       if (!grads[q] || !aligned(grads[q], ges)) return FSDP_ERR_INVALID_ARG;
-      const Range gr = range_of(grads[q], plan->T * ges);
-      for (const Range& o : ranges)
-        if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
-      vec = vec && aligned(grads[q], 16);
-      g.p[q] = grads[q];
+      c->reads.push_back(range_of(grads[q], plan->T * ges));
+      c->vec = c->vec && aligned(grads[q], 16);
+      c->g.p[q] = grads[q];
     }
   } else {
     if (grad_dtype != FSDP_F32 || !grads[0] || !aligned(grads[0], 4)) return FSDP_ERR_INVALID_ARG;
-    const Range gr = range_of(grads[0], n * 4);
-    for (const Range& o : ranges)
-      if (overlap(o, gr)) return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(grads[0], 16);
+    c->reads.push_back(range_of(grads[0], n * 4));
+    c->vec = c->vec && aligned(grads[0], 16);
+    c->g.p[0] = grads[0];
   }
-  if (any_overlap(ranges)) return FSDP_ERR_INVALID_ARG;
-  if (!grads_are_replicas)
-    return status_of(launch_adamw(n, static_cast<const float*>(grads[0]), master, m, v, param_out,
-                                  param_dtype, sc, scp, vec, sink));
-  const Work* w = nullptr;
-  const fsdp_status st = plan->shard_work.device(&w);
+  for (const Range& o : c->writes)
+    for (const Range& i : c->reads)
+      if (overlap(o, i)) return FSDP_ERR_INVALID_ARG;
+  if (any_overlap(c->writes)) return FSDP_ERR_INVALID_ARG;
+  c->plan = plan;
+  c->replicas = grads_are_replicas != 0;
+  c->grad_dt = grad_dtype;
+  c->param_dt = param_dtype;
+  c->master = master;
+  c->m = m;
+  c->v = v;
+  c->param = param_out;
+  if (c->replicas) {
+    const fsdp_status st = plan->shard_work.device(&c->w);
+    if (st != FSDP_OK) return st;
+    c->n_work = static_cast<int64_t>(plan->shard_work.host.size());
+  }
+  return FSDP_OK;
+}
+
+fsdp_status launch(const AdamCall& c, const AdamScalars& sc, const AdamScalars* scp,
+                   const Sink& sink) {
+  if (!c.replicas)
+    return status_of(launch_adamw(c.plan->R * c.plan->S, static_cast<const float*>(c.g.p[0]),
+                                  c.master, c.m, c.v, c.param, c.param_dt, sc, scp, c.vec, sink));
+  return status_of(launch_fused(c.w, c.n_work, c.g, c.plan->R, c.grad_dt, c.master, c.m, c.v,
+                                c.param, c.param_dt, sc, scp, c.vec, sink));
+}
+
+}  // namespace
+
+fsdp_status gather_impl(const fsdp_plan* plan, const void* shards, int32_t dtype,
+                        void* const* full_out, const Sink& sink) {
+  GatherCall c;
+  const fsdp_status st = prep_gather(plan, shards, dtype, full_out, &c);
+  return st != FSDP_OK ? st : launch(c, plan->R, sink);
+}
+
+fsdp_status adamw_impl(const fsdp_plan* plan, const AdamScalars& sc, const AdamScalars* scp,
+                       const void* const* grads, int32_t grad_dtype, int32_t grads_are_replicas,
+                       float* master, float* m, float* v, void* param_out, int32_t param_dtype,
+                       const Sink& sink) {
+  AdamCall c;
+  const fsdp_status st = prep_adamw(plan, grads, grad_dtype, grads_are_replicas, master, m, v,
+                                    param_out, param_dtype, &c);
+  return st != FSDP_OK ? st : launch(c, sc, scp, sink);
+}
+
+fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
+                              const AdamScalars* scp, const void* const* grads,
+                              int32_t grad_dtype, float* master, float* m, float* v,
+                              void* param_out, int32_t param_dtype, const fsdp_plan* next,
+                              const void* next_shards, void* const* full_out, const Sink& sink) {
+  AdamCall a;
+  fsdp_status st = prep_adamw(plan, grads, grad_dtype, 1, master, m, v, param_out, param_dtype, &a);
   if (st != FSDP_OK) return st;
-  return status_of(launch_fused(w, static_cast<int64_t>(plan->shard_work.host.size()), g, plan->R,
-                                grad_dtype, master, m, v, param_out, param_dtype, sc, scp, vec,
-                                sink));
+  GatherCall g;
+  st = prep_gather(next, next_shards, param_dtype, full_out, &g);
+  if (st != FSDP_OK) return st;
+  // the two run concurrently: neither may write what the other touches
+  for (const Range& w : g.writes) {
+    for (const Range& x : a.writes)
+      if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
+    for (const Range& x : a.reads)
+      if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
+  }
+  for (const Range& w : a.writes)
+    for (const Range& x : g.reads)
+      if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
+  if (g.n_dst == 0) return launch(a, sc, scp, sink);
+  if (a.n_work > kSmallFusedLaunch || a.n_work == 0) {
+    // a long step: its own launch (with its occupancy cap), then the gather
+    st = launch(a, sc, scp, sink);
+    return st != FSDP_OK ? st : launch(g, next->R, sink);
+  }
+  return status_of(launch_fused_gather(a.w, a.n_work, a.g, plan->R, grad_dtype, master, m, v,
+                                       param_out, param_dtype, sc, scp, a.vec, g.w, g.n_work,
+                                       g.src, g.dst, next->R, g.lane_bytes, g.vec, sink));
 }
 
 }  // namespace fsdp
@@ -356,6 +455,21 @@ fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparam
   if (st != FSDP_OK) return st;
   return fsdp::adamw_impl(plan, sc, nullptr, grads, grad_dtype, grads_are_replicas, master, m, v,
                           param_out, param_dtype, fsdp::StreamSink(stream));
+}
+
+fsdp_status fsdp_adamw_step_then_gather(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
+                                        int64_t step, const void* const* grads,
+                                        int32_t grad_dtype, float* master, float* m, float* v,
+                                        void* param_out, int32_t param_dtype,
+                                        const fsdp_plan* next, const void* next_shards,
+                                        void* const* full_out, void* stream) {
+  if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
+  AdamScalars sc;
+  const fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
+  if (st != FSDP_OK) return st;
+  return fsdp::adamw_gather_impl(plan, sc, nullptr, grads, grad_dtype, master, m, v, param_out,
+                                 param_dtype, next, next_shards, full_out,
+                                 fsdp::StreamSink(stream));
 }
 
 fsdp_status fsdp_reshard_plan(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder** out) {

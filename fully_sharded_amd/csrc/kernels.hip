@@ -296,19 +296,20 @@ struct CopyArgs {
   int vec;
 };
 
+// One work item of the copy; wg numbers the item (it picks the first
+// destination of the rotation).
 template <int ES, int W>
-__global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work, CopyArgs a) {
+__device__ __forceinline__ void copy_item(const Work& w, const CopyArgs& a, unsigned wg) {
   using E = typename Raw<ES>::E;
   using V = typename Lane<W>::V;
   constexpr int N = W / ES;  // elements per lane
-  const Work w = work[blockIdx.x];
   const E* __restrict__ src = static_cast<const E*>(a.src);
   const bool pad = w.src < 0;
   const int64_t delta = w.src - w.dst;
   const int k = static_cast<int>(((delta % N) + N) % N);  // source misalignment
   const bool vec = a.vec != 0;
   const int64_t end = w.dst + w.len;
-  const int first = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.n_dst));
+  const int first = static_cast<int>(wg % static_cast<unsigned>(a.n_dst));
   for (int64_t c = w.dst / N + threadIdx.x; c * N < end; c += kThreads) {
     const int64_t e0 = c * N;
     if (vec && e0 >= w.dst && e0 + N <= end) {
@@ -341,6 +342,11 @@ __global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work
       }
     }
   }
+}
+
+template <int ES, int W>
+__global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work, CopyArgs a) {
+  copy_item<ES, W>(work[blockIdx.x], a, blockIdx.x);
 }
 
 // The same copy for up to 64 independent (source, destination) pairs that
@@ -558,8 +564,7 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a,
 }
 
 template <typename G, typename P, int RT>
-__global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work, FusedArgs a) {
-  const Work w = work[blockIdx.x];
+__device__ __forceinline__ void fused_wg(const Work& w, const FusedArgs& a) {
   const AdamScalars sc = a.scp ? *a.scp : a.sc;
   const int k = static_cast<int>((((w.src - w.dst) % kEPL) + kEPL) % kEPL);
   if (w.src < 0)
@@ -568,6 +573,34 @@ __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ wor
     fused_item<G, P, RT, false, false>(w, a, sc, 0);
   else
     fused_item<G, P, RT, false, true>(w, a, sc, k);
+}
+
+template <typename G, typename P, int RT>
+__global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work, FusedArgs a) {
+  fused_wg<G, P, RT>(work[blockIdx.x], a);
+}
+
+// The fused step of one unit and the gather of another in one launch:
+// workgroups [0, n_fused) take the step's work items, the rest the
+// gather's, in that order.  Dispatch follows the workgroup order, so the
+// gather starts while the step's last workgroups drain instead of after
+// them.  wide: 16-byte gather lanes (else 8).  The gather copies the
+// parameter dtype P.
+template <typename G, typename P, int RT>
+__global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restrict__ fwork,
+                                                           FusedArgs fa, int n_fused,
+                                                           const Work* __restrict__ gwork,
+                                                           CopyArgs ca, int wide) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < n_fused) {
+    fused_wg<G, P, RT>(fwork[b], fa);
+    return;
+  }
+  const int i = b - n_fused;
+  if (wide)
+    copy_item<sizeof(P), 16>(gwork[i], ca, static_cast<unsigned>(i));
+  else
+    copy_item<sizeof(P), 8>(gwork[i], ca, static_cast<unsigned>(i));
 }
 
 // ------------------------------------------------- gradient accumulation
@@ -669,7 +702,7 @@ hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a
 // keep fewer pages busy while still covering the latency, once the launch
 // is long enough that its ramp does not dominate.
 unsigned fused_lds(int64_t n_work) {
-  if (n_work <= 4096) return 0;            // up to 2 rounds: full occupancy
+  if (n_work <= kSmallFusedLaunch) return 0;  // up to 2 rounds: full occupancy
   if (n_work <= 65536) return 32 * 1024;   // 5 per CU
   return 48 * 1024;                        // 3 per CU
 }
@@ -712,6 +745,21 @@ const void* pick_fused(int R) {
     case 7: return reinterpret_cast<const void*>(&k_fused<G, P, 7>);
     case 8: return reinterpret_cast<const void*>(&k_fused<G, P, 8>);
     default: return reinterpret_cast<const void*>(&k_fused<G, P, 0>);
+  }
+}
+
+template <typename G, typename P>
+const void* pick_fused_gather(int R) {
+  switch (R) {
+    case 1: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 2>);
+    case 3: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 3>);
+    case 4: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 4>);
+    case 5: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 5>);
+    case 6: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 6>);
+    case 7: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 7>);
+    case 8: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 8>);
+    default: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 0>);
   }
 }
 
@@ -828,6 +876,29 @@ hipError_t launch_set_scalars(AdamScalars* dst, const AdamScalars& sc, const Sin
 hipError_t StreamSink::launch(const void* fn, dim3 grid, dim3 block, void** args,
                               unsigned lds) const {
   return hipLaunchKernel(fn, grid, block, args, lds, stream_);
+}
+
+hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArray& grads, int R,
+                               int grad_dt, float* master, float* m, float* v, void* param,
+                               int param_dt, const AdamScalars& sc, const AdamScalars* scp,
+                               bool vec_f, const Work* gwork, int64_t n_gather,
+                               const void* shards, const PtrArray& dst, int n_dst,
+                               int lane_bytes, bool vec_g, const Sink& stream) {
+  if (n_fused <= 0 || n_gather <= 0 || n_dst < 1) return hipErrorInvalidValue;
+  if (n_fused + n_gather > 0x7fffffff) return hipErrorInvalidValue;
+  FusedArgs fa{grads, master, m, v, param, sc, scp, R, vec_f ? 1 : 0};
+  CopyArgs ca{shards, dst, n_dst, vec_g ? 1 : 0};
+  int nf = static_cast<int>(n_fused);
+  int wide = lane_bytes == 16 ? 1 : 0;
+  const void* fn;
+  if (grad_dt == FSDP_BF16)
+    fn = param_dt == FSDP_BF16 ? pick_fused_gather<u16, u16>(R) : pick_fused_gather<u16, float>(R);
+  else
+    fn = param_dt == FSDP_BF16 ? pick_fused_gather<float, u16>(R)
+                               : pick_fused_gather<float, float>(R);
+  void* args[] = {const_cast<Work**>(&fwork), &fa, &nf, const_cast<Work**>(&gwork), &ca, &wide};
+  return stream.launch(fn, dim3(static_cast<unsigned>(n_fused + n_gather)), dim3(kThreads), args,
+                       0);
 }
 
 }  // namespace fsdp

@@ -92,4 +92,18 @@ hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& s
 // Write sc to the device record dst (one single-lane kernel).
 hipError_t launch_set_scalars(AdamScalars* dst, const AdamScalars& sc, const Sink& stream);
 
+// launch_fused's step of one unit (n_fused work items), then in the same
+// launch launch_copy's gather of another (n_gather items, n_dst
+// destinations, elements of the parameter dtype).  Both counts > 0.
+hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArray& grads, int R,
+                               int grad_dt, float* master, float* m, float* v, void* param,
+                               int param_dt, const AdamScalars& sc, const AdamScalars* scp,
+                               bool vec_f, const Work* gwork, int64_t n_gather,
+                               const void* shards, const PtrArray& dst, int n_dst,
+                               int lane_bytes, bool vec_g, const Sink& stream);
+
+// Fused-step work items at or below which a launch keeps full occupancy
+// (no workgroup cap), and so gains from sharing its launch with a gather.
+constexpr int64_t kSmallFusedLaunch = 4096;
+
 }  // namespace fsdp

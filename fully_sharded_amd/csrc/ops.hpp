@@ -29,4 +29,13 @@ fsdp_status adamw_impl(const fsdp_plan* plan, const AdamScalars& sc, const AdamS
                        float* master, float* m, float* v, void* param_out, int32_t param_dtype,
                        const Sink& sink);
 
+// The fused AdamW step of `plan` (R gradient replicas) and the gather of
+// `next` (parameter dtype), in one launch when the step is short, else in
+// two; fsdp_adamw_step_then_gather's checks.
+fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
+                              const AdamScalars* scp, const void* const* grads,
+                              int32_t grad_dtype, float* master, float* m, float* v,
+                              void* param_out, int32_t param_dtype, const fsdp_plan* next,
+                              const void* next_shards, void* const* full_out, const Sink& sink);
+
 }  // namespace fsdp

@@ -3,8 +3,13 @@
 AdamW + recast of its gradients ("FSDP Training Step Walkthrough", steps 1-6;
 zwjcode FSDP2 page, section 05: one communication group per block).
 
-Three schedules, same kernels and same results bit for bit:
+Four schedules, same results bit for bit:
   serial    one stream: gather(u), step(u), gather(u+1), ...
+  overlap   one stream: gather(0), then step(u) together with gather(u+1)
+            (fsdp_adamw_step_then_gather: one launch for short steps), into
+            two alternating receive buffers, then step(last) -- the
+            prefetch of section 07 of the zwjcode FSDP2 page without a
+            second stream
   graph     the serial sequence recorded once as a HIP graph (StepGraph) and
             replayed each step with one launch
   prefetch  gathers on their own stream run ahead of the steps, into two
@@ -24,7 +29,8 @@ import ctypes
 
 import torch
 
-from .binding import Plan, StepGraph, bind_adamw_shard_step, bind_gather_unflatten
+from .binding import (Plan, StepGraph, bind_adamw_shard_step, bind_adamw_step_then_gather,
+                      bind_gather_unflatten)
 
 
 class Unit:
@@ -50,21 +56,29 @@ class StepRunner:
 
     def __init__(self, units, hp: dict, receivers, schedule: str = "serial",
                  gathers_per_step: int = 1):
-        if schedule not in ("serial", "prefetch", "graph"):
+        if schedule not in ("serial", "prefetch", "graph", "overlap"):
             raise ValueError(schedule)
-        if schedule == "prefetch" and len(receivers) < 2:
-            raise ValueError("the prefetch schedule needs two receive buffers")
+        if schedule in ("prefetch", "overlap") and len(receivers) < 2:
+            raise ValueError(f"the {schedule} schedule needs two receive buffers")
+        if schedule == "overlap" and gathers_per_step != 1:
+            raise ValueError("the overlap schedule gathers once per step")
         if gathers_per_step not in (1, 2):
             raise ValueError("gathers_per_step is 1 or 2")
         self.units = list(units)
         self.schedule = schedule
         self.gathers_per_step = gathers_per_step
-        nb = 2 if schedule == "prefetch" else 1
+        nb = 2 if schedule in ("prefetch", "overlap") else 1
         self.calls = [(bind_gather_unflatten(u.plan, u.param, receivers[i % nb]),
                        bind_adamw_shard_step(u.plan, hp, u.grads, u.master, u.m, u.v, u.param))
                       for i, u in enumerate(self.units)]
         self.stream = torch.cuda.current_stream()
         self._hs = ctypes.c_void_p(self.stream.cuda_stream)
+        if schedule == "overlap":
+            us = self.units
+            self.pairs = [bind_adamw_step_then_gather(u.plan, hp, u.grads, u.master, u.m, u.v,
+                                                      u.param, us[i + 1].plan, us[i + 1].param,
+                                                      receivers[(i + 1) % 2])
+                          for i, u in enumerate(us[:-1])]
         if schedule == "graph":
             self.graph = StepGraph(hp)
             for u in self.units:
@@ -87,6 +101,12 @@ class StepRunner:
         it before returning)."""
         if self.schedule == "graph":
             self.graph.launch(t, self._hs)
+            return
+        if self.schedule == "overlap":
+            self.calls[0][0](self._hs)
+            for pair in self.pairs:
+                pair(t, self._hs)
+            self.calls[-1][1](t, self._hs)
             return
         if self.schedule == "serial":
             for gather, fused in self.calls:
@@ -113,9 +133,10 @@ class StepRunner:
         """Bytes one rank holds ("FSDP2 ... memory peak", section 01): its
         sharded state (16 per shard element per unit), the largest unsharded
         group while gathered, and, for the prefetch schedule, the next
-        group's receive buffer; activations and temporaries excluded."""
+        group's receive buffer (prefetch and overlap schedules); activations
+        and temporaries excluded."""
         shard = sum(u.plan.state_bytes_per_rank() for u in self.units)
         largest = max(u.plan.T for u in self.units) * param_bytes
-        prefetch = largest if self.schedule == "prefetch" else 0
+        prefetch = largest if self.schedule in ("prefetch", "overlap") else 0
         return dict(sharded_state=shard, largest_unsharded_group=largest, prefetch=prefetch,
                     peak_lower_bound=shard + largest + prefetch)

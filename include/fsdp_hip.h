@@ -262,6 +262,28 @@ fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
                                int32_t grad_dtype, void* const* out, int32_t out_dtype,
                                void* stream);
 
+/* The fused AdamW shard step of one unit (fsdp_adamw_shard_step with
+ * grads_are_replicas = 1) and the all-gather + unflatten of the next unit's
+ * parameter shards (fsdp_gather_unflatten of `next`, elements of
+ * param_dtype), enqueued together: FSDP's prefetch, which all-gathers unit
+ * k+1 while unit k's gradients are reduce-scattered and its shard updated
+ * ("FSDP2 parameter all-gather, gradient reduce-scatter and memory peak",
+ * section 07; "Understanding FSDP from source", prefetching).  The results
+ * equal the two calls made one after the other.  When the step is short
+ * (at most 4,096 work items) both run in one kernel launch, the gather's
+ * workgroups after the step's, so the gather starts while the step drains;
+ * longer steps take two launches.
+ *   Arguments as in the two calls; in addition the two must not touch each
+ *   other's outputs: full_out must be disjoint from the gradients, master,
+ *   m, v and param_out, and param_out, master, m, v from next_shards (else
+ *   FSDP_ERR_INVALID_ARG). */
+fsdp_status fsdp_adamw_step_then_gather(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
+                                        int64_t step, const void* const* grads,
+                                        int32_t grad_dtype, float* master, float* m, float* v,
+                                        void* param_out, int32_t param_dtype,
+                                        const fsdp_plan* next, const void* next_shards,
+                                        void* const* full_out, void* stream);
+
 /* ---------------------------------------------------------------------
  * Step graph: a unit loop recorded once and replayed every step.
  *

@@ -1,0 +1,153 @@
+"""fsdp_adamw_step_then_gather: the fused AdamW step of one unit enqueued
+together with the all-gather of the next unit (FSDP's prefetch).  Short steps
+share one launch with the gather, long ones take two; both give the bits of
+the two separate calls, and the oracle's results."""
+
+import numpy as np
+import pytest
+import torch
+
+import fully_sharded_amd as F
+from oracle import fsdp_oracle as O
+from tests.gpu_util import (assert_adamw_close, assert_bitexact, to_dev, to_host)
+from workloads.configs import ADAMW, BLOCK_512, LINEARS_512, shapes_of
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    F.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+class HostUnit:
+    """Seeded host state of one unit: fp32 master shards (m = v = 0), the
+    parameter shards, R gradient replicas."""
+
+    def __init__(self, shapes, R, layout, seed, pdt="bf16", gdt="bf16"):
+        self.po = O.plan_layout(shapes, R, layout)
+        self.pl = F.Plan(shapes, R, layout)
+        rng = np.random.default_rng(seed)
+        full = rng.uniform(-0.05, 0.05, self.po.T).astype(np.float32)
+        self.master = O.shard_pack(self.po, full)
+        self.m = np.zeros_like(self.master)
+        self.v = np.zeros_like(self.master)
+        self.param = O.bf16_rne(self.master) if pdt == "bf16" else self.master.copy()
+        g = [(rng.standard_normal(self.po.T) * 1e-3).astype(np.float32) for _ in range(R)]
+        self.grads = [O.bf16_rne(x) for x in g] if gdt == "bf16" else g
+        self.pdt = pdt
+
+    def device(self):
+        d = dict(master=to_dev(self.master.reshape(-1)), m=to_dev(self.m.reshape(-1)),
+                 v=to_dev(self.v.reshape(-1)), param=to_dev(self.param.reshape(-1)),
+                 grads=[to_dev(x) for x in self.grads])
+        return d
+
+
+def receivers(pl, dtype, n=None):
+    return [torch.full((pl.T,), 3, dtype=dtype, device=DEV) for _ in range(n or pl.R)]
+
+
+def run_both(a: HostUnit, b: HostUnit, steps=(1, 2)):
+    """Runs the pair call and the two separate calls on copies of the same
+    state; returns both sets of device results."""
+    out = []
+    for combined in (True, False):
+        da, db = a.device(), b.device()
+        tdt = da["param"].dtype
+        recv = receivers(b.pl, tdt)
+        for t in steps:
+            if combined:
+                F.fsdp_adamw_step_then_gather(a.pl, ADAMW, t, da["grads"], da["master"], da["m"],
+                                              da["v"], da["param"], b.pl, db["param"], recv)
+            else:
+                F.fsdp_adamw_shard_step(a.pl, ADAMW, t, da["grads"], da["master"], da["m"],
+                                        da["v"], da["param"])
+                F.fsdp_gather_unflatten(b.pl, db["param"], recv)
+        torch.cuda.synchronize()
+        out.append((da, recv))
+    return out
+
+
+def assert_same(x, y):
+    for k in ("master", "m", "v", "param"):
+        assert_bitexact(to_host(x[0][k]), to_host(y[0][k]), k)
+    for r, (p, q) in enumerate(zip(x[1], y[1])):
+        assert_bitexact(to_host(p), to_host(q), f"receiver {r}")
+
+
+@pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "long_two_launches",
+                                  "long_flat"])
+def test_pair_equals_the_two_calls(case):
+    print(f"[gpu] step_then_gather {case}", flush=True)
+    blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
+    if case == "short_bf16":          # one launch; the next unit has another plan
+        a, b = HostUnit(blk, 4, "per_param", 1), HostUnit(lin, 4, "flat", 2)
+    elif case == "short_ragged_r3":   # padding, misaligned gradient sources
+        a, b = HostUnit(blk, 3, "per_param", 3), HostUnit(blk, 3, "flat", 4)
+    elif case == "short_fp32":        # fp32 gradients and parameters (4-byte gather)
+        a = HostUnit([(37, 5), (11,)], 2, "per_param", 5, pdt="f32", gdt="f32")
+        b = HostUnit([(9, 7), (3,)], 2, "per_param", 6, pdt="f32", gdt="f32")
+    elif case == "long_two_launches":  # > 4,096 work items: step, then gather
+        a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
+    else:
+        a, b = HostUnit(blk * 2, 8, "flat", 9), HostUnit(lin * 2, 8, "flat", 10)
+    pair, sep = run_both(a, b)
+    assert_same(pair, sep)
+    # and the oracle: two steps of unit a, the gather of unit b
+    mo, mm, vv = a.master, a.m, a.v
+    for t in (1, 2):
+        mo, mm, vv, _ = O.shard_step(a.po, a.grads, mo, mm, vv, t, ADAMW, a.pdt)
+    assert_adamw_close(to_host(pair[0]["master"]).reshape(a.po.R, a.po.S), mo, "master")
+    assert_adamw_close(to_host(pair[0]["m"]).reshape(a.po.R, a.po.S), mm, "m")
+    assert_adamw_close(to_host(pair[0]["v"]).reshape(a.po.R, a.po.S), vv, "v")
+    full, _ = O.gather_unflatten(b.po, b.param)
+    for r in pair[1]:
+        assert_bitexact(to_host(r), full, "gather")
+
+
+def test_skipped_receivers_and_no_receivers():
+    blk = shapes_of(BLOCK_512)
+    a, b = HostUnit(blk, 4, "per_param", 11), HostUnit(blk, 4, "per_param", 12)
+    da, db = a.device(), b.device()
+    recv = receivers(b.pl, torch.bfloat16)
+    some = [recv[0], None, recv[2], None]
+    F.fsdp_adamw_step_then_gather(a.pl, ADAMW, 1, da["grads"], da["master"], da["m"], da["v"],
+                                  da["param"], b.pl, db["param"], some)
+    torch.cuda.synchronize()
+    full, _ = O.gather_unflatten(b.po, b.param)
+    assert_bitexact(to_host(recv[0]), full, "receiver 0")
+    assert_bitexact(to_host(recv[2]), full, "receiver 2")
+    assert (recv[1] == 3).all() and (recv[3] == 3).all()   # skipped: untouched
+    # no receiver at all: only the step runs
+    dc = a.device()
+    F.fsdp_adamw_step_then_gather(a.pl, ADAMW, 1, dc["grads"], dc["master"], dc["m"], dc["v"],
+                                  dc["param"], b.pl, db["param"], [None] * 4)
+    torch.cuda.synchronize()
+    assert_bitexact(to_host(dc["master"]), to_host(da["master"]), "step only")
+
+
+def test_pair_rejects_memory_the_two_share():
+    blk = shapes_of(BLOCK_512)
+    a, b = HostUnit(blk, 4, "per_param", 13), HostUnit(blk, 4, "per_param", 14)
+    da, db = a.device(), b.device()
+    recv = receivers(b.pl, torch.bfloat16)
+    T = b.pl.T
+    args = (a.pl, ADAMW, 1, da["grads"], da["master"], da["m"], da["v"], da["param"], b.pl)
+    with pytest.raises(F.FsdpError):     # a receiver inside the master
+        bad = [da["master"].view(torch.bfloat16)[:T]] + recv[1:]
+        F.fsdp_adamw_step_then_gather(*args, db["param"], bad)
+    with pytest.raises(F.FsdpError):     # a receiver inside a gradient replica
+        F.fsdp_adamw_step_then_gather(*args, db["param"], [da["grads"][1]] + recv[1:])
+    with pytest.raises(F.FsdpError):     # the gather reads what the step writes
+        F.fsdp_adamw_step_then_gather(*args, da["param"], recv)
+    with pytest.raises(F.FsdpError):     # step counter starts at 1
+        F.fsdp_adamw_step_then_gather(a.pl, ADAMW, 0, da["grads"], da["master"], da["m"],
+                                      da["v"], da["param"], b.pl, db["param"], recv)
+    torch.cuda.synchronize()
+    assert (recv[0] == 3).all()          # nothing was enqueued

@@ -44,7 +44,8 @@ def bits(t):
     return t.view(torch.int16 if t.element_size() == 2 else torch.int32).clone()
 
 
-@pytest.mark.parametrize("schedule,gathers", [("prefetch", 1), ("serial", 2), ("prefetch", 2)])
+@pytest.mark.parametrize("schedule,gathers", [("prefetch", 1), ("serial", 2), ("prefetch", 2),
+                                              ("overlap", 1)])
 def test_schedules_agree_bit_for_bit(schedule, gathers):
     print(f"[gpu] schedule={schedule} gathers={gathers}", flush=True)
     ref_units, ref_recv = build("model12_r8")
@@ -60,7 +61,7 @@ def test_schedules_agree_bit_for_bit(schedule, gathers):
             assert torch.equal(x, y)
     # the receive buffers hold the last gathered units, the same in both runs
     n = len(units)
-    last = recv[(n - 1) % 2] if schedule == "prefetch" else recv[0]
+    last = recv[(n - 1) % 2] if schedule in ("prefetch", "overlap") else recv[0]
     for r in range(len(last)):
         assert torch.equal(last[r].view(torch.int16), ref_recv[0][r].view(torch.int16))
 
@@ -137,3 +138,28 @@ def test_step_graph_errors():
         g.add_gather(u.plan, u.param, recv[1])
     torch.cuda.synchronize()
     assert g.info() == (2, 1)
+
+
+@pytest.mark.parametrize("wl_name", ["toy_2layer_r2", "model12_flat_r8", "model12_perparam_r8"])
+def test_overlap_schedule_other_workloads(wl_name):
+    """The overlap schedule (each unit's step sharing its launch with the
+    next unit's gather) against the serial one: fp32 toy, FlatParameter
+    units, and 96 one-parameter units (ragged pieces, 3-element norms)."""
+    print(f"[gpu] overlap {wl_name}", flush=True)
+    ref_units, ref_recv = build(wl_name)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial")
+    units, recv = build(wl_name)
+    run = StepRunner(units, ADAMW, recv, "overlap")
+    for t in (1, 2, 3):
+        ref.step(t)
+        run.step(t)
+    torch.cuda.synchronize()
+    for a, b in zip(state_of(ref_units), state_of(units)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_overlap_schedule_rejects_two_gathers():
+    units, recv = build("block512_r4")
+    with pytest.raises(ValueError):
+        StepRunner(units, ADAMW, recv, "overlap", gathers_per_step=2)
