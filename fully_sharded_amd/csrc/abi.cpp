@@ -88,6 +88,7 @@ namespace {
 
 // A checked gather: its launch arguments and the memory it reads and writes.
 struct GatherCall {
+  const fsdp_plan* plan = nullptr;
   const Work* w = nullptr;
   int64_t n_work = 0;
   const void* src = nullptr;
@@ -118,14 +119,18 @@ fsdp_status prep_gather(const fsdp_plan* plan, const void* shards, int32_t dtype
   std::vector<Range> all = c->writes;
   all.push_back(c->reads[0]);
   if (any_overlap(all)) return FSDP_ERR_INVALID_ARG;
-  if (c->n_dst == 0) return FSDP_OK;
-  const fsdp_status st = plan->flat_work.device(&c->w);
-  if (st != FSDP_OK) return st;
+  c->plan = plan;
   c->n_work = static_cast<int64_t>(plan->flat_work.host.size());
   c->src = shards;
   c->es = static_cast<int>(es);
   c->lane_bytes = plan->gather_lane_bytes;
   return FSDP_OK;
+}
+
+// The work table on the current device (uploaded on first use), once every
+// check has passed.
+fsdp_status attach(GatherCall* c) {
+  return c->n_dst == 0 ? FSDP_OK : c->plan->flat_work.device(&c->w);
 }
 
 fsdp_status launch(const GatherCall& c, int R, const Sink& sink) {
@@ -186,12 +191,12 @@ fsdp_status prep_adamw(const fsdp_plan* plan, const void* const* grads, int32_t 
   c->m = m;
   c->v = v;
   c->param = param_out;
-  if (c->replicas) {
-    const fsdp_status st = plan->shard_work.device(&c->w);
-    if (st != FSDP_OK) return st;
-    c->n_work = static_cast<int64_t>(plan->shard_work.host.size());
-  }
+  if (c->replicas) c->n_work = static_cast<int64_t>(plan->shard_work.host.size());
   return FSDP_OK;
+}
+
+fsdp_status attach(AdamCall* c) {
+  return c->replicas ? c->plan->shard_work.device(&c->w) : FSDP_OK;
 }
 
 fsdp_status launch(const AdamCall& c, const AdamScalars& sc, const AdamScalars* scp,
@@ -208,7 +213,8 @@ fsdp_status launch(const AdamCall& c, const AdamScalars& sc, const AdamScalars* 
 fsdp_status gather_impl(const fsdp_plan* plan, const void* shards, int32_t dtype,
                         void* const* full_out, const Sink& sink) {
   GatherCall c;
-  const fsdp_status st = prep_gather(plan, shards, dtype, full_out, &c);
+  fsdp_status st = prep_gather(plan, shards, dtype, full_out, &c);
+  if (st == FSDP_OK) st = attach(&c);
   return st != FSDP_OK ? st : launch(c, plan->R, sink);
 }
 
@@ -217,8 +223,9 @@ fsdp_status adamw_impl(const fsdp_plan* plan, const AdamScalars& sc, const AdamS
                        float* master, float* m, float* v, void* param_out, int32_t param_dtype,
                        const Sink& sink) {
   AdamCall c;
-  const fsdp_status st = prep_adamw(plan, grads, grad_dtype, grads_are_replicas, master, m, v,
-                                    param_out, param_dtype, &c);
+  fsdp_status st = prep_adamw(plan, grads, grad_dtype, grads_are_replicas, master, m, v,
+                              param_out, param_dtype, &c);
+  if (st == FSDP_OK) st = attach(&c);
   return st != FSDP_OK ? st : launch(c, sc, scp, sink);
 }
 
@@ -243,6 +250,7 @@ fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
   for (const Range& w : a.writes)
     for (const Range& x : g.reads)
       if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
+  if ((st = attach(&a)) != FSDP_OK || (st = attach(&g)) != FSDP_OK) return st;
   if (g.n_dst == 0) return launch(a, sc, scp, sink);
   if (a.n_work > kSmallFusedLaunch || a.n_work == 0) {
     // a long step: its own launch (with its occupancy cap), then the gather

@@ -249,3 +249,81 @@ def test_header_compiles_as_c99_and_plans_from_plain_c(tmp_path):
     assert out[5] == "all_gather 2359296"
     assert out[6] == f"state_bytes {16 * 786432}"
     assert out[7] == "R=0 -> invalid argument, out NULL"
+
+
+# Argument checks of the entry points beyond the plan, on the host: every
+# check runs before the first device call, so invalid arguments are rejected
+# with FSDP_ERR_INVALID_ARG on a machine without a GPU too.  Pointers below
+# are plain numbers, disjoint 4 GiB apart, never dereferenced.
+def _fake(i, off=0):
+    return ctypes.c_void_p((1 << 40) + (i << 32) + off)
+
+
+def _parr(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*[p.value for p in ptrs])
+
+
+def test_step_then_gather_checks_arguments_before_any_device_call():
+    L = F.lib()
+    pa = F.Plan([(64, 8), (8,)], 4, "per_param")
+    pb = F.Plan([(32, 8)], 4, "flat")
+    hp = F.binding.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    grads = _parr([_fake(i) for i in range(4)])
+    master, m, v, param = _fake(10), _fake(11), _fake(12), _fake(13)
+    shards = _fake(20)
+    recv = [_fake(30 + i) for i in range(4)]
+
+    def call(step=1, h=hp, plan=pa, nxt=pb, sh=shards, rc=recv, par=param, g=grads):
+        return L.fsdp_adamw_step_then_gather(plan.handle if plan else None, ctypes.byref(h), step,
+                                             g, 1, master, m, v, par, 1,
+                                             nxt.handle if nxt else None, sh, _parr(rc), None)
+
+    assert call(plan=None) == -1
+    assert call(nxt=None) == -1
+    assert call(step=0) == -1
+    assert call(h=F.binding.AdamWHParams(1e-3, 1.0, 0.999, 1e-8, 0.01)) == -1   # beta1 = 1
+    assert call(rc=[master] + recv[1:]) == -1          # a receiver is the master
+    assert call(rc=[_fake(1, 64)] + recv[1:]) == -1    # a receiver inside gradient 1
+    assert call(sh=param) == -1                        # the gather reads what the step writes
+    assert call(sh=_fake(13, 16)) == -1                # ... or part of it
+    assert call(rc=[recv[0], recv[0]] + recv[2:]) == -1  # two receivers are one buffer
+    assert call(par=_fake(13, 1)) == -1                # bf16 parameter not 2-byte aligned
+    # valid arguments: the first device call fails without a GPU
+    assert call() == -4
+
+
+def test_step_graph_checks_arguments_without_a_device():
+    L = F.lib()
+    hp = F.binding.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    bad = F.binding.AdamWHParams(1e-3, 0.9, 0.999, 0.0, 0.01)       # eps = 0
+    g = ctypes.c_void_p(77)
+    assert L.fsdp_step_graph_create(ctypes.byref(hp), None) == -1
+    assert L.fsdp_step_graph_create(ctypes.byref(bad), ctypes.byref(g)) == -1
+    assert g.value is None                     # cleared on error
+    assert L.fsdp_step_graph_create(ctypes.byref(hp), ctypes.byref(g)) == -4   # no device
+    assert g.value is None
+    L.fsdp_step_graph_destroy(None)
+    n, a = ctypes.c_int64(), ctypes.c_int64()
+    assert L.fsdp_step_graph_info(None, ctypes.byref(n), ctypes.byref(a)) == -1
+    assert L.fsdp_step_graph_launch(None, 1, None) == -1
+    pa = F.Plan([(8,)], 2, "flat")
+    assert L.fsdp_step_graph_add_gather(None, pa.handle, _fake(1), 1, _parr([_fake(2), _fake(3)])) == -1
+
+
+def test_reshard_batch_checks_arguments_before_any_device_call():
+    L = F.lib()
+    a, b = F.Plan([(40, 3)], 4, "per_param"), F.Plan([(40, 3)], 3, "flat")
+    rs = F.Resharder(a, b)
+    srcs = [_fake(i) for i in range(3)]
+    dsts = [_fake(10 + i) for i in range(3)]
+
+    def call(s, d, n=None):
+        return L.fsdp_reshard_batch(rs.handle, len(s) if n is None else n, _parr(s), _parr(d), 0,
+                                    None)
+
+    assert call(srcs, dsts, n=0) == -1
+    assert call([_fake(i) for i in range(65)], [_fake(100 + i) for i in range(65)]) == -2
+    assert call(srcs, [dsts[0], dsts[0], dsts[2]]) == -1        # two destinations are one
+    assert call(srcs, [srcs[1]] + dsts[1:]) == -1               # a destination is a source
+    assert call(srcs, [_fake(10, 2)] + dsts[1:]) == -1          # fp32 misaligned
+    assert call(srcs, dsts) == -4                               # valid: no device here
