@@ -113,6 +113,12 @@ def test_step_parity_small_workloads(name):
             assert_adamw_close(gm, master_o, f"master t={t}")
             assert_adamw_close(to_host(m_d).reshape(R, S), m_o, f"m t={t}")
             assert_adamw_close(to_host(v_d).reshape(R, S), v_o, f"v t={t}")
+            # stronger than the tolerance: the kernels evaluate the update in
+            # IEEE double in the definition's order, as the oracle does, so
+            # the rounded fp32 results agree bit for bit
+            assert_bitexact(gm, master_o, f"master bits t={t}")
+            assert_bitexact(to_host(m_d).reshape(R, S), m_o, f"m bits t={t}")
+            assert_bitexact(to_host(v_d).reshape(R, S), v_o, f"v bits t={t}")
             gp = to_host(param_d).reshape(R, S)
             if pdt == "bf16":
                 assert_bf16_within_ulp(gp, param_o, f"param t={t}")
