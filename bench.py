@@ -47,6 +47,10 @@ def parse():
                          "double receive buffer; graph: the serial sequence replayed as one "
                          "HIP graph per step; overlap: each unit's fused step shares its "
                          "launch with the next unit's gather (double receive buffer)")
+    ap.add_argument("--cycle-gib", type=float, default=4.0,
+                    help="give the workload enough independent copies of its buffers that "
+                         "one round of steps touches at least this many GiB (the 256 MB "
+                         "last-level cache keeps part of a smaller cycle between steps)")
     ap.add_argument("--gathers-per-step", type=int, choices=(1, 2), default=1,
                     help="1: parameters kept from forward to backward "
                          "(reshard_after_forward=False); 2: freed after forward and "
@@ -252,11 +256,12 @@ def main():
     plans, units = setup_units(wl, dev)
     if args.mode != "step":
         return run_mode(args, wl, plans, units)
-    # A workload smaller than 1 GiB would stay in the 256 MB last-level
-    # cache (MALL) when re-run: give it several independent copies of its
-    # buffers and let consecutive steps cycle through them.
+    # A small workload would partly stay in the 256 MB last-level cache
+    # (MALL) when re-run: give it independent copies of its buffers, cycled
+    # step by step, so that one round touches at least --cycle-gib GiB.
     ws = sum(u.plan.T * (2 * R + 28) for u in units)
-    n_copies = 1 if ws >= (1 << 30) else min(16, -(-(1 << 30) // ws))
+    cycle = int(args.cycle_gib * (1 << 30))
+    n_copies = 1 if ws >= cycle else min(32, -(-cycle // ws))
     copies = [units] + [setup_units(wl, dev)[1] for _ in range(n_copies - 1)]
     T_max = max(p.T for p in plans.values())
     n_recv = 2 if args.schedule in ("prefetch", "overlap") else 1
