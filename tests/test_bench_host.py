@@ -1,0 +1,104 @@
+"""Host logic of bench.py (no GPU): the counter summary that turns two
+rocprofv3 --pmc CSVs into HBM bytes per launch, the traffic file's
+validity check, the launch count per step, and the buffer carving rule."""
+
+import argparse
+import csv
+import json
+
+import pytest
+import torch
+
+import bench
+import fully_sharded_amd as F
+from workloads.configs import BLOCK_512, shapes_of
+
+FUSED = "void fsdp::(anonymous namespace)::k_fused<unsigned short, unsigned short, 8>(Work const*)"
+PAIR = ("void fsdp::(anonymous namespace)::k_fused_gather<unsigned short, unsigned short, 8>"
+        "(Work const*)")
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::copy_kernel>(int)"
+
+
+def write_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+        # another counter in the same file is ignored
+        w.writerow({"Kernel_Name": FUSED, "Counter_Name": "GRBM_COUNT", "Counter_Value": 1})
+
+
+@pytest.fixture
+def traffic_dir(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "traffic_path",
+                        lambda wl, key: str(tmp_path / f"traffic_{wl}_{key}.json"))
+    return tmp_path
+
+
+def test_counter_summary_scales_by_the_calibration_copy(traffic_dir, capsys):
+    fetch, write = traffic_dir / "f.csv", traffic_dir / "w.csv"
+    gib_kib = float(1 << 20)
+    # FETCH_SIZE reads half of what the 1 GiB copy moves, WRITE_SIZE all of it
+    write_csv(fetch, "FETCH_SIZE", [(FUSED, 100.0), (FUSED, 102.0), (PAIR, 300.0),
+                                    (COPY, gib_kib / 2)])
+    write_csv(write, "WRITE_SIZE", [(FUSED, 50.0), (FUSED, 50.0), (PAIR, 90.0), (COPY, gib_kib)])
+    bench.summarise_counters(str(fetch), str(write), "wl")
+    fused = json.load(open(traffic_dir / "traffic_wl_fused.json"))
+    pair = json.load(open(traffic_dir / "traffic_wl_fused_gather.json"))
+    assert fused["fetch_scale"] == pytest.approx(2.0) and fused["write_scale"] == pytest.approx(1.0)
+    # the k_fused rows only: the k_fused_gather dispatch is not mixed in
+    assert fused["fetch_kib_per_launch"] == pytest.approx(101.0)
+    assert fused["bytes_per_launch"] == pytest.approx((101.0 * 2 + 50.0) * 1024)
+    assert pair["dispatches"] == {"FETCH_SIZE": 1, "WRITE_SIZE": 1}
+    assert pair["bytes_per_launch"] == pytest.approx((300.0 * 2 + 90.0) * 1024)
+    assert fused["kernel_src_sha"] == bench.kernel_src_hash()
+
+
+def test_counter_summary_needs_the_calibration_copy(traffic_dir):
+    fetch, write = traffic_dir / "f.csv", traffic_dir / "w.csv"
+    write_csv(fetch, "FETCH_SIZE", [(FUSED, 100.0)])
+    write_csv(write, "WRITE_SIZE", [(FUSED, 50.0)])
+    with pytest.raises(SystemExit):
+        bench.summarise_counters(str(fetch), str(write), "wl")
+
+
+def test_traffic_is_dropped_once_the_kernels_change(traffic_dir, monkeypatch):
+    path = traffic_dir / "traffic_wl_fused.json"
+    json.dump({"kernel_src_sha": bench.kernel_src_hash(), "bytes_per_launch": 123.0},
+              open(path, "w"))
+    assert bench.load_traffic("wl", "fused") == 123.0
+    assert bench.load_traffic("other", "fused") is None
+    monkeypatch.setattr(bench, "kernel_src_hash", lambda: "changed")
+    assert bench.load_traffic("wl", "fused") is None
+
+
+class _Unit:
+    def __init__(self, plan):
+        self.plan = plan
+
+
+def test_launches_per_step_by_schedule():
+    blk = F.Plan(shapes_of(BLOCK_512), 8, "per_param")          # 3,073 work items
+    big = F.Plan(shapes_of(BLOCK_512) * 2, 8, "per_param")      # > 4,096 work items
+    assert len(blk.work_items(0)) <= 4096 < len(big.work_items(0))
+    units = [_Unit(blk)] * 12
+    a = argparse.Namespace
+    assert bench.launches_per_step(a(schedule="serial", gathers_per_step=1), units) == 24
+    assert bench.launches_per_step(a(schedule="serial", gathers_per_step=2), units) == 36
+    assert bench.launches_per_step(a(schedule="graph", gathers_per_step=1), units) == 25
+    # gather(0), 11 pair launches, the last step
+    assert bench.launches_per_step(a(schedule="overlap", gathers_per_step=1), units) == 13
+    # long steps keep their own launch
+    mixed = [_Unit(big), _Unit(blk), _Unit(big)]
+    assert bench.launches_per_step(a(schedule="overlap", gathers_per_step=1), mixed) == 1 + 2 + 1 + 1
+
+
+def test_rows_stagger_strides_that_are_multiples_of_4k():
+    a = bench.rows(3, 1024, torch.float32, "cpu")          # 4 KiB per row -> stride + 256 B
+    assert a[1].data_ptr() - a[0].data_ptr() == 4096 + 256
+    b = bench.rows(3, 1000, torch.float32, "cpu")          # 4,000 B -> 4,096 B: + 256 B too
+    assert b[1].data_ptr() - b[0].data_ptr() == 4096 + 256
+    c = bench.rows(2, 100, torch.bfloat16, "cpu")          # 200 B -> 256 B
+    assert c[1].data_ptr() - c[0].data_ptr() == 256
+    assert all(t.numel() == 1024 for t in a) and all(t.numel() == 100 for t in c)
