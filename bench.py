@@ -78,10 +78,17 @@ def parse():
 
 
 def kernel_src_hash():
+    """Hash of the sources that decide what the kernels do and how they are
+    launched, comments and blank space left out (editing a comment does not
+    change a kernel)."""
+    import re
     h = hashlib.sha256()
     for f in ("kernels.hip", "kernels.hpp", "plan.cpp", "abi.cpp"):
-        with open(os.path.join(ROOT, "fully_sharded_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "fully_sharded_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -340,6 +347,43 @@ def main():
                 pair(step_no[0], hs)
         pair_avg_ms = timed(pair_pass) * len(units) / (len(units) - 1)
 
+    # the other steps of the path, each timed alone the same way: the
+    # reduce-scatter-average and AdamW + recast unfused (a4, a5 + a6), and
+    # the init-time pack of the fp32 master and of the cast parameter (a2)
+    extra = {}
+    for ri, r in enumerate(runners):
+        r_units = copies[ri]
+        outs = [torch.empty(u.plan.R * u.plan.S, dtype=torch.float32, device=dev)
+                for u in r_units]
+        fulls = [torch.empty(u.plan.T, dtype=torch.float32, device=dev).uniform_(-0.05, 0.05)
+                 for u in r_units]
+        extra[ri] = dict(
+            rs=[F.bind_reduce_scatter_avg(u.plan, u.grads, o) for u, o in zip(r_units, outs)],
+            adamw=[F.bind_adamw_shard_step(u.plan, ADAMW, o, u.master, u.m, u.v, u.param,
+                                           grads_are_replicas=False)
+                   for u, o in zip(r_units, outs)],
+            pack=[F.bind_shard_pack(u.plan, f, u.master) for u, f in zip(r_units, fulls)],
+            cast=[F.bind_shard_pack(u.plan, f, u.param) for u, f in zip(r_units, fulls)],
+            keep=(outs, fulls))
+    xp = [0]
+
+    def pass_of(name, with_step=False):
+        def run():
+            xp[0] += 1
+            step_no[0] += 1
+            for call in extra[xp[0] % len(runners)][name]:
+                if with_step:
+                    call(step_no[0], hs)
+                else:
+                    call(hs)
+        return run
+
+    rs_avg_ms = timed(pass_of("rs"))
+    adamw_avg_ms = timed(pass_of("adamw", with_step=True))
+    pack_avg_ms = timed(pass_of("pack"))
+    cast_avg_ms = timed(pass_of("cast"))
+    del extra
+
     # algorithmic bytes (valid parameters only, padding excluded)
     ges = 2 if gdt == torch.bfloat16 else 4
     pes = 2 if pdt == torch.bfloat16 else 4
@@ -356,6 +400,13 @@ def main():
                              "bytes": float(np.mean(gather_bytes_unit)), "gbps": gather_gbps},
         "timed_launches_each": reps * len(units),
     }
+    Tm = float(np.mean([u.plan.T for u in units]))
+    for key, ms, per_param in (("reduce_scatter_avg", rs_avg_ms, ges * R + 4),
+                               ("adamw_recast", adamw_avg_ms, 4 + 24 + pes),
+                               ("shard_pack_f32", pack_avg_ms, 8),
+                               ("shard_pack_cast", cast_avg_ms, 4 + pes)):
+        kernels[key] = {"avg_ms": ms, "bytes": Tm * per_param,
+                        "gbps": Tm * per_param / (ms * 1e-3) / 1e9}
     # the dominant kernel of the step as scheduled: the fused step, or, in
     # the overlap schedule with short steps, the launch that holds one
     # unit's fused step and the next unit's gather

@@ -453,27 +453,37 @@ def bind_gather_unflatten(plan: Plan, shards: torch.Tensor, full_out) -> "BoundC
     return run
 
 
-def bind_adamw_shard_step(plan: Plan, hp: dict, grads, master, m, v, param_out):
-    """fsdp_adamw_shard_step (fused, R gradient replicas) with cached
-    arguments; call as f(step, stream=None)."""
+def bind_adamw_shard_step(plan: Plan, hp: dict, grads, master, m, v, param_out,
+                          grads_are_replicas: bool = True):
+    """fsdp_adamw_shard_step with cached arguments; call as
+    f(step, stream=None).  grads: R gradient replicas (fused with the
+    reduce-scatter), or with grads_are_replicas=False one fp32 [R*S] tensor
+    (the reduce-scatter's output)."""
     n = plan.R * plan.S
     for t, nm in ((master, "master"), (m, "m"), (v, "v")):
         if t.numel() != n or t.dtype != torch.float32:
             raise ValueError(f"{nm} must be fp32 with R*S elements")
-    if param_out.numel() != n or len(grads) != plan.R:
-        raise ValueError("size mismatch with the plan")
-    dt = _dtype_code(grads[0])
-    for g in grads:
-        if g.numel() != plan.T or _dtype_code(g) != dt:
-            raise ValueError("gradient size or dtype mismatch")
-    arr = _ptr_array(grads, "grads")
+    if grads_are_replicas:
+        if param_out.numel() != n or len(grads) != plan.R:
+            raise ValueError("size mismatch with the plan")
+        dt = _dtype_code(grads[0])
+        for g in grads:
+            if g.numel() != plan.T or _dtype_code(g) != dt:
+                raise ValueError("gradient size or dtype mismatch")
+        keep_g = list(grads)
+    else:
+        if param_out.numel() != n or grads.numel() != n or grads.dtype != torch.float32:
+            raise ValueError("the reduced gradient must be fp32 with R*S elements")
+        dt = F32
+        keep_g = [grads]
+    arr = _ptr_array(keep_g, "grads")
     h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
     head = (plan.handle, ctypes.byref(h))
-    tail = (arr, dt, 1, ctypes.c_void_p(_dev(master, "master")), ctypes.c_void_p(_dev(m, "m")),
-            ctypes.c_void_p(_dev(v, "v")), ctypes.c_void_p(_dev(param_out, "param_out")),
-            _dtype_code(param_out))
+    tail = (arr, dt, int(bool(grads_are_replicas)), ctypes.c_void_p(_dev(master, "master")),
+            ctypes.c_void_p(_dev(m, "m")), ctypes.c_void_p(_dev(v, "v")),
+            ctypes.c_void_p(_dev(param_out, "param_out")), _dtype_code(param_out))
     call = BoundCall("fsdp_adamw_shard_step", None,
-                     (plan, h, list(grads), master, m, v, param_out))
+                     (plan, h, keep_g, master, m, v, param_out))
 
     def run(step, stream=None):
         call._run(*head, int(step), *tail, _stream(stream))
@@ -532,6 +542,38 @@ def bind_adamw_step_then_gather(plan: Plan, hp: dict, grads, master, m, v, param
 
     def run(step, stream=None):
         call._run(*head, int(step), *tail, _stream(stream))
+    run.call = call
+    return run
+
+
+def bind_reduce_scatter_avg(plan: Plan, grads, out: torch.Tensor):
+    """fsdp_reduce_scatter_avg with cached arguments; call as f(stream=None)."""
+    if len(grads) != plan.R or out.numel() != plan.R * plan.S or out.dtype != torch.float32:
+        raise ValueError("need R gradients and an fp32 [R*S] output")
+    dt = _dtype_code(grads[0])
+    for g in grads:
+        if g.numel() != plan.T or _dtype_code(g) != dt:
+            raise ValueError("gradient size or dtype mismatch")
+    arr = _ptr_array(grads, "grads")
+    o = ctypes.c_void_p(_dev(out, "out"))
+    call = BoundCall("fsdp_reduce_scatter_avg", None, (plan, list(grads), out))
+
+    def run(stream=None):
+        call._run(plan.handle, arr, dt, o, _stream(stream))
+    run.call = call
+    return run
+
+
+def bind_shard_pack(plan: Plan, full: torch.Tensor, shards: torch.Tensor):
+    """fsdp_shard_pack with cached arguments; call as f(stream=None)."""
+    if full.numel() != plan.T or shards.numel() != plan.R * plan.S:
+        raise ValueError("size mismatch with the plan")
+    args = (plan.handle, ctypes.c_void_p(_dev(full, "full")), _dtype_code(full),
+            ctypes.c_void_p(_dev(shards, "shards")), _dtype_code(shards))
+    call = BoundCall("fsdp_shard_pack", None, (plan, full, shards))
+
+    def run(stream=None):
+        call._run(*args, _stream(stream))
     run.call = call
     return run
 

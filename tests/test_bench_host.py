@@ -102,3 +102,17 @@ def test_rows_stagger_strides_that_are_multiples_of_4k():
     c = bench.rows(2, 100, torch.bfloat16, "cpu")          # 200 B -> 256 B
     assert c[1].data_ptr() - c[0].data_ptr() == 256
     assert all(t.numel() == 1024 for t in a) and all(t.numel() == 100 for t in c)
+
+
+def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "fully_sharded_amd" / "csrc"
+    src.mkdir(parents=True)
+    files = ("kernels.hip", "kernels.hpp", "plan.cpp", "abi.cpp")
+    for f in files:
+        (src / f).write_text("int f() { return 1; }\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_src_hash()
+    (src / "kernels.hip").write_text("// a comment\nint f() {  /* more */ return 1; }\n\n")
+    assert bench.kernel_src_hash() == h0
+    (src / "kernels.hip").write_text("int f() { return 2; }\n")
+    assert bench.kernel_src_hash() != h0
