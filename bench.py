@@ -238,7 +238,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the R ranks are virtual ranks in one GPU's "
-              f"memory and this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              f"memory and the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
