@@ -352,8 +352,10 @@ def flat_index(po, r, j):
 
 
 def test_model12_r8_full_step_bench_launch_configuration():
-    """The 12-layer R=8 model, per step: gather(u) then fused(u) per unit,
-    as the benchmark times it; 3 steps.  Units 0 and 11 are checked whole,
+    """The 12-layer R=8 model, 3 steps, in the benchmark's default launch
+    configuration: per step the gather of unit 0, then one launch per unit u
+    holding u's fused step and unit u+1's gather (two alternating receive
+    buffers), then unit 11's fused step.  Units 0 and 11 are checked whole,
     the others on sampled elements."""
     wl = WORKLOADS["model12_r8"]
     R = wl["R"]
@@ -362,6 +364,7 @@ def test_model12_r8_full_step_bench_launch_configuration():
     pg = F.Plan(shapes, R, wl["layout"])
     T, S = po.T, po.S
     n_units = len(wl["units"])
+    last = n_units - 1
     banner(f"model12_r8: {n_units} units, T={T}, S={S}")
     rng = np.random.default_rng(12)
     rs_, js_ = sample_positions(rng, R, S, 4096)
@@ -378,22 +381,33 @@ def test_model12_r8_full_step_bench_launch_configuration():
         state.append([md, torch.zeros_like(md), torch.zeros_like(md), pd])
         mo = O.shard_pack(po, to_host(full))
         oracle.append([mo, np.zeros_like(mo), np.zeros_like(mo), O.bf16_rne(mo)])
-    recv = [torch.empty(T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    recv = [[torch.empty(T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+            for _ in range(2)]
+
+    def check_gather(u, t):
+        """Unit u's receivers hold the gather of its current parameter."""
+        want, _ = O.gather_unflatten(po, oracle[u][3])
+        got = to_host(recv[u % 2][3])
+        if t == 1:
+            assert_bitexact(got, want, f"gather u={u}")
+        else:
+            assert_bf16_within_ulp(got, want, f"gather u={u}")
+
     for t in range(1, wl["steps"] + 1):
+        F.fsdp_gather_unflatten(pg, state[0][3], recv[0])
+        check_gather(0, t)
         for u in range(n_units):
             md, m, v, pd = state[u]
-            F.fsdp_gather_unflatten(pg, pd, recv)
-            if u in (0, n_units - 1):
-                want, _ = O.gather_unflatten(po, oracle[u][3])
-                got = to_host(recv[3])
-                if t == 1:
-                    assert_bitexact(got, want, f"gather u={u}")
-                else:
-                    assert_bf16_within_ulp(got, want, f"gather u={u}")
             grads = [gen.device_grad(wl, t, u, r, T, DEV) for r in range(R)]
-            F.fsdp_adamw_shard_step(pg, ADAMW, t, grads, md, m, v, pd)
+            if u < last:
+                F.fsdp_adamw_step_then_gather(pg, ADAMW, t, grads, md, m, v, pd, pg,
+                                              state[u + 1][3], recv[(u + 1) % 2])
+                if u + 1 == last:
+                    check_gather(last, t)
+            else:
+                F.fsdp_adamw_shard_step(pg, ADAMW, t, grads, md, m, v, pd)
             o = oracle[u]
-            if u in (0, n_units - 1):
+            if u in (0, last):
                 hg = [to_host(g) for g in grads]
                 o[0], o[1], o[2], o[3] = O.shard_step(po, hg, o[0], o[1], o[2], t, ADAMW, "bf16")
                 gm = to_host(md).reshape(R, S)
@@ -417,8 +431,9 @@ def test_model12_r8_full_step_bench_launch_configuration():
                 assert_adamw_close(to_host(v[idx]), v1, f"v u={u} sampled")
                 assert_bf16_within_ulp(to_host(pd[idx]), O.bf16_rne(p1), f"param u={u} sampled")
         banner(f"model12_r8 step {t} ok")
-    for r in range(1, R):
-        assert torch.equal(recv[0].view(torch.int16), recv[r].view(torch.int16))
+    for b in recv:
+        for r in range(1, R):
+            assert torch.equal(b[0].view(torch.int16), b[r].view(torch.int16))
 
 
 def test_group4096_flat_r8_full_size_sampled():
