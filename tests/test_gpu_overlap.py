@@ -151,3 +151,23 @@ def test_pair_rejects_memory_the_two_share():
                                       da["v"], da["param"], b.pl, db["param"], recv)
     torch.cuda.synchronize()
     assert (recv[0] == 3).all()          # nothing was enqueued
+
+
+@pytest.mark.parametrize("R", [1, 2, 64])
+def test_pair_at_extreme_world_sizes(R):
+    """One rank (the step is local, the gather a copy) and 64 ranks (most
+    ranks own no rows of the small parameters): the pair call equals the two
+    calls and the oracle."""
+    print(f"[gpu] step_then_gather R={R}", flush=True)
+    shapes = [(65, 9), (7,), (130, 3)]
+    a = HostUnit(shapes, R, "per_param", 20 + R)
+    b = HostUnit([(33, 4), (5,)], R, "flat", 40 + R)
+    pair, sep = run_both(a, b)
+    assert_same(pair, sep)
+    mo, mm, vv = a.master, a.m, a.v
+    for t in (1, 2):
+        mo, mm, vv, _ = O.shard_step(a.po, a.grads, mo, mm, vv, t, ADAMW, a.pdt)
+    assert_adamw_close(to_host(pair[0]["master"]).reshape(a.po.R, a.po.S), mo, "master")
+    full, _ = O.gather_unflatten(b.po, b.param)
+    for r in pair[1]:
+        assert_bitexact(to_host(r), full, "gather")
