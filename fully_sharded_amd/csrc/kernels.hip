@@ -694,21 +694,24 @@ hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a
 }
 
 // Workgroups of the fused step resident per CU, set through LDS: the kernel
-// uses none, so asking for 160 KB / n per workgroup caps a CU at n of them.
-// Measured on MI355X (R = 8, hidden-512 blocks, bf16 gradients, 4+ GB of
-// buffers cycled so the last-level cache serves nothing), GB/s at 8 / 5 / 3
-// workgroups per CU: 1 block (3,073 items) 5353 / 5300 / 5219; 4 blocks
-// 5767 / 5836 / 5763; 16 blocks (49k items) 5920 / 6136 / 6031; 32 blocks
-// 5704 / 5885 / 6086; 128 blocks (394k items) 5404 / 5641 / 5824; and the
-// 872M-parameter group (852k items) 5674 / 5931 / 6205.  Sixteen streams
-// per workgroup (8 gradients, 3 states read; 4 arrays written) are far more
-// than the DRAM pages one channel keeps open; fewer workgroups in flight
-// keep fewer pages busy while still covering the latency, once the launch
-// is long enough that its ramp does not dominate.
+// uses none, so asking for L bytes per workgroup lets at most
+// floor(LDS per CU / L) of them share a CU.  Measured on MI355X with
+// per-workgroup timestamps: without LDS the kernel's own resources allow 5
+// per CU (1,280 resident); 32 KB gives 4, 48 KB 3, 64 KB 2.  GB/s at 5 / 4
+// / 3 per CU (R = 8, hidden-512 blocks, bf16 gradients, 4+ GB of buffers
+// cycled so the last-level cache serves nothing): 1 block (3,073 items)
+// 5353 / 5300 / 5219; 4 blocks 5767 / 5836 / 5763; 16 blocks (49k items)
+// 5920 / 6136 / 6031; 32 blocks 5704 / 5885 / 6086; 128 blocks (394k items)
+// 5404 / 5641 / 5824; the 872M-parameter group (852k items)
+// 5674 / 5931 / 6205.  Sixteen streams per workgroup (8 gradients, 3 states
+// read; 4 arrays written) are far more than the DRAM pages one channel
+// keeps open; fewer workgroups in flight keep fewer pages busy while still
+// covering the latency, once the launch is long enough that its ramp does
+// not dominate.
 unsigned fused_lds(int64_t n_work) {
-  if (n_work <= kSmallFusedLaunch) return 0;  // up to 2 rounds: full occupancy
-  if (n_work <= 65536) return 32 * 1024;   // 5 per CU
-  return 48 * 1024;                        // 3 per CU
+  if (n_work <= kSmallFusedLaunch) return 0;  // short: the kernel's own 5 per CU
+  if (n_work <= 65536) return 32 * 1024;        // 4 per CU
+  return 48 * 1024;                             // 3 per CU
 }
 
 template <typename G>
