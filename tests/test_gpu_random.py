@@ -1,0 +1,110 @@
+"""Randomised sequences through the C ABI against the oracle: random small
+units (1-4 parameters, 1-3 dims, dims 1-70), random R (1-16) and layouts;
+per case pack, two steps through the paired step-then-gather call, a
+re-shard of the trained state to another R and layout, the averaged
+all-reduce and a two-micro-batch accumulation.  Bit-exact wherever the
+contract says so, AdamW to its tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+import fully_sharded_amd as F
+from oracle import fsdp_oracle as O
+from tests.gpu_util import (assert_adamw_close, assert_bf16_within_ulp, assert_bitexact,
+                            to_dev, to_host)
+from workloads.configs import ADAMW
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    F.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def random_shapes(rng):
+    out = []
+    for _ in range(int(rng.integers(1, 5))):
+        nd = int(rng.integers(1, 4))
+        out.append(tuple(int(x) for x in rng.integers(1, 71, nd)))
+    return out
+
+
+def random_unit(rng, R, layout):
+    shapes = random_shapes(rng)
+    po = O.plan_layout(shapes, R, layout)
+    full = rng.uniform(-1, 1, po.T).astype(np.float32)
+    grads = [O.bf16_rne((rng.standard_normal(po.T) * 1e-2).astype(np.float32))
+             for _ in range(R)]
+    return shapes, po, full, grads
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_sequence_matches_the_oracle(seed):
+    rng = np.random.default_rng(9000 + seed)
+    R = int(rng.integers(1, 17))
+    layout = ["per_param", "flat"][int(rng.integers(0, 2))]
+    print(f"[gpu] random seed={seed} R={R} {layout}", flush=True)
+    shapes, po, full, grads = random_unit(rng, R, layout)
+    nshapes, npo, nfull, _ = random_unit(rng, R, ["per_param", "flat"][int(rng.integers(0, 2))])
+    pg, npg = F.Plan(shapes, R, layout), F.Plan(nshapes, R, npo.layout)
+
+    # pack: fp32 master exactly, bf16 parameter through RNE
+    master = torch.empty(R * po.S, device=DEV)
+    param = torch.empty(R * po.S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_shard_pack(pg, to_dev(full), master)
+    F.fsdp_shard_pack(pg, to_dev(full), param)
+    mo = O.shard_pack(po, full)
+    assert_bitexact(to_host(master).reshape(R, po.S), mo, "pack f32")
+    assert_bitexact(to_host(param).reshape(R, po.S), O.bf16_rne(mo), "pack bf16")
+    nparam = torch.empty(R * npo.S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_shard_pack(npg, to_dev(nfull), nparam)
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    recv = [torch.empty(npo.T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    g_d = [to_dev(g) for g in grads]
+
+    # two steps, each with the next unit's gather in the same call
+    om, ov = np.zeros_like(mo), np.zeros_like(mo)
+    for t in (1, 2):
+        F.fsdp_adamw_step_then_gather(pg, ADAMW, t, g_d, master, m, v, param, npg, nparam, recv)
+        mo, om, ov, po_param = O.shard_step(po, grads, mo, om, ov, t, ADAMW, "bf16")
+        torch.cuda.synchronize()
+        gm = to_host(master).reshape(R, po.S)
+        assert_adamw_close(gm, mo, f"master t={t}")
+        assert_adamw_close(to_host(m).reshape(R, po.S), om, f"m t={t}")
+        assert_adamw_close(to_host(v).reshape(R, po.S), ov, f"v t={t}")
+        gp = to_host(param).reshape(R, po.S)
+        assert_bf16_within_ulp(gp, po_param, f"param t={t}")
+        assert_bitexact(gp, O.bf16_rne(gm), "param = RNE(master)")
+        want, _ = O.gather_unflatten(npo, O.bf16_rne(O.shard_pack(npo, nfull)))
+        for r in recv:
+            assert_bitexact(to_host(r), want, "next unit's gather")
+
+    # re-shard the trained fp32 state to another world size and layout
+    R2 = int(rng.integers(1, 17))
+    l2 = ["per_param", "flat"][int(rng.integers(0, 2))]
+    po2 = O.plan_layout(shapes, R2, l2)
+    rs = F.Resharder(pg, F.Plan(shapes, R2, l2))
+    outs = [torch.full((R2 * po2.S,), 9.0, device=DEV) for _ in range(3)]
+    F.fsdp_reshard_batch(rs, [master, m, v], outs)
+    for got, src in zip(outs, (master, m, v)):
+        assert_bitexact(to_host(got).reshape(R2, po2.S),
+                        O.reshard(po, po2, to_host(src).reshape(R, po.S)), "reshard")
+
+    # DDP's averaged all-reduce and a two-micro-batch accumulation
+    ar = [torch.empty(po.T, device=DEV) for _ in range(R)]
+    F.fsdp_allreduce_avg(pg, g_d, ar)
+    want = O.allreduce_avg(grads)
+    for a, w in zip(ar, want):
+        assert_bitexact(to_host(a), w, "all-reduce")
+    acc = [torch.empty(po.T, device=DEV) for _ in range(R)]
+    F.fsdp_grad_accumulate(pg, g_d, acc, True)
+    F.fsdp_grad_accumulate(pg, g_d[::-1], acc, False)
+    for r in range(R):
+        assert_bitexact(to_host(acc[r]), O.grad_accumulate([grads[r], grads[R - 1 - r]]),
+                        "accumulate")
