@@ -268,7 +268,8 @@ fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
  * param_dtype), enqueued together: FSDP's prefetch, which all-gathers unit
  * k+1 while unit k's gradients are reduce-scattered and its shard updated
  * ("FSDP2 parameter all-gather, gradient reduce-scatter and memory peak",
- * section 07; "Understanding FSDP from source", prefetching).  The results
+ * section 07; "Understanding FSDP from source", section 5, overlap of
+ * communication and computation).  The results
  * equal the two calls made one after the other.  When the step is short
  * (at most 4,096 work items) both run in one kernel launch, the gather's
  * workgroups after the step's, so the gather starts while the step drains;
