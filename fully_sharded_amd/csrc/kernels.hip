@@ -209,11 +209,11 @@ __device__ __forceinline__ void grad_avg4(const PtrArray& g, int R, int64_t s, i
 #pragma unroll
     for (int q = 0; q < RT; ++q) grad_load4<G, RT, SHIFT>(g, q, s, k, x[q]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float acc = x[0][k];
+    for (int j = 0; j < 4; ++j) {
+      float acc = x[0][j];
 #pragma unroll
-      for (int q = 1; q < RT; ++q) acc = acc + x[q][k];
-      avg[k] = acc / static_cast<float>(RT);
+      for (int q = 1; q < RT; ++q) acc = acc + x[q][j];
+      avg[j] = acc / static_cast<float>(RT);
     }
   } else {
     grad_load4<G, RT, SHIFT>(g, 0, s, k, avg);
@@ -221,11 +221,11 @@ __device__ __forceinline__ void grad_avg4(const PtrArray& g, int R, int64_t s, i
       float x[4];
       grad_load4<G, RT, SHIFT>(g, q, s, k, x);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) avg[k] = avg[k] + x[k];
+      for (int j = 0; j < 4; ++j) avg[j] = avg[j] + x[j];
     }
     const float fr = static_cast<float>(R);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) avg[k] = avg[k] / fr;
+    for (int j = 0; j < 4; ++j) avg[j] = avg[j] / fr;
   }
 }
 
@@ -330,7 +330,7 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs& a, unsi
             v = ld_nt16_shifted(al, k * ES);
         }
       }
-      for (int k = 0, r = first; k < a.n_dst; ++k, r = r + 1 == a.n_dst ? 0 : r + 1) {
+      for (int i = 0, r = first; i < a.n_dst; ++i, r = r + 1 == a.n_dst ? 0 : r + 1) {
         E* d = static_cast<E*>(const_cast<void*>(a.dst.p[r]));
         if (d) Lane<W>::store(d + e0, v);
       }
@@ -339,8 +339,8 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs& a, unsi
       const int64_t hi = e0 + N < end ? e0 + N : end;
       for (int64_t e = lo; e < hi; ++e) {
         const E x = pad ? E(0) : src[e + delta];
-        for (int k = 0; k < a.n_dst; ++k) {
-          E* d = static_cast<E*>(const_cast<void*>(a.dst.p[k]));
+        for (int i = 0; i < a.n_dst; ++i) {
+          E* d = static_cast<E*>(const_cast<void*>(a.dst.p[i]));
           if (d) d[e] = x;
         }
       }
@@ -550,7 +550,7 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs& a,
         float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (!PAD) grad_avg4<G, RT, SHIFT>(a.g, a.R, e0 + delta, k, g);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], sc);
+        for (int j = 0; j < 4; ++j) adamw1(g[j], p[j], m[j], v[j], sc);
         Io<float>::store4(a.master + e0, true, p);
         Io<float>::store4(a.m + e0, true, m);
         Io<float>::store4(a.v + e0, true, v);
