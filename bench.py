@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--workload", default="model12_r8")
     ap.add_argument("--schedule", choices=("serial", "prefetch", "graph", "overlap"),
                     default=None,
-                    help="default overlap (serial with --gathers-per-step 2); "
+                    help="default overlap; "
                          "serial: per unit gather then fused step on one stream; prefetch: "
                          "gathers on their own stream run ahead of the fused steps, into a "
                          "double receive buffer; graph: the serial sequence replayed as one "
@@ -73,7 +73,7 @@ def parse():
                          "and exit (no GPU needed)")
     args = ap.parse_args()
     if args.schedule is None:
-        args.schedule = "overlap" if args.gathers_per_step == 1 else "serial"
+        args.schedule = "overlap"
     return args
 
 
@@ -188,9 +188,11 @@ def launches_per_step(args, units):
     n = len(units)
     if args.schedule == "overlap":
         # a unit's step shares its launch with the next gather when it has
-        # at most 4,096 work items
-        big = sum(1 for u in units[:-1] if len(u.plan.work_items(0)) > 4096)
-        return 1 + (n - 1) + big + 1
+        # at most 4,096 work items; with two gathers per step the forward
+        # gathers come first and the backward runs from the last unit
+        paired = units[:-1] if args.gathers_per_step == 1 else units[1:]
+        big = sum(1 for u in paired if len(u.plan.work_items(0)) > 4096)
+        return (args.gathers_per_step - 1) * n + 1 + (n - 1) + big + 1
     return (args.gathers_per_step + 1) * n + (1 if args.schedule == "graph" else 0)
 
 
@@ -475,7 +477,7 @@ def main():
             "gathers_per_step": args.gathers_per_step,
             "launches_per_step": launches_per_step(args, units),
             "host_calls_per_step": 2 if args.schedule == "graph"
-            else len(units) + 1 if args.schedule == "overlap"
+            else len(units) * args.gathers_per_step + 1 if args.schedule == "overlap"
             else (args.gathers_per_step + 1) * len(units),
             "buffer_copies": len(runners),
             "step": "per unit: gather+unflatten to R receivers, fused RS-avg+AdamW+recast "

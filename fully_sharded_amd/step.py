@@ -9,7 +9,10 @@ Four schedules, same results bit for bit:
             (fsdp_adamw_step_then_gather: one launch for short steps), into
             two alternating receive buffers, then step(last) -- the
             prefetch of section 07 of the zwjcode FSDP2 page without a
-            second stream
+            second stream.  With two gathers per step the forward gathers
+            run unit by unit, and the backward goes from the last unit to
+            the first: its re-gather, then step(u) together with the
+            re-gather of unit u-1, then step(0)
   graph     the serial sequence recorded once as a HIP graph (StepGraph) and
             replayed each step with one launch
   prefetch  gathers on their own stream run ahead of the steps, into two
@@ -60,8 +63,6 @@ class StepRunner:
             raise ValueError(schedule)
         if schedule in ("prefetch", "overlap") and len(receivers) < 2:
             raise ValueError(f"the {schedule} schedule needs two receive buffers")
-        if schedule == "overlap" and gathers_per_step != 1:
-            raise ValueError("the overlap schedule gathers once per step")
         if gathers_per_step not in (1, 2):
             raise ValueError("gathers_per_step is 1 or 2")
         self.units = list(units)
@@ -75,10 +76,15 @@ class StepRunner:
         self._hs = ctypes.c_void_p(self.stream.cuda_stream)
         if schedule == "overlap":
             us = self.units
-            self.pairs = [bind_adamw_step_then_gather(u.plan, hp, u.grads, u.master, u.m, u.v,
-                                                      u.param, us[i + 1].plan, us[i + 1].param,
-                                                      receivers[(i + 1) % 2])
-                          for i, u in enumerate(us[:-1])]
+            if gathers_per_step == 1:   # forward order: step u, gather u+1
+                self.pairs = [bind_adamw_step_then_gather(
+                    u.plan, hp, u.grads, u.master, u.m, u.v, u.param, us[i + 1].plan,
+                    us[i + 1].param, receivers[(i + 1) % 2]) for i, u in enumerate(us[:-1])]
+            else:                       # backward order: step u, re-gather u-1
+                self.pairs = [bind_adamw_step_then_gather(
+                    us[i].plan, hp, us[i].grads, us[i].master, us[i].m, us[i].v, us[i].param,
+                    us[i - 1].plan, us[i - 1].param, receivers[(i - 1) % 2])
+                    for i in range(len(us) - 1, 0, -1)]
         if schedule == "graph":
             self.graph = StepGraph(hp)
             for u in self.units:
@@ -103,10 +109,18 @@ class StepRunner:
             self.graph.launch(t, self._hs)
             return
         if self.schedule == "overlap":
-            self.calls[0][0](self._hs)
-            for pair in self.pairs:
-                pair(t, self._hs)
-            self.calls[-1][1](t, self._hs)
+            if self.gathers_per_step == 1:
+                self.calls[0][0](self._hs)
+                for pair in self.pairs:
+                    pair(t, self._hs)
+                self.calls[-1][1](t, self._hs)
+            else:
+                for gather, _ in self.calls:      # forward
+                    gather(self._hs)
+                self.calls[-1][0](self._hs)       # backward: last unit first
+                for pair in self.pairs:
+                    pair(t, self._hs)
+                self.calls[0][1](t, self._hs)
             return
         if self.schedule == "serial":
             for gather, fused in self.calls:

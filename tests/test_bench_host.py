@@ -89,6 +89,8 @@ def test_launches_per_step_by_schedule():
     assert bench.launches_per_step(a(schedule="graph", gathers_per_step=1), units) == 25
     # gather(0), 11 pair launches, the last step
     assert bench.launches_per_step(a(schedule="overlap", gathers_per_step=1), units) == 13
+    # 12 forward gathers, the last unit's re-gather, 11 pairs, step(0)
+    assert bench.launches_per_step(a(schedule="overlap", gathers_per_step=2), units) == 25
     # long steps keep their own launch
     mixed = [_Unit(big), _Unit(blk), _Unit(big)]
     assert bench.launches_per_step(a(schedule="overlap", gathers_per_step=1), mixed) == 1 + 2 + 1 + 1

@@ -45,14 +45,17 @@ def bits(t):
 
 
 @pytest.mark.parametrize("schedule,gathers", [("prefetch", 1), ("serial", 2), ("prefetch", 2),
-                                              ("overlap", 1)])
+                                              ("overlap", 1), ("overlap", 2)])
 def test_schedules_agree_bit_for_bit(schedule, gathers):
     print(f"[gpu] schedule={schedule} gathers={gathers}", flush=True)
     ref_units, ref_recv = build("model12_r8")
     ref = StepRunner(ref_units, ADAMW, ref_recv, "serial", 1)
     units, recv = build("model12_r8")
     run = StepRunner(units, ADAMW, recv, schedule, gathers)
+    before = None
     for t in (1, 2, 3):
+        if t == 3:   # the parameters the last step's gathers read
+            before = [u.param.clone() for u in ref_units[:2]]
         ref.step(t)
         run.step(t)
     torch.cuda.synchronize()
@@ -61,6 +64,17 @@ def test_schedules_agree_bit_for_bit(schedule, gathers):
             assert torch.equal(x, y)
     # the receive buffers hold the last gathered units, the same in both runs
     n = len(units)
+    if schedule == "overlap" and gathers == 2:
+        # the backward runs from the last unit to the first: the last
+        # re-gathers are those of units 1 and 0 (buffers 1 and 0), each
+        # taken before that unit's step
+        for b, p in enumerate(before):
+            want = [torch.empty_like(x) for x in ref_recv[0]]
+            F.fsdp_gather_unflatten(ref_units[b].plan, p, want)
+            torch.cuda.synchronize()
+            for r in range(len(want)):
+                assert torch.equal(recv[b][r].view(torch.int16), want[r].view(torch.int16))
+        return
     last = recv[(n - 1) % 2] if schedule in ("prefetch", "overlap") else recv[0]
     for r in range(len(last)):
         assert torch.equal(last[r].view(torch.int16), ref_recv[0][r].view(torch.int16))
@@ -159,7 +173,19 @@ def test_overlap_schedule_other_workloads(wl_name):
             assert torch.equal(x, y)
 
 
-def test_overlap_schedule_rejects_two_gathers():
-    units, recv = build("block512_r4")
-    with pytest.raises(ValueError):
-        StepRunner(units, ADAMW, recv, "overlap", gathers_per_step=2)
+@pytest.mark.parametrize("wl_name", ["toy_2layer_r2", "model12_flat_r8"])
+def test_overlap_schedule_with_two_gathers(wl_name):
+    """reshard_after_forward=True under the overlap schedule: forward
+    gathers, then the backward from the last unit, each step paired with the
+    re-gather of the unit before it; the same state as the serial loop."""
+    ref_units, ref_recv = build(wl_name)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial", 2)
+    units, recv = build(wl_name)
+    run = StepRunner(units, ADAMW, recv, "overlap", 2)
+    for t in (1, 2, 3):
+        ref.step(t)
+        run.step(t)
+    torch.cuda.synchronize()
+    for a, b in zip(state_of(ref_units), state_of(units)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
