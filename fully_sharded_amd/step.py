@@ -52,7 +52,8 @@ class StepRunner:
     """Runs training steps over a list of units.
 
     receivers: one list of R receiver tensors per receive buffer (at least
-    as long as the largest unit); the prefetch schedule needs two.
+    as long as the largest unit); the prefetch and overlap schedules need
+    two.
     gathers_per_step: 1 keeps the gathered parameters from forward to
     backward (reshard_after_forward=False), 2 frees them after forward and
     gathers again in backward (reshard_after_forward=True)."""
