@@ -82,7 +82,7 @@ def assert_same(x, y):
 
 
 @pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "long_two_launches",
-                                  "long_flat"])
+                                  "long_flat", "short_mixed_world"])
 def test_pair_equals_the_two_calls(case):
     print(f"[gpu] step_then_gather {case}", flush=True)
     blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
@@ -93,6 +93,8 @@ def test_pair_equals_the_two_calls(case):
     elif case == "short_fp32":        # fp32 gradients and parameters (4-byte gather)
         a = HostUnit([(37, 5), (11,)], 2, "per_param", 5, pdt="f32", gdt="f32")
         b = HostUnit([(9, 7), (3,)], 2, "per_param", 6, pdt="f32", gdt="f32")
+    elif case == "short_mixed_world":  # the two halves of one launch with different R
+        a, b = HostUnit(blk, 3, "per_param", 11), HostUnit(lin, 8, "flat", 12)
     elif case == "long_two_launches":  # > 4,096 work items: step, then gather
         a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
     else:
