@@ -173,3 +173,40 @@ def test_pair_at_extreme_world_sizes(R):
     full, _ = O.gather_unflatten(b.po, b.param)
     for r in pair[1]:
         assert_bitexact(to_host(r), full, "gather")
+
+
+@pytest.mark.parametrize("hp,t", [
+    (dict(lr=0.1, beta1=0.0, beta2=0.5, eps=1e-3, weight_decay=0.0), 1),
+    (dict(lr=3e-4, beta1=0.95, beta2=0.9999, eps=1e-12, weight_decay=0.1), 1000),
+    (dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.5), 7),
+    (dict(lr=1e-2, beta1=0.5, beta2=0.25, eps=1.0, weight_decay=1e-4), 100000),
+])
+def test_other_hyper_parameters_and_step_counters(hp, t):
+    """The step's float64 scalars (decay, bias corrections at large t) for
+    other hyper-parameters, through the stream call, the paired call and a
+    step graph: each agrees with the oracle."""
+    blk = shapes_of(BLOCK_512)
+    a, b = HostUnit(blk, 4, "per_param", 31), HostUnit(blk, 4, "per_param", 32)
+    mo, mm, vv, _ = O.shard_step(a.po, a.grads, a.master, a.m, a.v, t, hp, "bf16")
+    outs = []
+    for how in ("stream", "pair", "graph"):
+        da, db = a.device(), b.device()
+        recv = receivers(b.pl, torch.bfloat16)
+        if how == "stream":
+            F.fsdp_adamw_shard_step(a.pl, hp, t, da["grads"], da["master"], da["m"], da["v"],
+                                    da["param"])
+        elif how == "pair":
+            F.fsdp_adamw_step_then_gather(a.pl, hp, t, da["grads"], da["master"], da["m"],
+                                          da["v"], da["param"], b.pl, db["param"], recv)
+        else:
+            g = F.StepGraph(hp)
+            g.add_adamw(a.pl, da["grads"], da["master"], da["m"], da["v"], da["param"])
+            g.launch(t)
+        torch.cuda.synchronize()
+        outs.append(da)
+        assert_adamw_close(to_host(da["master"]).reshape(a.po.R, a.po.S), mo, f"master {how}")
+        assert_adamw_close(to_host(da["m"]).reshape(a.po.R, a.po.S), mm, f"m {how}")
+        assert_adamw_close(to_host(da["v"]).reshape(a.po.R, a.po.S), vv, f"v {how}")
+    for k in ("master", "m", "v", "param"):
+        assert_bitexact(to_host(outs[1][k]), to_host(outs[0][k]), f"pair vs stream {k}")
+        assert_bitexact(to_host(outs[2][k]), to_host(outs[0][k]), f"graph vs stream {k}")
