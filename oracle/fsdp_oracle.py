@@ -15,6 +15,10 @@ goes through in a training step with R ranks:
   adamw_step          AdamW on each rank's fp32 master / m / v shard
   bf16_rne            the bf16 recast of the updated master
   comm_ledger, ...    the per-rank communication and memory accounting
+  reshard             shards under one plan -> shards under another world
+                      size or layout (restoring at another world size)
+  grad_accumulate     one rank's gradient summed over micro-batches
+  allreduce_avg       DDP's averaged all-reduce (the comparator)
 
 Sources (pages, by title and section):
   [WALK]  "FSDP Training Step Walkthrough" (astro-wiki): Setup, Initial state,
@@ -23,8 +27,9 @@ Sources (pages, by title and section):
   [FSDP2] "FSDP2 parameter all-gather, gradient reduce-scatter and memory peak"
           (zwjcode): sections 01 (memory formulas), 03 (two-rank, 8-element
           hand calculation), 04 (AdamW over the shards), 06 (reshard after
-          forward), 09 (reduce-scatter = reduce then hand segment r to rank r),
-          16 (exercises).
+          forward), 08 (gradient accumulation), 09 (reduce-scatter = reduce
+          then hand segment r to rank r; all-reduce for DDP), 10 (restore at
+          another world size), 16 (exercises).
   [TINY]  "Understanding FSDP from source" (roger-lv, on Tiny-FSDP): 2.1
           intra-tensor dim-0 partition with a rounded-up shard size, 2.2
           gather (all-gather then concatenate non-empty shards along dim 0),
