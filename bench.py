@@ -188,10 +188,10 @@ def launches_per_step(args, units):
     n = len(units)
     if args.schedule == "overlap":
         # a unit's step shares its launch with the next gather when it has
-        # at most 4,096 work items; with two gathers per step the forward
+        # at most 65,536 work items; with two gathers per step the forward
         # gathers come first and the backward runs from the last unit
         paired = units[:-1] if args.gathers_per_step == 1 else units[1:]
-        big = sum(1 for u in paired if len(u.plan.work_items(0)) > 4096)
+        big = sum(1 for u in paired if len(u.plan.work_items(0)) > 65536)
         return (args.gathers_per_step - 1) * n + 1 + (n - 1) + big + 1
     return (args.gathers_per_step + 1) * n + (1 if args.schedule == "graph" else 0)
 

@@ -252,7 +252,7 @@ fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
       if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
   if ((st = attach(&a)) != FSDP_OK || (st = attach(&g)) != FSDP_OK) return st;
   if (g.n_dst == 0) return launch(a, sc, scp, sink);
-  if (a.n_work > kSmallFusedLaunch || a.n_work == 0) {
+  if (a.n_work > kPairMax || a.n_work == 0) {
     // a long step: its own launch (with its occupancy cap), then the gather
     st = launch(a, sc, scp, sink);
     return st != FSDP_OK ? st : launch(g, next->R, sink);

@@ -905,7 +905,7 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                                : pick_fused_gather<float, float>(R);
   void* args[] = {const_cast<Work**>(&fwork), &fa, &nf, const_cast<Work**>(&gwork), &ca, &wide};
   return stream.launch(fn, dim3(static_cast<unsigned>(n_fused + n_gather)), dim3(kThreads), args,
-                       0);
+                       fused_lds(n_fused));
 }
 
 }  // namespace fsdp

@@ -103,7 +103,15 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                                int lane_bytes, bool vec_g, const Sink& stream);
 
 // Fused-step work items at or below which a launch keeps full occupancy
-// (no workgroup cap), and so gains from sharing its launch with a gather.
+// (no workgroup cap).
 constexpr int64_t kSmallFusedLaunch = 4096;
+
+// Fused-step work items up to which a step shares its launch with the next
+// unit's gather (with the step's own workgroup cap).  Longer steps take the
+// tighter cap of 3 per CU, which the gather does not want, and are long
+// enough that one more launch boundary costs little.  Measured on MI355X,
+// the 12-layer model at R = 8 as 6 units of 2 blocks (6,146 items): 398.8
+// µs per step with two launches per unit, 390.0 µs paired.
+constexpr int64_t kPairMax = 65536;
 
 }  // namespace fsdp

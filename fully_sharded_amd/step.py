@@ -152,6 +152,7 @@ class StepRunner:
         and temporaries excluded."""
         shard = sum(u.plan.state_bytes_per_rank() for u in self.units)
         largest = max(u.plan.T for u in self.units) * param_bytes
-        prefetch = largest if self.schedule in ("prefetch", "overlap") else 0
+        prefetch = (largest if self.schedule in ("prefetch", "overlap") and len(self.units) > 1
+                    else 0)
         return dict(sharded_state=shard, largest_unsharded_group=largest, prefetch=prefetch,
                     peak_lower_bound=shard + largest + prefetch)

@@ -270,10 +270,10 @@ fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
  * ("FSDP2 parameter all-gather, gradient reduce-scatter and memory peak",
  * section 07; "Understanding FSDP from source", section 5, overlap of
  * communication and computation).  The results
- * equal the two calls made one after the other.  When the step is short
- * (at most 4,096 work items) both run in one kernel launch, the gather's
- * workgroups after the step's, so the gather starts while the step drains;
- * longer steps take two launches.
+ * equal the two calls made one after the other.  When the step has at most
+ * 65,536 work items (fsdp_plan_work_items, space 0) both run in one kernel
+ * launch, the gather's workgroups after the step's, so the gather starts
+ * while the step drains; longer steps take two launches.
  *   Arguments as in the two calls; in addition the two must not touch each
  *   other's outputs: full_out must be disjoint from the gradients, master,
  *   m, v and param_out, and param_out, master, m, v from next_shards (else

@@ -80,8 +80,8 @@ class _Unit:
 
 def test_launches_per_step_by_schedule():
     blk = F.Plan(shapes_of(BLOCK_512), 8, "per_param")          # 3,073 work items
-    big = F.Plan(shapes_of(BLOCK_512) * 2, 8, "per_param")      # > 4,096 work items
-    assert len(blk.work_items(0)) <= 4096 < len(big.work_items(0))
+    big = F.Plan([(65537 * 1024,)], 8, "flat")                  # > 65,536 work items
+    assert len(blk.work_items(0)) <= 65536 < len(big.work_items(0))
     units = [_Unit(blk)] * 12
     a = argparse.Namespace
     assert bench.launches_per_step(a(schedule="serial", gathers_per_step=1), units) == 24

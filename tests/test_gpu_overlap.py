@@ -1,7 +1,8 @@
 """fsdp_adamw_step_then_gather: the fused AdamW step of one unit enqueued
-together with the all-gather of the next unit (FSDP's prefetch).  Short steps
-share one launch with the gather, long ones take two; both give the bits of
-the two separate calls, and the oracle's results."""
+together with the all-gather of the next unit (FSDP's prefetch).  Steps of
+up to 65,536 work items share one launch with the gather, longer ones take
+two; both give the bits of the two separate calls, and the oracle's
+results."""
 
 import numpy as np
 import pytest
@@ -81,8 +82,8 @@ def assert_same(x, y):
         assert_bitexact(to_host(p), to_host(q), f"receiver {r}")
 
 
-@pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "long_two_launches",
-                                  "long_flat", "short_mixed_world"])
+@pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "capped_pair",
+                                  "capped_pair_flat", "short_mixed_world"])
 def test_pair_equals_the_two_calls(case):
     print(f"[gpu] step_then_gather {case}", flush=True)
     blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
@@ -95,7 +96,7 @@ def test_pair_equals_the_two_calls(case):
         b = HostUnit([(9, 7), (3,)], 2, "per_param", 6, pdt="f32", gdt="f32")
     elif case == "short_mixed_world":  # the two halves of one launch with different R
         a, b = HostUnit(blk, 3, "per_param", 11), HostUnit(lin, 8, "flat", 12)
-    elif case == "long_two_launches":  # > 4,096 work items: step, then gather
+    elif case == "capped_pair":       # > 4,096 work items: one launch, 4 per CU
         a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
     else:
         a, b = HostUnit(blk * 2, 8, "flat", 9), HostUnit(lin * 2, 8, "flat", 10)
@@ -210,3 +211,36 @@ def test_other_hyper_parameters_and_step_counters(hp, t):
     for k in ("master", "m", "v", "param"):
         assert_bitexact(to_host(outs[1][k]), to_host(outs[0][k]), f"pair vs stream {k}")
         assert_bitexact(to_host(outs[2][k]), to_host(outs[0][k]), f"graph vs stream {k}")
+
+
+def test_pair_long_steps_take_two_launches():
+    """A step of more than 65,536 work items (70M elements at R = 8) runs
+    in its own launch, then the gather: the same bits as the two calls."""
+    R, T = 8, 70_000_000
+    pa = F.Plan([(T,)], R, "flat")
+    pb = F.Plan(shapes_of(BLOCK_512), R, "per_param")
+    assert len(pa.work_items(0)) > 65536
+    gen_ = torch.Generator(device=DEV).manual_seed(70)
+    grads = [(torch.randn(T, device=DEV, generator=gen_) * 1e-2).to(torch.bfloat16)
+             for _ in range(R)]
+    master0 = torch.rand(R * pa.S, device=DEV, generator=gen_) - 0.5
+    nparam = (torch.rand(R * pb.S, device=DEV, generator=gen_) - 0.5).to(torch.bfloat16)
+    out = []
+    for combined in (True, False):
+        master, m, v = master0.clone(), torch.zeros_like(master0), torch.zeros_like(master0)
+        param = master0.to(torch.bfloat16)
+        recv = receivers(pb, torch.bfloat16)
+        for t in (1, 2):
+            if combined:
+                F.fsdp_adamw_step_then_gather(pa, ADAMW, t, grads, master, m, v, param, pb,
+                                              nparam, recv)
+            else:
+                F.fsdp_adamw_shard_step(pa, ADAMW, t, grads, master, m, v, param)
+                F.fsdp_gather_unflatten(pb, nparam, recv)
+        torch.cuda.synchronize()
+        out.append((master, m, v, param, recv))
+    for x, y in zip(out[0][:4], out[1][:4]):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+    for p_, q_ in zip(out[0][4], out[1][4]):
+        assert torch.equal(p_.view(torch.int16), q_.view(torch.int16))

@@ -97,12 +97,20 @@ WORKLOADS = {
         grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3,
         master_init="fan_in"),
     # the same 12-layer model wrapped at other granularities (the FSDP unit
-    # decides what one all-gather covers): the whole model as one unit, and
-    # one unit per parameter
+    # decides what one all-gather covers): the whole model as one unit, two
+    # or four blocks per unit, and one unit per parameter
     "model12_whole_r8": dict(
         cid=8, units=[[(f"l{i}.{n}", s) for i in range(12) for n, s in BLOCK_512]], R=8,
         layout=PER_PARAM, grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3,
         master_init="fan_in"),
+    "model12_pair_r8": dict(
+        cid=10, units=[[(f"l{2 * i + j}.{n}", sh) for j in range(2) for n, sh in BLOCK_512]
+                       for i in range(6)], R=8, layout=PER_PARAM, grad_dtype="bf16",
+        param_dtype="bf16", grad_sigma=1e-3, steps=3, master_init="fan_in"),
+    "model12_quad_r8": dict(
+        cid=11, units=[[(f"l{4 * i + j}.{n}", sh) for j in range(4) for n, sh in BLOCK_512]
+                       for i in range(3)], R=8, layout=PER_PARAM, grad_dtype="bf16",
+        param_dtype="bf16", grad_sigma=1e-3, steps=3, master_init="fan_in"),
     "model12_perparam_r8": dict(
         cid=9, units=[[p] for _ in range(12) for p in BLOCK_512], R=8, layout=PER_PARAM,
         grad_dtype="bf16", param_dtype="bf16", grad_sigma=1e-3, steps=3, master_init="fan_in"),
