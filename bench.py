@@ -39,14 +39,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="model12_r8")
-    ap.add_argument("--schedule", choices=("serial", "prefetch", "graph", "overlap"),
+    ap.add_argument("--schedule", choices=("serial", "prefetch", "graph", "overlap",
+                                           "graph-overlap"),
                     default=None,
                     help="default overlap; "
                          "serial: per unit gather then fused step on one stream; prefetch: "
                          "gathers on their own stream run ahead of the fused steps, into a "
                          "double receive buffer; graph: the serial sequence replayed as one "
                          "HIP graph per step; overlap: each unit's fused step shares its "
-                         "launch with the next unit's gather (double receive buffer)")
+                         "launch with the next unit's gather (double receive buffer); "
+                         "graph-overlap: the overlap sequence replayed as one HIP graph")
     ap.add_argument("--cycle-gib", type=float, default=4.0,
                     help="give the workload enough independent copies of its buffers that "
                          "one round of steps touches at least this many GiB (the 256 MB "
@@ -186,13 +188,14 @@ def launches_per_step(args, units):
     """Kernel launches of one step (the graph schedule adds its one-lane
     scalar kernel)."""
     n = len(units)
-    if args.schedule == "overlap":
+    if args.schedule in ("overlap", "graph-overlap"):
         # a unit's step shares its launch with the next gather when it has
         # at most 65,536 work items; with two gathers per step the forward
         # gathers come first and the backward runs from the last unit
         paired = units[:-1] if args.gathers_per_step == 1 else units[1:]
         big = sum(1 for u in paired if len(u.plan.work_items(0)) > 65536)
-        return (args.gathers_per_step - 1) * n + 1 + (n - 1) + big + 1
+        return ((args.gathers_per_step - 1) * n + 1 + (n - 1) + big + 1
+                + (1 if args.schedule == "graph-overlap" else 0))
     return (args.gathers_per_step + 1) * n + (1 if args.schedule == "graph" else 0)
 
 
@@ -273,7 +276,7 @@ def main():
     n_copies = 1 if ws >= cycle else min(32, -(-cycle // ws))
     copies = [units] + [setup_units(wl, dev)[1] for _ in range(n_copies - 1)]
     T_max = max(p.T for p in plans.values())
-    n_recv = 2 if args.schedule in ("prefetch", "overlap") else 1
+    n_recv = 2 if args.schedule in ("prefetch", "overlap", "graph-overlap") else 1
     runners = []
     for cu in copies:
         recv = [rows(R, T_max, pdt, dev) for _ in range(n_recv)]
@@ -339,7 +342,7 @@ def main():
     fused_avg_ms = timed(fused_pass)
     gather_avg_ms = timed(gather_pass)
     pair_avg_ms = None
-    if args.schedule == "overlap" and len(units) > 1:
+    if args.schedule in ("overlap", "graph-overlap") and len(units) > 1:
         pp = [0]
 
         def pair_pass():
@@ -476,7 +479,7 @@ def main():
             "schedule": args.schedule,
             "gathers_per_step": args.gathers_per_step,
             "launches_per_step": launches_per_step(args, units),
-            "host_calls_per_step": 2 if args.schedule == "graph"
+            "host_calls_per_step": 2 if args.schedule in ("graph", "graph-overlap")
             else len(units) * args.gathers_per_step + 1 if args.schedule == "overlap"
             else (args.gathers_per_step + 1) * len(units),
             "buffer_copies": len(runners),

@@ -108,6 +108,13 @@ _SIGS = {
                                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_int32]),
+    "fsdp_step_graph_add_adamw_gather": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                                        ctypes.POINTER(ctypes.c_void_p),
+                                                        ctypes.c_int32, ctypes.c_void_p,
+                                                        ctypes.c_void_p, ctypes.c_void_p,
+                                                        ctypes.c_void_p, ctypes.c_int32,
+                                                        ctypes.c_void_p, ctypes.c_void_p,
+                                                        ctypes.POINTER(ctypes.c_void_p)]),
     "fsdp_step_graph_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
                                             ctypes.POINTER(ctypes.c_int64)]),
     "fsdp_step_graph_launch": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
@@ -657,8 +664,27 @@ class StepGraph:
                    _dtype_code(param_out)))
         self._keep.append((plan, list(grads), master, m, v, param_out))
 
+    def add_adamw_gather(self, plan: Plan, grads, master, m, v, param_out, next_plan: Plan,
+                         next_shards, full_out):
+        """Record fsdp_adamw_step_then_gather: this unit's fused step with the
+        next unit's gather."""
+        dt = _check_step_args(plan, grads, master, m, v, param_out)
+        _check_gather_args(next_plan, next_shards, full_out)
+        if next_shards.dtype != param_out.dtype:
+            raise ValueError("the next unit's shards must have the parameter dtype")
+        _check("fsdp_step_graph_add_adamw_gather",
+               lib().fsdp_step_graph_add_adamw_gather(
+                   self._handle, plan.handle, _ptr_array(grads, "grads"), dt,
+                   ctypes.c_void_p(_dev(master, "master")), ctypes.c_void_p(_dev(m, "m")),
+                   ctypes.c_void_p(_dev(v, "v")), ctypes.c_void_p(_dev(param_out, "param_out")),
+                   _dtype_code(param_out), next_plan.handle,
+                   ctypes.c_void_p(_dev(next_shards, "next_shards")),
+                   _ptr_array(full_out, "full_out")))
+        self._keep.append((plan, list(grads), master, m, v, param_out, next_plan, next_shards,
+                           list(full_out)))
+
     def info(self):
-        """(kernel nodes, AdamW nodes) recorded so far."""
+        """(kernel nodes, AdamW steps) recorded so far."""
         a, b = ctypes.c_int64(), ctypes.c_int64()
         _check("fsdp_step_graph_info",
                lib().fsdp_step_graph_info(self._handle, ctypes.byref(a), ctypes.byref(b)))

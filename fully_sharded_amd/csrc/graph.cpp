@@ -124,6 +124,22 @@ fsdp_status fsdp_step_graph_add_adamw(fsdp_step_graph* g, const fsdp_plan* plan,
   return r;
 }
 
+fsdp_status fsdp_step_graph_add_adamw_gather(fsdp_step_graph* g, const fsdp_plan* plan,
+                                             const void* const* grads, int32_t grad_dtype,
+                                             float* master, float* m, float* v, void* param_out,
+                                             int32_t param_dtype, const fsdp_plan* next,
+                                             const void* next_shards, void* const* full_out) {
+  const fsdp_status st = check_open(g);
+  if (st != FSDP_OK) return st;
+  const int64_t before = g->n_nodes;
+  const fsdp::AdamScalars unused{};
+  const fsdp_status r = fsdp::adamw_gather_impl(plan, unused, g->scalars, grads, grad_dtype,
+                                                master, m, v, param_out, param_dtype, next,
+                                                next_shards, full_out, GraphSink(g));
+  if (r == FSDP_OK && g->n_nodes > before) ++g->n_adamw;
+  return r;
+}
+
 fsdp_status fsdp_step_graph_info(const fsdp_step_graph* g, int64_t* n_nodes, int64_t* n_adamw) {
   if (!g || !n_nodes || !n_adamw) return FSDP_ERR_INVALID_ARG;
   *n_nodes = g->n_nodes;

@@ -3,7 +3,7 @@
 AdamW + recast of its gradients ("FSDP Training Step Walkthrough", steps 1-6;
 zwjcode FSDP2 page, section 05: one communication group per block).
 
-Four schedules, same results bit for bit:
+Five schedules, same results bit for bit:
   serial    one stream: gather(u), step(u), gather(u+1), ...
   overlap   one stream: gather(0), then step(u) together with gather(u+1)
             (fsdp_adamw_step_then_gather: one launch for short steps), into
@@ -15,6 +15,8 @@ Four schedules, same results bit for bit:
             re-gather of unit u-1, then step(0)
   graph     the serial sequence recorded once as a HIP graph (StepGraph) and
             replayed each step with one launch
+  graph-overlap  the overlap sequence (one gather per step) recorded as a
+            HIP graph the same way
   prefetch  gathers on their own stream run ahead of the steps, into two
             alternating receive buffers (zwjcode FSDP2 page, section 07:
             all-gather block k+1 while block k computes, at the price of a
@@ -60,22 +62,24 @@ class StepRunner:
 
     def __init__(self, units, hp: dict, receivers, schedule: str = "serial",
                  gathers_per_step: int = 1):
-        if schedule not in ("serial", "prefetch", "graph", "overlap"):
+        if schedule not in ("serial", "prefetch", "graph", "overlap", "graph-overlap"):
             raise ValueError(schedule)
-        if schedule in ("prefetch", "overlap") and len(receivers) < 2:
+        if schedule == "graph-overlap" and gathers_per_step != 1:
+            raise ValueError("the graph-overlap schedule gathers once per step")
+        if schedule in ("prefetch", "overlap", "graph-overlap") and len(receivers) < 2:
             raise ValueError(f"the {schedule} schedule needs two receive buffers")
         if gathers_per_step not in (1, 2):
             raise ValueError("gathers_per_step is 1 or 2")
         self.units = list(units)
         self.schedule = schedule
         self.gathers_per_step = gathers_per_step
-        nb = 2 if schedule in ("prefetch", "overlap") else 1
+        nb = 2 if schedule in ("prefetch", "overlap", "graph-overlap") else 1
         self.calls = [(bind_gather_unflatten(u.plan, u.param, receivers[i % nb]),
                        bind_adamw_shard_step(u.plan, hp, u.grads, u.master, u.m, u.v, u.param))
                       for i, u in enumerate(self.units)]
         self.stream = torch.cuda.current_stream()
         self._hs = ctypes.c_void_p(self.stream.cuda_stream)
-        if schedule == "overlap":
+        if schedule in ("overlap", "graph-overlap"):
             us = self.units
             if gathers_per_step == 1:   # forward order: step u, gather u+1
                 self.pairs = [bind_adamw_step_then_gather(
@@ -92,6 +96,16 @@ class StepRunner:
                 for _ in range(gathers_per_step):
                     self.graph.add_gather(u.plan, u.param, receivers[0])
                 self.graph.add_adamw(u.plan, u.grads, u.master, u.m, u.v, u.param)
+        if schedule == "graph-overlap":
+            us = self.units
+            self.graph = StepGraph(hp)
+            self.graph.add_gather(us[0].plan, us[0].param, receivers[0])
+            for i, u in enumerate(us[:-1]):
+                self.graph.add_adamw_gather(u.plan, u.grads, u.master, u.m, u.v, u.param,
+                                            us[i + 1].plan, us[i + 1].param,
+                                            receivers[(i + 1) % 2])
+            last = us[-1]
+            self.graph.add_adamw(last.plan, last.grads, last.master, last.m, last.v, last.param)
         if schedule == "prefetch":
             self.s_gather = torch.cuda.Stream()   # default priority
             self.s_step = torch.cuda.Stream()
@@ -106,7 +120,7 @@ class StepRunner:
         """One training step with AdamW step counter t (>= 1), enqueued on
         the current stream (the prefetch schedule joins its streams back to
         it before returning)."""
-        if self.schedule == "graph":
+        if self.schedule in ("graph", "graph-overlap"):
             self.graph.launch(t, self._hs)
             return
         if self.schedule == "overlap":
@@ -152,7 +166,7 @@ class StepRunner:
         and temporaries excluded."""
         shard = sum(u.plan.state_bytes_per_rank() for u in self.units)
         largest = max(u.plan.T for u in self.units) * param_bytes
-        prefetch = (largest if self.schedule in ("prefetch", "overlap") and len(self.units) > 1
-                    else 0)
+        prefetch = (largest if self.schedule in ("prefetch", "overlap", "graph-overlap")
+                    and len(self.units) > 1 else 0)
         return dict(sharded_state=shard, largest_unsharded_group=largest, prefetch=prefetch,
                     peak_lower_bound=shard + largest + prefetch)

@@ -330,7 +330,16 @@ fsdp_status fsdp_step_graph_add_adamw(fsdp_step_graph* graph, const fsdp_plan* p
                                       int32_t grads_are_replicas, float* master, float* m,
                                       float* v, void* param_out, int32_t param_dtype);
 
-/* Kernel nodes recorded so far, and how many of them are AdamW steps. */
+/* Appends what fsdp_adamw_step_then_gather would enqueue with these
+ * arguments (same checks, same errors): one kernel node holding the step
+ * and the next unit's gather, or two nodes for a long step. */
+fsdp_status fsdp_step_graph_add_adamw_gather(fsdp_step_graph* graph, const fsdp_plan* plan,
+                                             const void* const* grads, int32_t grad_dtype,
+                                             float* master, float* m, float* v, void* param_out,
+                                             int32_t param_dtype, const fsdp_plan* next,
+                                             const void* next_shards, void* const* full_out);
+
+/* Kernel nodes recorded so far, and how many AdamW steps they hold. */
 fsdp_status fsdp_step_graph_info(const fsdp_step_graph* graph, int64_t* n_nodes,
                                  int64_t* n_adamw);
 

@@ -189,3 +189,29 @@ def test_overlap_schedule_with_two_gathers(wl_name):
     for a, b in zip(state_of(ref_units), state_of(units)):
         for x, y in zip(a, b):
             assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("wl_name", ["model12_r8", "toy_2layer_r2", "model12_pair_r8"])
+def test_graph_overlap_replays_match_the_overlap_calls(wl_name):
+    """The overlap sequence recorded as a step graph (paired nodes): every
+    replay, with eager work and a synchronisation between replays, leaves
+    the same bits as the stream calls of the overlap schedule."""
+    print(f"[gpu] graph-overlap {wl_name}", flush=True)
+    ref_units, ref_recv = build(wl_name)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "overlap")
+    units, recv = build(wl_name)
+    run = StepRunner(units, ADAMW, recv, "graph-overlap")
+    n_nodes, n_adamw = run.graph.info()
+    assert n_adamw == len(units)
+    scratch = torch.randn(1 << 20, device=DEV)
+    for t in (1, 2, 3):
+        run.step(t)
+        scratch.mul_(0.999).add_(1.0)
+        ref.step(t)
+        torch.cuda.synchronize()
+        for a, b in zip(state_of(ref_units), state_of(units)):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), f"step {t}"
+        for k in range(2):
+            for r in range(len(recv[k])):
+                assert torch.equal(bits(recv[k][r]), bits(ref_recv[k][r])), f"step {t}"
