@@ -308,6 +308,10 @@ def test_step_graph_checks_arguments_without_a_device():
     assert L.fsdp_step_graph_launch(None, 1, None) == -1
     pa = F.Plan([(8,)], 2, "flat")
     assert L.fsdp_step_graph_add_gather(None, pa.handle, _fake(1), 1, _parr([_fake(2), _fake(3)])) == -1
+    assert L.fsdp_step_graph_add_adamw_gather(None, pa.handle, _parr([_fake(4), _fake(5)]), 1,
+                                              _fake(6), _fake(7), _fake(8), _fake(9), 1,
+                                              pa.handle, _fake(10),
+                                              _parr([_fake(11), _fake(12)])) == -1
 
 
 def test_reshard_batch_checks_arguments_before_any_device_call():
