@@ -172,6 +172,29 @@ def test_allreduce_avg_bit_exact(R, gdt, odt):
         assert_bitexact(to_host(out[r]), w, f"allreduce rank {r}")
 
 
+@pytest.mark.parametrize("R,layout", [(2, "flat"), (3, "per_param"), (8, "per_param"),
+                                      (13, "flat")])
+def test_allreduce_is_reduce_scatter_then_gather(R, layout):
+    """The all-reduce equals the reduce-scatter-average followed by the
+    all-gather of the averaged fp32 shards ([FSDP2] 09), with the library's
+    own calls on both sides: bit for bit."""
+    rng = np.random.default_rng(100 + R)
+    shapes = [(41, 7), (300,), (2, 3, 11)]
+    pg = F.Plan(shapes, R, layout)
+    T, S = pg.T, pg.S
+    grads = [to_dev(O.bf16_rne((rng.standard_normal(T) * 1e-2).astype(np.float32)))
+             for _ in range(R)]
+    ar = [torch.empty(T, device=DEV) for _ in range(R)]
+    F.fsdp_allreduce_avg(pg, grads, ar)
+    rs = torch.empty(R * S, device=DEV)
+    F.fsdp_reduce_scatter_avg(pg, grads, rs)
+    full = [torch.empty(T, device=DEV) for _ in range(R)]
+    F.fsdp_gather_unflatten(pg, rs, full)
+    torch.cuda.synchronize()
+    for r in range(R):
+        assert torch.equal(ar[r].view(torch.int32), full[r].view(torch.int32)), r
+
+
 def test_new_ops_reject_bad_arguments_before_launch():
     pg = F.Plan([(16, 4)], 2, "flat")
     other = F.Plan([(16, 4)], 4, "per_param")
