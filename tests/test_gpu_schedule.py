@@ -3,6 +3,8 @@ schedule (gathers on their own stream, double receive buffer), two gathers
 per step, and the step graph (the serial sequence replayed as one HIP graph)
 change ordering, traffic or launch count, not results."""
 
+import ctypes
+
 import pytest
 import torch
 
@@ -215,3 +217,28 @@ def test_graph_overlap_replays_match_the_overlap_calls(wl_name):
         for k in range(2):
             for r in range(len(recv[k])):
                 assert torch.equal(bits(recv[k][r]), bits(ref_recv[k][r])), f"step {t}"
+
+
+def test_units_sharing_a_plan_on_two_streams():
+    """Operations with the same plan on two streams at once (the plan's work
+    tables are shared): each unit ends bit-identical to the serial run."""
+    ref_units, ref_recv = build("model12_r8", n_units=4)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial")
+    units, recv = build("model12_r8", n_units=4)
+    assert units[0].plan is units[3].plan
+    other = [[torch.empty_like(x) for x in recv[0]] for _ in range(2)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        a = StepRunner(units[:2], ADAMW, recv, "overlap")
+    with torch.cuda.stream(s2):
+        b = StepRunner(units[2:], ADAMW, other, "serial")
+    assert a.stream == s1 and b.stream == s2
+    for t in (1, 2, 3):
+        ref.step(t)
+        a.step(t)
+        b.step(t)
+    torch.cuda.synchronize()
+    for x, y in zip(state_of(ref_units), state_of(units)):
+        for p, q in zip(x, y):
+            assert torch.equal(p, q)
