@@ -252,7 +252,10 @@ fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
       if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
   if ((st = attach(&a)) != FSDP_OK || (st = attach(&g)) != FSDP_OK) return st;
   if (g.n_dst == 0) return launch(a, sc, scp, sink);
-  if (a.n_work > kPairMax || a.n_work == 0) {
+  // one launch when the step is short enough and the step's pointer slots
+  // also hold the gather's receivers
+  const bool slots_fit = plan->R > kSmallPtrs || next->R <= kSmallPtrs;
+  if (a.n_work > kPairMax || a.n_work == 0 || !slots_fit) {
     // a long step: its own launch (with its occupancy cap), then the gather
     st = launch(a, sc, scp, sink);
     return st != FSDP_OK ? st : launch(g, next->R, sink);

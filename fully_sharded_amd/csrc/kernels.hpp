@@ -102,6 +102,10 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                                const void* shards, const PtrArray& dst, int n_dst,
                                int lane_bytes, bool vec_g, const Sink& stream);
 
+// Pointer-array slots of the kernels specialised for R <= 8 (a paired launch
+// with such a step carries the gather's receivers in the same 8 slots).
+constexpr int kSmallPtrs = 8;
+
 // Fused-step work items at or below which a launch keeps full occupancy
 // (no workgroup cap).
 constexpr int64_t kSmallFusedLaunch = 4096;

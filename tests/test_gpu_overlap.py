@@ -83,7 +83,8 @@ def assert_same(x, y):
 
 
 @pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "capped_pair",
-                                  "capped_pair_flat", "short_mixed_world"])
+                                  "capped_pair_flat", "short_mixed_world", "mixed_world_wide",
+                                  "wide_world"])
 def test_pair_equals_the_two_calls(case):
     print(f"[gpu] step_then_gather {case}", flush=True)
     blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
@@ -96,9 +97,13 @@ def test_pair_equals_the_two_calls(case):
         b = HostUnit([(9, 7), (3,)], 2, "per_param", 6, pdt="f32", gdt="f32")
     elif case == "short_mixed_world":  # the two halves of one launch with different R
         a, b = HostUnit(blk, 3, "per_param", 11), HostUnit(lin, 8, "flat", 12)
+    elif case == "mixed_world_wide":  # R <= 8 step, R > 8 gather: two launches
+        a, b = HostUnit(blk, 4, "per_param", 13), HostUnit(lin, 16, "flat", 14)
+    elif case == "wide_world":        # R > 8 on both halves: one launch, 64 slots
+        a, b = HostUnit([(300, 40), (50,)], 12, "per_param", 15), HostUnit(lin, 9, "flat", 16)
     elif case == "capped_pair":       # > 4,096 work items: one launch, 4 per CU
         a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
-    else:
+    else:                             # capped_pair_flat
         a, b = HostUnit(blk * 2, 8, "flat", 9), HostUnit(lin * 2, 8, "flat", 10)
     pair, sep = run_both(a, b)
     assert_same(pair, sep)
