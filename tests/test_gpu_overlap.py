@@ -84,7 +84,7 @@ def assert_same(x, y):
 
 @pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "capped_pair",
                                   "capped_pair_flat", "short_mixed_world", "mixed_world_wide",
-                                  "wide_world"])
+                                  "wide_world", "f32_grads_bf16_params"])
 def test_pair_equals_the_two_calls(case):
     print(f"[gpu] step_then_gather {case}", flush=True)
     blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
@@ -101,6 +101,9 @@ def test_pair_equals_the_two_calls(case):
         a, b = HostUnit(blk, 4, "per_param", 13), HostUnit(lin, 16, "flat", 14)
     elif case == "wide_world":        # R > 8 on both halves: one launch, 64 slots
         a, b = HostUnit([(300, 40), (50,)], 12, "per_param", 15), HostUnit(lin, 9, "flat", 16)
+    elif case == "f32_grads_bf16_params":  # e.g. accumulated fp32 gradients
+        a = HostUnit(blk, 8, "per_param", 17, pdt="bf16", gdt="f32")
+        b = HostUnit(blk, 8, "per_param", 18)
     elif case == "capped_pair":       # > 4,096 work items: one launch, 4 per CU
         a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
     else:                             # capped_pair_flat
