@@ -61,7 +61,6 @@ bf16 values are held as their uint16 bit patterns.
 
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass, field
 
 import numpy as np
