@@ -3,8 +3,6 @@ schedule (gathers on their own stream, double receive buffer), two gathers
 per step, and the step graph (the serial sequence replayed as one HIP graph)
 change ordering, traffic or launch count, not results."""
 
-import ctypes
-
 import pytest
 import torch
 
