@@ -252,10 +252,10 @@ fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
       if (overlap(w, x)) return FSDP_ERR_INVALID_ARG;
   if ((st = attach(&a)) != FSDP_OK || (st = attach(&g)) != FSDP_OK) return st;
   if (g.n_dst == 0) return launch(a, sc, scp, sink);
-  // one launch when the step is short enough and the step's pointer slots
-  // also hold the gather's receivers
+  // one launch when the step is short enough, the step's pointer slots also
+  // hold the gather's receivers and the two fit in one grid
   const bool slots_fit = plan->R > kSmallPtrs || next->R <= kSmallPtrs;
-  if (a.n_work > kPairMax || a.n_work == 0 || !slots_fit) {
+  if (a.n_work > kPairMax || a.n_work == 0 || !slots_fit || a.n_work + g.n_work > kMaxItems) {
     // a long step: its own launch (with its occupancy cap), then the gather
     st = launch(a, sc, scp, sink);
     return st != FSDP_OK ? st : launch(g, next->R, sink);
@@ -398,74 +398,85 @@ fsdp_status fsdp_plan_work_items(const fsdp_plan* plan, int32_t space, int64_t* 
 }
 
 fsdp_status fsdp_plan_prepare(const fsdp_plan* plan, void* stream) {
-  (void)stream;
-  if (!plan) return FSDP_ERR_INVALID_ARG;
-  const Work* w = nullptr;
-  const fsdp_status st = plan->shard_work.device(&w);
-  return st != FSDP_OK ? st : plan->flat_work.device(&w);
+  return fsdp::guarded([&]() -> fsdp_status {
+    (void)stream;
+    if (!plan) return FSDP_ERR_INVALID_ARG;
+    const Work* w = nullptr;
+    const fsdp_status st = plan->shard_work.device(&w);
+    return st != FSDP_OK ? st : plan->flat_work.device(&w);
+  });
 }
 
 fsdp_status fsdp_shard_pack(const fsdp_plan* plan, const void* full, int32_t full_dtype,
                             void* shards, int32_t shard_dtype, void* stream) {
-  if (!plan || !full || !shards) return FSDP_ERR_INVALID_ARG;
-  if (!valid_dtype(full_dtype) || !valid_dtype(shard_dtype)) return FSDP_ERR_INVALID_ARG;
-  if (!aligned(full, dtype_size(full_dtype)) || !aligned(shards, dtype_size(shard_dtype)))
-    return FSDP_ERR_INVALID_ARG;
-  if (overlap(range_of(full, plan->T * dtype_size(full_dtype)),
-              range_of(shards, plan->R * plan->S * dtype_size(shard_dtype))))
-    return FSDP_ERR_INVALID_ARG;
-  const Work* w = nullptr;
-  const fsdp_status st = plan->shard_work.device(&w);
-  if (st != FSDP_OK) return st;
-  const bool vec = aligned(full, 16) && aligned(shards, 16);
-  const auto n_work = static_cast<int64_t>(plan->shard_work.host.size());
-  const fsdp::StreamSink s(stream);
-  if (full_dtype == shard_dtype) {
-    PtrArray dst{};
-    dst.p[0] = shards;
-    return from_hip(fsdp::launch_copy(w, n_work, full, dst, 1,
-                                      static_cast<int>(dtype_size(full_dtype)), 16, vec, s));
-  }
-  return from_hip(fsdp::launch_pack_cast(w, n_work, full, full_dtype, shards, shard_dtype, vec, s));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !full || !shards) return FSDP_ERR_INVALID_ARG;
+    if (!valid_dtype(full_dtype) || !valid_dtype(shard_dtype)) return FSDP_ERR_INVALID_ARG;
+    if (!aligned(full, dtype_size(full_dtype)) || !aligned(shards, dtype_size(shard_dtype)))
+      return FSDP_ERR_INVALID_ARG;
+    if (overlap(range_of(full, plan->T * dtype_size(full_dtype)),
+                range_of(shards, plan->R * plan->S * dtype_size(shard_dtype))))
+      return FSDP_ERR_INVALID_ARG;
+    const Work* w = nullptr;
+    const fsdp_status st = plan->shard_work.device(&w);
+    if (st != FSDP_OK) return st;
+    const bool vec = aligned(full, 16) && aligned(shards, 16);
+    const auto n_work = static_cast<int64_t>(plan->shard_work.host.size());
+    const fsdp::StreamSink s(stream);
+    if (full_dtype == shard_dtype) {
+      PtrArray dst{};
+      dst.p[0] = shards;
+      return from_hip(fsdp::launch_copy(w, n_work, full, dst, 1,
+                                        static_cast<int>(dtype_size(full_dtype)), 16, vec, s));
+    }
+    return from_hip(
+        fsdp::launch_pack_cast(w, n_work, full, full_dtype, shards, shard_dtype, vec, s));
+  });
 }
 
 fsdp_status fsdp_gather_unflatten(const fsdp_plan* plan, const void* shards, int32_t dtype,
                                   void* const* full_out, void* stream) {
-  return fsdp::gather_impl(plan, shards, dtype, full_out, fsdp::StreamSink(stream));
+  return fsdp::guarded([&]() -> fsdp_status {
+    return fsdp::gather_impl(plan, shards, dtype, full_out, fsdp::StreamSink(stream));
+  });
 }
 
 fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* grads,
                                     int32_t grad_dtype, float* out, void* stream) {
-  if (!plan || !grads || !out || !valid_dtype(grad_dtype)) return FSDP_ERR_INVALID_ARG;
-  const int64_t es = dtype_size(grad_dtype);
-  if (!aligned(out, 4)) return FSDP_ERR_INVALID_ARG;
-  const Range out_r = range_of(out, plan->R * plan->S * 4);
-  PtrArray g{};
-  bool vec = aligned(out, 16);
-  for (int q = 0; q < plan->R; ++q) {
-    if (!grads[q] || !aligned(grads[q], es)) return FSDP_ERR_INVALID_ARG;
-    if (overlap(out_r, range_of(grads[q], plan->T * es))) return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(grads[q], 16);
-    g.p[q] = grads[q];
-  }
-  const Work* w = nullptr;
-  const fsdp_status st = plan->shard_work.device(&w);
-  if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_rs_avg(w, static_cast<int64_t>(plan->shard_work.host.size()), g,
-                                      plan->R, grad_dtype, out, vec,
-                                      fsdp::StreamSink(stream)));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !grads || !out || !valid_dtype(grad_dtype)) return FSDP_ERR_INVALID_ARG;
+    const int64_t es = dtype_size(grad_dtype);
+    if (!aligned(out, 4)) return FSDP_ERR_INVALID_ARG;
+    const Range out_r = range_of(out, plan->R * plan->S * 4);
+    PtrArray g{};
+    bool vec = aligned(out, 16);
+    for (int q = 0; q < plan->R; ++q) {
+      if (!grads[q] || !aligned(grads[q], es)) return FSDP_ERR_INVALID_ARG;
+      if (overlap(out_r, range_of(grads[q], plan->T * es))) return FSDP_ERR_INVALID_ARG;
+      vec = vec && aligned(grads[q], 16);
+      g.p[q] = grads[q];
+    }
+    const Work* w = nullptr;
+    const fsdp_status st = plan->shard_work.device(&w);
+    if (st != FSDP_OK) return st;
+    return from_hip(fsdp::launch_rs_avg(w, static_cast<int64_t>(plan->shard_work.host.size()), g,
+                                        plan->R, grad_dtype, out, vec,
+                                        fsdp::StreamSink(stream)));
+  });
 }
 
 fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
                                   int64_t step, const void* const* grads, int32_t grad_dtype,
                                   int32_t grads_are_replicas, float* master, float* m, float* v,
                                   void* param_out, int32_t param_dtype, void* stream) {
-  if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
-  AdamScalars sc;
-  const fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
-  if (st != FSDP_OK) return st;
-  return fsdp::adamw_impl(plan, sc, nullptr, grads, grad_dtype, grads_are_replicas, master, m, v,
-                          param_out, param_dtype, fsdp::StreamSink(stream));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
+    AdamScalars sc;
+    const fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
+    if (st != FSDP_OK) return st;
+    return fsdp::adamw_impl(plan, sc, nullptr, grads, grad_dtype, grads_are_replicas, master, m, v,
+                            param_out, param_dtype, fsdp::StreamSink(stream));
+  });
 }
 
 fsdp_status fsdp_adamw_step_then_gather(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
@@ -474,13 +485,15 @@ fsdp_status fsdp_adamw_step_then_gather(const fsdp_plan* plan, const fsdp_adamw_
                                         void* param_out, int32_t param_dtype,
                                         const fsdp_plan* next, const void* next_shards,
                                         void* const* full_out, void* stream) {
-  if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
-  AdamScalars sc;
-  const fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
-  if (st != FSDP_OK) return st;
-  return fsdp::adamw_gather_impl(plan, sc, nullptr, grads, grad_dtype, master, m, v, param_out,
-                                 param_dtype, next, next_shards, full_out,
-                                 fsdp::StreamSink(stream));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
+    AdamScalars sc;
+    const fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
+    if (st != FSDP_OK) return st;
+    return fsdp::adamw_gather_impl(plan, sc, nullptr, grads, grad_dtype, master, m, v, param_out,
+                                   param_dtype, next, next_shards, full_out,
+                                   fsdp::StreamSink(stream));
+  });
 }
 
 fsdp_status fsdp_reshard_plan(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder** out) {
@@ -513,102 +526,111 @@ fsdp_status fsdp_reshard_items(const fsdp_resharder* rs, int64_t* out, int64_t c
 
 fsdp_status fsdp_reshard(const fsdp_resharder* rs, const void* src, void* dst, int32_t dtype,
                          void* stream) {
-  if (!rs || !src || !dst || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
-  const int64_t es = dtype_size(dtype);
-  if (!aligned(src, es) || !aligned(dst, es)) return FSDP_ERR_INVALID_ARG;
-  if (overlap(range_of(src, rs->R_from * rs->S_from * es), range_of(dst, rs->R_to * rs->S_to * es)))
-    return FSDP_ERR_INVALID_ARG;
-  const Work* w = nullptr;
-  const fsdp_status st = rs->work.device(&w);
-  if (st != FSDP_OK) return st;
-  PtrArray d{};
-  d.p[0] = dst;
-  return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(rs->work.host.size()), src, d, 1,
-                                    static_cast<int>(es), 16, aligned(src, 16) && aligned(dst, 16),
-                                    fsdp::StreamSink(stream)));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!rs || !src || !dst || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
+    const int64_t es = dtype_size(dtype);
+    if (!aligned(src, es) || !aligned(dst, es)) return FSDP_ERR_INVALID_ARG;
+    if (overlap(range_of(src, rs->R_from * rs->S_from * es),
+                range_of(dst, rs->R_to * rs->S_to * es)))
+      return FSDP_ERR_INVALID_ARG;
+    const Work* w = nullptr;
+    const fsdp_status st = rs->work.device(&w);
+    if (st != FSDP_OK) return st;
+    PtrArray d{};
+    d.p[0] = dst;
+    const bool vec = aligned(src, 16) && aligned(dst, 16);
+    return from_hip(fsdp::launch_copy(w, static_cast<int64_t>(rs->work.host.size()), src, d, 1,
+                                      static_cast<int>(es), 16, vec, fsdp::StreamSink(stream)));
+  });
 }
 
 fsdp_status fsdp_reshard_batch(const fsdp_resharder* rs, int32_t n, const void* const* srcs,
                                void* const* dsts, int32_t dtype, void* stream) {
-  if (!rs || !srcs || !dsts || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
-  if (n < 1 || n > FSDP_MAX_RANKS) return n < 1 ? FSDP_ERR_INVALID_ARG : FSDP_ERR_UNSUPPORTED;
-  const int64_t es = dtype_size(dtype);
-  std::vector<Range> ins, outs;
-  PtrArray s{}, d{};
-  bool vec = true;
-  for (int i = 0; i < n; ++i) {
-    if (!srcs[i] || !dsts[i] || !aligned(srcs[i], es) || !aligned(dsts[i], es))
-      return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(srcs[i], 16) && aligned(dsts[i], 16);
-    ins.push_back(range_of(srcs[i], rs->R_from * rs->S_from * es));
-    outs.push_back(range_of(dsts[i], rs->R_to * rs->S_to * es));
-    s.p[i] = srcs[i];
-    d.p[i] = dsts[i];
-  }
-  if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
-  for (const Range& o : outs)
-    for (const Range& x : ins)
-      if (overlap(o, x)) return FSDP_ERR_INVALID_ARG;
-  const Work* w = nullptr;
-  const fsdp_status st = rs->work.device(&w);
-  if (st != FSDP_OK) return st;
-  return from_hip(fsdp::launch_copy_pairs(w, static_cast<int64_t>(rs->work.host.size()), s, d, n,
-                                          static_cast<int>(es), vec,
-                                          fsdp::StreamSink(stream)));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!rs || !srcs || !dsts || !valid_dtype(dtype)) return FSDP_ERR_INVALID_ARG;
+    if (n < 1 || n > FSDP_MAX_RANKS) return n < 1 ? FSDP_ERR_INVALID_ARG : FSDP_ERR_UNSUPPORTED;
+    const int64_t es = dtype_size(dtype);
+    std::vector<Range> ins, outs;
+    PtrArray s{}, d{};
+    bool vec = true;
+    for (int i = 0; i < n; ++i) {
+      if (!srcs[i] || !dsts[i] || !aligned(srcs[i], es) || !aligned(dsts[i], es))
+        return FSDP_ERR_INVALID_ARG;
+      vec = vec && aligned(srcs[i], 16) && aligned(dsts[i], 16);
+      ins.push_back(range_of(srcs[i], rs->R_from * rs->S_from * es));
+      outs.push_back(range_of(dsts[i], rs->R_to * rs->S_to * es));
+      s.p[i] = srcs[i];
+      d.p[i] = dsts[i];
+    }
+    if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
+    for (const Range& o : outs)
+      for (const Range& x : ins)
+        if (overlap(o, x)) return FSDP_ERR_INVALID_ARG;
+    const Work* w = nullptr;
+    const fsdp_status st = rs->work.device(&w);
+    if (st != FSDP_OK) return st;
+    return from_hip(fsdp::launch_copy_pairs(w, static_cast<int64_t>(rs->work.host.size()), s, d, n,
+                                            static_cast<int>(es), vec,
+                                            fsdp::StreamSink(stream)));
+  });
 }
 
 fsdp_status fsdp_grad_accumulate(const fsdp_plan* plan, const void* const* grads,
                                  int32_t grad_dtype, float* const* acc, int32_t first,
                                  void* stream) {
-  if (!plan || !grads || !acc || !valid_dtype(grad_dtype)) return FSDP_ERR_INVALID_ARG;
-  if (first != 0 && first != 1) return FSDP_ERR_INVALID_ARG;
-  const int64_t ges = dtype_size(grad_dtype);
-  std::vector<Range> outs;
-  std::vector<Range> ins;
-  PtrArray g{}, a{};
-  bool vec = true;
-  for (int r = 0; r < plan->R; ++r) {
-    if (!grads[r] || !acc[r] || !aligned(grads[r], ges) || !aligned(acc[r], 4))
-      return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(grads[r], 16) && aligned(acc[r], 16);
-    ins.push_back(range_of(grads[r], plan->T * ges));
-    outs.push_back(range_of(acc[r], plan->T * 4));
-    g.p[r] = grads[r];
-    a.p[r] = acc[r];
-  }
-  if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
-  for (const Range& o : outs)
-    for (const Range& i : ins)
-      if (overlap(o, i)) return FSDP_ERR_INVALID_ARG;
-  return from_hip(fsdp::launch_accumulate(plan->T, plan->R, g, grad_dtype, a, first != 0, vec,
-                                          fsdp::StreamSink(stream)));
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !grads || !acc || !valid_dtype(grad_dtype)) return FSDP_ERR_INVALID_ARG;
+    if (first != 0 && first != 1) return FSDP_ERR_INVALID_ARG;
+    const int64_t ges = dtype_size(grad_dtype);
+    std::vector<Range> outs;
+    std::vector<Range> ins;
+    PtrArray g{}, a{};
+    bool vec = true;
+    for (int r = 0; r < plan->R; ++r) {
+      if (!grads[r] || !acc[r] || !aligned(grads[r], ges) || !aligned(acc[r], 4))
+        return FSDP_ERR_INVALID_ARG;
+      vec = vec && aligned(grads[r], 16) && aligned(acc[r], 16);
+      ins.push_back(range_of(grads[r], plan->T * ges));
+      outs.push_back(range_of(acc[r], plan->T * 4));
+      g.p[r] = grads[r];
+      a.p[r] = acc[r];
+    }
+    if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
+    for (const Range& o : outs)
+      for (const Range& i : ins)
+        if (overlap(o, i)) return FSDP_ERR_INVALID_ARG;
+    return from_hip(fsdp::launch_accumulate(plan->T, plan->R, g, grad_dtype, a, first != 0, vec,
+                                            fsdp::StreamSink(stream)));
+  });
 }
 
 fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
                                int32_t grad_dtype, void* const* out, int32_t out_dtype,
                                void* stream) {
-  if (!plan || !grads || !out || !valid_dtype(grad_dtype) || !valid_dtype(out_dtype))
-    return FSDP_ERR_INVALID_ARG;
-  const int64_t ges = dtype_size(grad_dtype), oes = dtype_size(out_dtype);
-  std::vector<Range> outs;
-  std::vector<Range> ins;
-  PtrArray g{}, o{};
-  bool vec = true;
-  for (int r = 0; r < plan->R; ++r) {
-    if (!grads[r] || !out[r] || !aligned(grads[r], ges) || !aligned(out[r], oes))
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !grads || !out || !valid_dtype(grad_dtype) || !valid_dtype(out_dtype))
       return FSDP_ERR_INVALID_ARG;
-    vec = vec && aligned(grads[r], 16) && aligned(out[r], 16);
-    ins.push_back(range_of(grads[r], plan->T * ges));
-    outs.push_back(range_of(out[r], plan->T * oes));
-    g.p[r] = grads[r];
-    o.p[r] = out[r];
-  }
-  if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
-  for (const Range& x : outs)
-    for (const Range& i : ins)
-      if (overlap(x, i)) return FSDP_ERR_INVALID_ARG;
-  return from_hip(fsdp::launch_allreduce(plan->T, plan->R, g, grad_dtype, o, out_dtype, vec,
-                                         fsdp::StreamSink(stream)));
+    const int64_t ges = dtype_size(grad_dtype), oes = dtype_size(out_dtype);
+    std::vector<Range> outs;
+    std::vector<Range> ins;
+    PtrArray g{}, o{};
+    bool vec = true;
+    for (int r = 0; r < plan->R; ++r) {
+      if (!grads[r] || !out[r] || !aligned(grads[r], ges) || !aligned(out[r], oes))
+        return FSDP_ERR_INVALID_ARG;
+      vec = vec && aligned(grads[r], 16) && aligned(out[r], 16);
+      ins.push_back(range_of(grads[r], plan->T * ges));
+      outs.push_back(range_of(out[r], plan->T * oes));
+      g.p[r] = grads[r];
+      o.p[r] = out[r];
+    }
+    if (any_overlap(outs)) return FSDP_ERR_INVALID_ARG;
+    for (const Range& x : outs)
+      for (const Range& i : ins)
+        if (overlap(x, i)) return FSDP_ERR_INVALID_ARG;
+    return from_hip(fsdp::launch_allreduce(plan->T, plan->R, g, grad_dtype, o, out_dtype, vec,
+                                           fsdp::StreamSink(stream)));
+  });
 }
 
 const char* fsdp_status_string(fsdp_status status) {

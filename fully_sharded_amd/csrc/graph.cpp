@@ -88,7 +88,8 @@ fsdp_status fsdp_step_graph_create(const fsdp_adamw_hparams* hp, fsdp_step_graph
   if (!g) return FSDP_ERR_OUT_OF_MEMORY;
   g->hp = *hp;
   hipError_t e = hipGetDevice(&g->device);
-  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&g->scalars), sizeof(fsdp::AdamScalars));
+  if (e == hipSuccess)
+    e = hipMalloc(reinterpret_cast<void**>(&g->scalars), sizeof(fsdp::AdamScalars));
   if (e == hipSuccess) e = hipGraphCreate(&g->graph, 0);
   if (e != hipSuccess) {
     destroy(g);
@@ -104,24 +105,28 @@ void fsdp_step_graph_destroy(fsdp_step_graph* g) {
 
 fsdp_status fsdp_step_graph_add_gather(fsdp_step_graph* g, const fsdp_plan* plan,
                                        const void* shards, int32_t dtype, void* const* full_out) {
-  const fsdp_status st = check_open(g);
-  if (st != FSDP_OK) return st;
-  return fsdp::gather_impl(plan, shards, dtype, full_out, GraphSink(g));
+  return fsdp::guarded([&]() -> fsdp_status {
+    const fsdp_status st = check_open(g);
+    if (st != FSDP_OK) return st;
+    return fsdp::gather_impl(plan, shards, dtype, full_out, GraphSink(g));
+  });
 }
 
 fsdp_status fsdp_step_graph_add_adamw(fsdp_step_graph* g, const fsdp_plan* plan,
                                       const void* const* grads, int32_t grad_dtype,
                                       int32_t grads_are_replicas, float* master, float* m,
                                       float* v, void* param_out, int32_t param_dtype) {
-  const fsdp_status st = check_open(g);
-  if (st != FSDP_OK) return st;
-  const int64_t before = g->n_nodes;
-  const fsdp::AdamScalars unused{};
-  const fsdp_status r = fsdp::adamw_impl(plan, unused, g->scalars, grads, grad_dtype,
-                                         grads_are_replicas, master, m, v, param_out, param_dtype,
-                                         GraphSink(g));
-  if (r == FSDP_OK && g->n_nodes > before) ++g->n_adamw;
-  return r;
+  return fsdp::guarded([&]() -> fsdp_status {
+    const fsdp_status st = check_open(g);
+    if (st != FSDP_OK) return st;
+    const int64_t before = g->n_nodes;
+    const fsdp::AdamScalars unused{};
+    const fsdp_status r = fsdp::adamw_impl(plan, unused, g->scalars, grads, grad_dtype,
+                                           grads_are_replicas, master, m, v, param_out, param_dtype,
+                                           GraphSink(g));
+    if (g->n_nodes > before) ++g->n_adamw;  // a node reads the record, even on a later error
+    return r;
+  });
 }
 
 fsdp_status fsdp_step_graph_add_adamw_gather(fsdp_step_graph* g, const fsdp_plan* plan,
@@ -129,15 +134,17 @@ fsdp_status fsdp_step_graph_add_adamw_gather(fsdp_step_graph* g, const fsdp_plan
                                              float* master, float* m, float* v, void* param_out,
                                              int32_t param_dtype, const fsdp_plan* next,
                                              const void* next_shards, void* const* full_out) {
-  const fsdp_status st = check_open(g);
-  if (st != FSDP_OK) return st;
-  const int64_t before = g->n_nodes;
-  const fsdp::AdamScalars unused{};
-  const fsdp_status r = fsdp::adamw_gather_impl(plan, unused, g->scalars, grads, grad_dtype,
-                                                master, m, v, param_out, param_dtype, next,
-                                                next_shards, full_out, GraphSink(g));
-  if (r == FSDP_OK && g->n_nodes > before) ++g->n_adamw;
-  return r;
+  return fsdp::guarded([&]() -> fsdp_status {
+    const fsdp_status st = check_open(g);
+    if (st != FSDP_OK) return st;
+    const int64_t before = g->n_nodes;
+    const fsdp::AdamScalars unused{};
+    const fsdp_status r = fsdp::adamw_gather_impl(plan, unused, g->scalars, grads, grad_dtype,
+                                                  master, m, v, param_out, param_dtype, next,
+                                                  next_shards, full_out, GraphSink(g));
+    if (g->n_nodes > before) ++g->n_adamw;  // a node reads the record, even on a later error
+    return r;
+  });
 }
 
 fsdp_status fsdp_step_graph_info(const fsdp_step_graph* g, int64_t* n_nodes, int64_t* n_adamw) {

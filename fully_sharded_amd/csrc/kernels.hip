@@ -34,6 +34,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kEPL = 4;  // elements per lane per pass, arithmetic kernels
+// A grid dimension holds at most 2^32 - 1 lanes.
+constexpr int64_t kMaxBlocks = 0xFFFFFFFFLL / kThreads;
 
 // Pointer arrays passed by value in the kernel arguments.  Kernels
 // specialised for R <= 8 carry 8 slots, the others FSDP_MAX_RANKS: the
@@ -713,7 +715,7 @@ template <typename Args>
 hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a, const Sink& sink,
                        unsigned lds = 0) {
   if (n_work <= 0) return hipSuccess;
-  if (n_work > 0x7fffffff) return hipErrorInvalidValue;
+  if (n_work > kMaxBlocks) return hipErrorInvalidValue;
   void* args[] = {const_cast<Work**>(&work), &a};
   return sink.launch(fn, dim3(static_cast<unsigned>(n_work)), dim3(kThreads), args, lds);
 }
@@ -879,7 +881,7 @@ hipError_t launch_accumulate(int64_t T, int R, const PtrArray& grads, int grad_d
                              const PtrArray& acc, bool first, bool vec, const Sink& stream) {
   if (T <= 0) return hipSuccess;
   const int64_t blocks = (T + kThreads * kEPL - 1) / (kThreads * kEPL);
-  if (blocks > 0x7fffffff || R < 1 || R > FSDP_MAX_RANKS) return hipErrorInvalidValue;
+  if (blocks > kMaxBlocks || R < 1 || R > FSDP_MAX_RANKS) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(R));
   if (R <= kSmallPtrs) {
     AccArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), narrow<kSmallPtrs>(acc), T, first ? 1 : 0,
@@ -903,7 +905,7 @@ hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt
                             const PtrArray& out, int out_dt, bool vec, const Sink& stream) {
   if (T <= 0) return hipSuccess;
   const int64_t blocks = (T + kThreads * kEPL - 1) / (kThreads * kEPL);
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks > kMaxBlocks) return hipErrorInvalidValue;
   const void* fn;
   if (grad_dt == FSDP_BF16)
     fn = out_dt == FSDP_BF16 ? pick_allreduce<u16, u16>(R) : pick_allreduce<u16, float>(R);
@@ -925,7 +927,7 @@ hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& s
                              const PtrArray& dst, int n_pairs, int es, bool vec,
                              const Sink& stream) {
   if (n_work <= 0 || n_pairs <= 0) return hipSuccess;
-  if (n_work > 0x7fffffff || n_pairs > FSDP_MAX_RANKS) return hipErrorInvalidValue;
+  if (n_work > kMaxBlocks || n_pairs > FSDP_MAX_RANKS) return hipErrorInvalidValue;
   PairArgs a{narrow<FSDP_MAX_RANKS>(src), narrow<FSDP_MAX_RANKS>(dst), vec ? 1 : 0};
   const void* fn = es == 2 ? reinterpret_cast<const void*>(&k_copy_pairs<2>)
                            : reinterpret_cast<const void*>(&k_copy_pairs<4>);
@@ -952,7 +954,7 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                                const void* shards, const PtrArray& dst, int n_dst,
                                int lane_bytes, bool vec_g, const Sink& stream) {
   if (n_fused <= 0 || n_gather <= 0 || n_dst < 1) return hipErrorInvalidValue;
-  if (n_fused + n_gather > 0x7fffffff) return hipErrorInvalidValue;
+  if (n_fused + n_gather > kMaxBlocks) return hipErrorInvalidValue;
   int nf = static_cast<int>(n_fused);
   int wide = lane_bytes == 16 ? 1 : 0;
   const void* fn;

@@ -2,11 +2,28 @@
 // graph: argument checks plus one launch into a Sink.
 #pragma once
 
+#include <new>
+
 #include "fsdp_hip.h"
 #include "kernels.hpp"
 #include "plan.hpp"
 
 namespace fsdp {
+
+// Runs the body of a C entry point and turns a C++ exception into a status,
+// so that none crosses the C ABI: a failed host allocation (argument lists,
+// the per-device table map) gives FSDP_ERR_OUT_OF_MEMORY, anything else
+// (a lock that cannot be taken) FSDP_ERR_HIP.
+template <typename F>
+fsdp_status guarded(F&& body) noexcept {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return FSDP_ERR_OUT_OF_MEMORY;
+  } catch (...) {
+    return FSDP_ERR_HIP;
+  }
+}
 
 // FSDP_OK, or the status a failed HIP call maps to (clearing HIP's error).
 fsdp_status status_of(hipError_t e);

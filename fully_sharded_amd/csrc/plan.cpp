@@ -46,6 +46,13 @@ void emit_items(const std::vector<Work>& runs, int64_t chunk, std::vector<Work>&
   }
 }
 
+int64_t count_items(const std::vector<Work>& runs, int64_t chunk) {
+  int64_t n = 0;
+  for (const Work& w : runs)
+    if (w.len > 0) n += (w.dst + w.len - 1) / chunk - w.dst / chunk + 1;
+  return n;
+}
+
 fsdp_status WorkTable::device(const Work** out) const {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -147,6 +154,7 @@ fsdp_status build_plan(fsdp_plan* pl) {
       push_run(pl->shard_runs, r * pl->S + pos, -1, pl->S - pos);
     }
   }
+  if (count_items(pl->shard_runs, kShardChunk) > kMaxItems) return FSDP_ERR_UNSUPPORTED;
   emit_items(pl->shard_runs, kShardChunk, pl->shard_work.host);
 
   // flat-space runs: the same segments ordered by flat offset; they tile
@@ -162,8 +170,9 @@ fsdp_status build_plan(fsdp_plan* pl) {
   }
   if (expect != pl->T) return FSDP_ERR_INVALID_ARG;
   pl->gather_lane_bytes = pl->T <= kWideGatherMax ? 16 : 8;
-  emit_items(pl->flat_runs, pl->gather_lane_bytes == 16 ? kFlatChunk : kFlatChunk / 2,
-             pl->flat_work.host);
+  const int64_t flat_chunk = pl->gather_lane_bytes == 16 ? kFlatChunk : kFlatChunk / 2;
+  if (count_items(pl->flat_runs, flat_chunk) > kMaxItems) return FSDP_ERR_UNSUPPORTED;
+  emit_items(pl->flat_runs, flat_chunk, pl->flat_work.host);
   return FSDP_OK;
 }
 
@@ -202,6 +211,7 @@ fsdp_status build_reshard(const fsdp_plan* from, const fsdp_plan* to, fsdp_resha
       ++k;
     }
   }
+  if (count_items(runs, kFlatChunk) > kMaxItems) return FSDP_ERR_UNSUPPORTED;
   emit_items(runs, kFlatChunk, rs->work.host);
   return FSDP_OK;
 }

@@ -101,6 +101,16 @@ constexpr int64_t kFlatChunk = 2048;
 // 5.26 TB/s at 25M, 4.96 vs 5.68 at 100M).
 constexpr int64_t kWideGatherMax = 12582912;
 
+// A launch covers at most 2^32 - 1 lanes along x: 16,777,215 workgroups of
+// 256 lanes.  A plan (or re-shard) whose work table would need more items
+// than that is refused with FSDP_ERR_UNSUPPORTED.  The shard space holds at
+// least ceil(T / 1024) items, so the same bound covers the kernels that
+// cut the full unit into 1024-element blocks (accumulate, all-reduce).
+constexpr int64_t kMaxItems = 0xFFFFFFFFLL / 256;
+
+// Number of work items emit_items would cut `runs` into.
+int64_t count_items(const std::vector<Work>& runs, int64_t chunk);
+
 // Build every host-side table of a plan; returns FSDP_OK or an error.
 fsdp_status build_plan(fsdp_plan* pl);
 

@@ -97,7 +97,10 @@ typedef struct fsdp_plan_info {
  *   n_params >= 1 parameters; ndims[p] in [1, 8]; dims holds all shapes
  *   concatenated (sum of ndims entries, each > 0); 1 <= R <= 64; layout is
  *   FSDP_LAYOUT_*.  On success *out owns a new plan (free it with
- *   fsdp_plan_destroy); on error *out is set to NULL. */
+ *   fsdp_plan_destroy); on error *out is set to NULL.  A unit whose work
+ *   would not fit one launch's grid (16,777,215 workgroups of 1024
+ *   elements: R*S above about 17.2G elements) returns
+ *   FSDP_ERR_UNSUPPORTED. */
 fsdp_status fsdp_plan_layout(int32_t n_params, const int32_t* ndims, const int64_t* dims,
                              int32_t R, int32_t layout, fsdp_plan** out);
 
@@ -213,7 +216,8 @@ typedef struct fsdp_resharder fsdp_resharder; /* opaque; immutable once created 
  * FSDP2 page, section 10; "Understanding FSDP from source" 4.5 gathers the
  * full weights to save and re-shards them to load).  Host only; *out owns a
  * new object, freed by fsdp_reshard_destroy; the plans may be destroyed
- * afterwards. */
+ * afterwards.  FSDP_ERR_UNSUPPORTED when the copy would not fit one
+ * launch's grid (16,777,215 workgroups of 2048 elements). */
 fsdp_status fsdp_reshard_plan(const fsdp_plan* from, const fsdp_plan* to, fsdp_resharder** out);
 void fsdp_reshard_destroy(fsdp_resharder* rs);
 /* Its work items (host copy), as fsdp_plan_work_items: dst indexes `to`'s

@@ -18,7 +18,8 @@ HEADER = os.path.join(ROOT, "include", "fsdp_hip.h")
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    with open(HEADER) as f:
+        src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(fsdp_[a-z_]+)\s*\(", src)))
 
@@ -158,7 +159,8 @@ def test_product_code_never_imports_the_oracle():
     for dirpath, _, files in os.walk(pkg):
         for fn in files:
             if fn.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
-                src = open(os.path.join(dirpath, fn)).read()
+                with open(os.path.join(dirpath, fn)) as f:
+                    src = f.read()
                 assert "oracle" not in src.lower(), fn
 
 
@@ -331,3 +333,32 @@ def test_reshard_batch_checks_arguments_before_any_device_call():
     assert call(srcs, [srcs[1]] + dsts[1:]) == -1               # a destination is a source
     assert call(srcs, [_fake(10, 2)] + dsts[1:]) == -1          # fp32 misaligned
     assert call(srcs, dsts) == -4                               # valid: no device here
+
+
+def test_units_beyond_one_launch_grid_are_refused():
+    """A launch holds at most 2^32 - 1 lanes per grid dimension: 16,777,215
+    workgroups of 256 lanes, so 16,777,215 work items of 1024 shard
+    elements.  Larger units are refused when planned, before any table is
+    built; the largest accepted size is checked through the item count."""
+    L = F.lib()
+    limit = 0xFFFFFFFF // 256
+
+    def status(shapes, R, layout):
+        nd = [len(s) for s in shapes]
+        flat = [d for s in shapes for d in s]
+        h = ctypes.c_void_p()
+        st = L.fsdp_plan_layout(len(nd), (ctypes.c_int32 * len(nd))(*nd),
+                                (ctypes.c_int64 * len(flat))(*flat), R, layout, ctypes.byref(h))
+        if st == 0:
+            L.fsdp_plan_destroy(h)
+        return st
+
+    over = limit * 1024 + 1
+    assert status([(over,)], 1, 1) == -2                    # flat, R = 1
+    assert status([(over // 8 + 1, 8)], 8, 0) == -2        # per-parameter rows, R = 8
+    assert status([(3, over // 3 + 1)], 64, 0) == -2       # padding counts too: S = row
+    with pytest.raises(F.FsdpError):
+        F.Plan([(over,)], 1, "flat")
+    # exactly the limit is still planned (two tables of 16,777,215 items,
+    # about 800 MB of host memory)
+    assert status([(limit * 1024,)], 1, 1) == 0

@@ -44,8 +44,8 @@ def test_counter_summary_scales_by_the_calibration_copy(traffic_dir, capsys):
                                     (COPY, gib_kib / 2)])
     write_csv(write, "WRITE_SIZE", [(FUSED, 50.0), (FUSED, 50.0), (PAIR, 90.0), (COPY, gib_kib)])
     bench.summarise_counters(str(fetch), str(write), "wl")
-    fused = json.load(open(traffic_dir / "traffic_wl_fused.json"))
-    pair = json.load(open(traffic_dir / "traffic_wl_fused_gather.json"))
+    fused = json.loads((traffic_dir / "traffic_wl_fused.json").read_text())
+    pair = json.loads((traffic_dir / "traffic_wl_fused_gather.json").read_text())
     assert fused["fetch_scale"] == pytest.approx(2.0) and fused["write_scale"] == pytest.approx(1.0)
     # the k_fused rows only: the k_fused_gather dispatch is not mixed in
     assert fused["fetch_kib_per_launch"] == pytest.approx(101.0)
@@ -65,8 +65,8 @@ def test_counter_summary_needs_the_calibration_copy(traffic_dir):
 
 def test_traffic_is_dropped_once_the_kernels_change(traffic_dir, monkeypatch):
     path = traffic_dir / "traffic_wl_fused.json"
-    json.dump({"kernel_src_sha": bench.kernel_src_hash(), "bytes_per_launch": 123.0},
-              open(path, "w"))
+    path.write_text(json.dumps({"kernel_src_sha": bench.kernel_src_hash(),
+                                "bytes_per_launch": 123.0}))
     assert bench.load_traffic("wl", "fused") == 123.0
     assert bench.load_traffic("other", "fused") is None
     monkeypatch.setattr(bench, "kernel_src_hash", lambda: "changed")
