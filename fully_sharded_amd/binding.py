@@ -366,12 +366,9 @@ def fsdp_shard_pack(plan: Plan, full: torch.Tensor, shards: torch.Tensor, stream
 
 
 def fsdp_gather_unflatten(plan: Plan, shards: torch.Tensor, full_out, stream=None):
-    """shards [R, S] -> R full-unit buffers (list of R tensors [T] or None)."""
-    if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
-        raise ValueError("size mismatch with the plan")
-    for t in full_out:
-        if t is not None and (t.numel() != plan.T or t.dtype != shards.dtype):
-            raise ValueError("receiver size or dtype mismatch")
+    """shards [R, S] -> R full-unit buffers (a list of R tensors of at least T
+    elements, the first T written, or None to skip a receiver)."""
+    _check_gather_args(plan, shards, full_out)
     arr = _ptr_array(full_out, "full_out")
     _check("fsdp_gather_unflatten",
            lib().fsdp_gather_unflatten(plan.handle, _dev(shards, "shards"), _dtype_code(shards),
@@ -444,11 +441,7 @@ class BoundCall:
 
 def bind_gather_unflatten(plan: Plan, shards: torch.Tensor, full_out) -> "BoundCall":
     """fsdp_gather_unflatten with cached arguments; call as f(stream=None)."""
-    if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
-        raise ValueError("size mismatch with the plan")
-    for t in full_out:
-        if t is not None and (t.numel() < plan.T or t.dtype != shards.dtype):
-            raise ValueError("receiver size or dtype mismatch")
+    _check_gather_args(plan, shards, full_out)
     arr = _ptr_array(full_out, "full_out")
     call = BoundCall("fsdp_gather_unflatten",
                      (plan.handle, ctypes.c_void_p(_dev(shards, "shards")),
@@ -632,11 +625,7 @@ class StepGraph:
 
     def add_gather(self, plan: Plan, shards: torch.Tensor, full_out):
         """Record fsdp_gather_unflatten(plan, shards, full_out)."""
-        if shards.numel() != plan.R * plan.S or len(full_out) != plan.R:
-            raise ValueError("size mismatch with the plan")
-        for t in full_out:
-            if t is not None and (t.numel() < plan.T or t.dtype != shards.dtype):
-                raise ValueError("receiver size or dtype mismatch")
+        _check_gather_args(plan, shards, full_out)
         _check("fsdp_step_graph_add_gather",
                lib().fsdp_step_graph_add_gather(self._handle, plan.handle,
                                                 ctypes.c_void_p(_dev(shards, "shards")),
