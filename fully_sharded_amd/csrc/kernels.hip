@@ -11,7 +11,8 @@
 //     requests in flight for the same registers;
 //   * every streaming access is nontemporal: the data is touched once, and
 //     keeping it out of the caches raised the fused kernel from 4.8 to
-//     5.6 TB/s in isolation;
+//     5.6 TB/s in isolation (the overlapping word pairs of misaligned
+//     windows below are the exception);
 //   * work items whose source is misaligned relative to the destination
 //     funnel each lane's window out of two aligned vector loads; lanes
 //     whose chunk is cut by the ends of the range take an element-by-element
@@ -79,7 +80,11 @@ __device__ __forceinline__ void st_nt16(void* p, u32x4 x) {
 // aligned W-byte word, so it loads that word and the next one and funnels
 // the wanted bytes out of the pair (v_alignbit).  Both words hold at least
 // one element the lane needs, so nothing outside them is read and no extra
-// page is touched.
+// page is touched.  A lane's second word is its neighbour's first, so these
+// two loads are ordinary cached loads, not nontemporal ones: on the R = 3
+// hidden-512 block (every rank but 0 misaligned) the step took 28.7-29.1
+// instead of 29.6-29.8 us, the fused kernel 21.0-21.3 instead of 21.5-21.7
+// (the standalone reduce-scatter 8.8 instead of 8.6), alternating A/B runs.
 template <int NW, int Q>
 __device__ __forceinline__ void funnel_words(const uint32_t (&w)[2 * NW], uint32_t shift,
                                              uint32_t (&r)[NW]) {
@@ -107,15 +112,17 @@ __device__ __forceinline__ void funnel(const uint32_t (&w)[2 * NW], int byte, ui
 
 // 8 or 16 bytes starting `byte` bytes (0 < byte < W, element-aligned) past
 // the W-aligned address p.
-__device__ __forceinline__ u32x2 ld_nt8_shifted(const char* p, int byte) {
-  const u32x2 a = ld_nt8(p), b = ld_nt8(p + 8);
+__device__ __forceinline__ u32x2 ld8_shifted(const char* p, int byte) {
+  const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 b = *reinterpret_cast<const u32x2*>(p + 8);
   const uint32_t w[4] = {a.x, a.y, b.x, b.y};
   uint32_t r[2];
   funnel<2>(w, byte, r);
   return u32x2{r[0], r[1]};
 }
-__device__ __forceinline__ u32x4 ld_nt16_shifted(const char* p, int byte) {
-  const u32x4 a = ld_nt16(p), b = ld_nt16(p + 16);
+__device__ __forceinline__ u32x4 ld16_shifted(const char* p, int byte) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t r[4];
   funnel<4>(w, byte, r);
@@ -163,7 +170,7 @@ struct Io<float> {
   }
   // elements [s, s+4) with s % 4 == k != 0
   __device__ __forceinline__ static void load4s(const float* p, int64_t s, int k, float (&x)[4]) {
-    const u32x4 u = ld_nt16_shifted(reinterpret_cast<const char*>(p + (s - k)), 4 * k);
+    const u32x4 u = ld16_shifted(reinterpret_cast<const char*>(p + (s - k)), 4 * k);
     x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
     x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
   }
@@ -196,7 +203,7 @@ struct Io<u16> {
   }
   // elements [s, s+4) with s % 4 == k != 0
   __device__ __forceinline__ static void load4s(const u16* p, int64_t s, int k, float (&x)[4]) {
-    const u32x2 u = ld_nt8_shifted(reinterpret_cast<const char*>(p + (s - k)), 2 * k);
+    const u32x2 u = ld8_shifted(reinterpret_cast<const char*>(p + (s - k)), 2 * k);
     x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
     x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
   }
@@ -344,9 +351,9 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, 
         } else {
           const char* al = reinterpret_cast<const char*>(sp - k);
           if constexpr (W == 8)
-            v = ld_nt8_shifted(al, k * ES);
+            v = ld8_shifted(al, k * ES);
           else
-            v = ld_nt16_shifted(al, k * ES);
+            v = ld16_shifted(al, k * ES);
         }
       }
       for (int i = 0, r = first; i < a.n_dst; ++i, r = r + 1 == a.n_dst ? 0 : r + 1) {
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void k_copy_pairs(const Work* __restrict_
       u32x4 v = {0u, 0u, 0u, 0u};
       if (!pad) {
         const E* sp = src + e0 + delta;
-        v = k == 0 ? ld_nt16(sp) : ld_nt16_shifted(reinterpret_cast<const char*>(sp - k), k * ES);
+        v = k == 0 ? ld_nt16(sp) : ld16_shifted(reinterpret_cast<const char*>(sp - k), k * ES);
       }
       st_nt16(dst + e0, v);
     } else {
