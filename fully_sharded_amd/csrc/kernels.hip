@@ -516,14 +516,15 @@ struct AdamArgs {
   int vec;
 };
 
+// One pass per workgroup: lane c of the grid owns elements [4c, 4c + 4).
 template <typename P>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
   P* __restrict__ param = static_cast<P*>(a.param);
   const AdamScalars sc = a.scp ? *a.scp : a.sc;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; c * kEPL < a.n;
-       c += stride) {
+  {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     const int64_t e0 = c * kEPL;
+    if (e0 >= a.n) return;
     if (a.vec && e0 + kEPL <= a.n) {
       float g[4], p[4], m[4], v[4];
       Io<float>::load4(a.g + e0, true, g);
@@ -750,6 +751,15 @@ unsigned fused_lds(int64_t n_work) {
   return 48 * 1024;                             // 3 per CU
 }
 
+// The same cap for the unfused AdamW step (8 streams per workgroup: the
+// reduced gradient, master, m and v read; master, m, v and the parameter
+// written), whose best is 4 per CU.  One pass per workgroup, on the
+// 872M-parameter group (852k workgroups): GB/s uncapped 5,652-5,764; 4 per
+// CU 5,997; 3 per CU 5,754-5,765; 2 per CU 5,055 -- and 5,119 for the
+// earlier grid-stride loop over 65,536 workgroups.  Short launches take no
+// cap, as for the fused step.
+unsigned adamw_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 32 * 1024; }
+
 template <typename G>
 const void* pick_rs(int R) {
   switch (R) {
@@ -859,12 +869,13 @@ hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, floa
   if (n <= 0) return hipSuccess;
   AdamArgs a{g, master, m, v, param, sc, scp, n, vec ? 1 : 0};
   const int64_t chunks = (n + kEPL - 1) / kEPL;
-  int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t blocks = (chunks + kThreads - 1) / kThreads;
+  if (blocks > kMaxBlocks) return hipErrorInvalidValue;
   const void* fn = param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16>)
                                          : reinterpret_cast<const void*>(&k_adamw<float>);
   void* args[] = {&a};
-  return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args, 0);
+  return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
+                       adamw_lds(blocks));
 }
 
 hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads, int R,
