@@ -521,32 +521,30 @@ template <typename P>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
   P* __restrict__ param = static_cast<P*>(a.param);
   const AdamScalars sc = a.scp ? *a.scp : a.sc;
-  {
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const int64_t e0 = c * kEPL;
-    if (e0 >= a.n) return;
-    if (a.vec && e0 + kEPL <= a.n) {
-      float g[4], p[4], m[4], v[4];
-      Io<float>::load4(a.g + e0, true, g);
-      Io<float>::load4(a.master + e0, true, p);
-      Io<float>::load4(a.m + e0, true, m);
-      Io<float>::load4(a.v + e0, true, v);
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = c * kEPL;
+  if (e0 >= a.n) return;
+  if (a.vec && e0 + kEPL <= a.n) {
+    float g[4], p[4], m[4], v[4];
+    Io<float>::load4(a.g + e0, true, g);
+    Io<float>::load4(a.master + e0, true, p);
+    Io<float>::load4(a.m + e0, true, m);
+    Io<float>::load4(a.v + e0, true, v);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], sc);
-      Io<float>::store4(a.master + e0, true, p);
-      Io<float>::store4(a.m + e0, true, m);
-      Io<float>::store4(a.v + e0, true, v);
-      Io<P>::store4(param + e0, true, p);
-    } else {
-      const int64_t hi = e0 + kEPL < a.n ? e0 + kEPL : a.n;
-      for (int64_t e = e0; e < hi; ++e) {
-        float p = a.master[e], m = a.m[e], v = a.v[e];
-        adamw1(a.g[e], p, m, v, sc);
-        a.master[e] = p;
-        a.m[e] = m;
-        a.v[e] = v;
-        Io<P>::store1(param + e, p);
-      }
+    for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], sc);
+    Io<float>::store4(a.master + e0, true, p);
+    Io<float>::store4(a.m + e0, true, m);
+    Io<float>::store4(a.v + e0, true, v);
+    Io<P>::store4(param + e0, true, p);
+  } else {
+    const int64_t hi = e0 + kEPL < a.n ? e0 + kEPL : a.n;
+    for (int64_t e = e0; e < hi; ++e) {
+      float p = a.master[e], m = a.m[e], v = a.v[e];
+      adamw1(a.g[e], p, m, v, sc);
+      a.master[e] = p;
+      a.m[e] = m;
+      a.v[e] = v;
+      Io<P>::store1(param + e, p);
     }
   }
 }
