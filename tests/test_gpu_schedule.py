@@ -240,3 +240,55 @@ def test_units_sharing_a_plan_on_two_streams():
     for x, y in zip(state_of(ref_units), state_of(units)):
         for p, q in zip(x, y):
             assert torch.equal(p, q)
+
+
+def build_wide(R, layout, n_units, seed):
+    """n_units units of ragged shapes sharing one plan at a world size above
+    8 (the kernels with 64 pointer slots), bf16 parameters and gradients."""
+    gen_ = torch.Generator(device=DEV)
+    gen_.manual_seed(seed)
+    pl = F.Plan([(2 * R + 3, 5), (R - 1,), (7, 3, 2)], R, layout)
+    units = []
+    for _ in range(n_units):
+        full = torch.rand(pl.T, generator=gen_, device=DEV).sub_(0.5)
+        master = torch.empty(R * pl.S, device=DEV)
+        F.fsdp_shard_pack(pl, full, master)
+        param = torch.empty(R * pl.S, dtype=torch.bfloat16, device=DEV)
+        F.fsdp_shard_pack(pl, full, param)
+        grads = [torch.randn(pl.T, generator=gen_, device=DEV).mul_(1e-2).bfloat16()
+                 for _ in range(R)]
+        units.append(Unit(pl, master, torch.zeros_like(master), torch.zeros_like(master),
+                          param, grads))
+    recv = [[torch.empty(pl.T, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+            for _ in range(2)]
+    return units, recv
+
+
+@pytest.mark.parametrize("R,layout,schedule,ref_schedule", [
+    (13, "per_param", "graph", "serial"), (64, "flat", "graph", "serial"),
+    (13, "flat", "graph-overlap", "overlap"), (64, "per_param", "graph-overlap", "overlap")])
+def test_step_graph_at_world_sizes_above_eight(R, layout, schedule, ref_schedule):
+    """The step graph with the generic kernels (R > 8, 64 pointer slots):
+    every replay, with eager work and a synchronisation between replays,
+    matches the stream calls of the same schedule bit for bit."""
+    print(f"[gpu] step graph R={R} {layout} {schedule}", flush=True)
+    ref_units, ref_recv = build_wide(R, layout, 3, seed=R)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, ref_schedule)
+    units, recv = build_wide(R, layout, 3, seed=R)
+    run = StepRunner(units, ADAMW, recv, schedule)
+    assert run.graph.info()[1] == len(units)
+    scratch = torch.randn(1 << 16, device=DEV)
+    for t in (1, 2, 3):
+        run.step(t)
+        scratch.mul_(0.5).add_(1.0)
+        ref.step(t)
+        torch.cuda.synchronize()
+        for a, b in zip(state_of(ref_units), state_of(units)):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y), f"step {t}"
+        n_buf = 2 if schedule == "graph-overlap" else 1
+        for k in range(n_buf):
+            for r in range(R):
+                assert torch.equal(bits(recv[k][r]), bits(ref_recv[k][r])), f"step {t}"
+    # the replays did the work
+    assert bool((units[0].m != 0).any())
