@@ -51,7 +51,7 @@ def parse():
                          "graph-overlap: the overlap sequence replayed as one HIP graph")
     ap.add_argument("--cycle-gib", type=float, default=4.0,
                     help="give the workload enough independent copies of its buffers that "
-                         "one round of steps touches at least this many GiB (the 256 MB "
+                         "one cycle of steps touches at least this many GiB (the 256 MB "
                          "last-level cache keeps part of a smaller cycle between steps)")
     ap.add_argument("--gathers-per-step", type=int, choices=(1, 2), default=1,
                     help="1: parameters kept from forward to backward "
