@@ -182,9 +182,10 @@ fsdp_status fsdp_reduce_scatter_avg(const fsdp_plan* plan, const void* const* gr
 
 /* AdamW on every rank's shard, then the parameter recast.  Per element,
  * with g the rank's averaged gradient and t = step:
- *   p1 = p (1 - lr wd); m' = b1 m + (1-b1) g; v' = b2 v + (1-b2) g^2;
- *   p' = p1 - (lr m'/(1-b1^t)) / (sqrt(v'/(1-b2^t)) + eps)
- * evaluated in IEEE double from the fp32 state and gradient, in that order,
+ *   p1 = p (1 - lr wd); m' = b1 m + (1-b1) g; v' = b2 v + ((1-b2) g) g;
+ *   p' = p1 - (lr (m'/(1-b1^t))) / (sqrt(v'/(1-b2^t)) + eps)
+ * evaluated in IEEE double from the fp32 state and gradient, in that order
+ * (products and sums left to right, 1-b1^t and 1-b2^t computed once),
  * each of p', m', v' rounded once to fp32; param_out = p' cast to
  * param_dtype.  The pages run
  * torch.optim.AdamW on the local shards with state shaped like the shard
