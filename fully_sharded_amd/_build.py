@@ -54,7 +54,28 @@ def build(verbose: bool = True) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_c_driver(verbose)
     return LIB
+
+
+# A plain C99 program that drives one training step through the C ABI with
+# device memory from the HIP runtime (tests/c/step_from_c.c): the GPU tests
+# run it to show the library works without Python.  Host code only (gcc).
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c", "step_from_c.c")
+C_DRIVER = os.path.join(ROOT, "tests", "c", "step_from_c")
+
+
+def build_c_driver(verbose: bool = True) -> str:
+    tmp = C_DRIVER + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", "/opt/rocm/include", C_DRIVER_SRC, "-o", tmp, "-L", PKG, "-lfsdp_hip",
+           "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../fully_sharded_amd",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, C_DRIVER)
+    return C_DRIVER
 
 
 if __name__ == "__main__":

@@ -5,6 +5,7 @@ with the oracle's independently written layout."""
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -235,7 +236,6 @@ def test_header_compiles_as_c99_and_plans_from_plain_c(tmp_path):
     """A plain C99 program includes include/fsdp_hip.h, links the library and
     plans the TransformerBlock FlatParameter of the 4-GPU example."""
     import shutil
-    import subprocess
     gcc = shutil.which("gcc") or shutil.which("cc")
     if gcc is None:
         pytest.skip("no C compiler")
@@ -362,3 +362,18 @@ def test_units_beyond_one_launch_grid_are_refused():
     # exactly the limit is still planned (two tables of 16,777,215 items,
     # about 800 MB of host memory)
     assert status([(limit * 1024,)], 1, 1) == 0
+
+
+def test_c_driver_refuses_bad_input_before_any_device_call(tmp_path):
+    """The plain-C driver of the GPU tests (built with the library) checks
+    its input files before it touches the GPU."""
+    exe = os.path.join(ROOT, "tests", "c", "step_from_c")
+    assert os.path.exists(exe), "build the library first: python -m fully_sharded_amd._build"
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 1 and "usage" in out.stderr
+    out = subprocess.run([exe, str(tmp_path / "missing")], capture_output=True, text=True,
+                         timeout=60)
+    assert out.returncode == 1 and "shape.txt" in out.stderr
+    (tmp_path / "shape.txt").write_text("2 0 1\n0\n")
+    out = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 1 and "bad ndims" in out.stderr
