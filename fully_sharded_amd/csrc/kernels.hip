@@ -17,10 +17,10 @@
 //     funnel each lane's window out of two aligned vector loads; lanes
 //     whose chunk is cut by the ends of the range take an element-by-element
 //     path with the same arithmetic;
-//   * long fused launches cap their resident workgroups per CU (see
-//     fused_lds), and a short fused step can share its launch with the next
-//     unit's gather (k_fused_gather), which then starts while the step
-//     drains.
+//   * long fused and unfused AdamW launches cap their resident workgroups
+//     per CU (fused_lds, adamw_lds), and a short fused step can share its
+//     launch with the next unit's gather (k_fused_gather), which then
+//     starts while the step drains.
 //
 // Reductions are fp32, in rank order 0..R-1 starting from rank 0's value,
 // then one correctly rounded division by R: one lane owns an element and
