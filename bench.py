@@ -135,27 +135,40 @@ def rows(n_rows, n, dtype, device):
     return [buf[i * stride // es:i * stride // es + n] for i in range(n_rows)]
 
 
+# Timed dispatches of the --calibrate-copy leg: the last plain copies of a
+# run (nothing after it launches a kernel).
+CALIB_TIMED = 10
+
+
 def summarise_counters(fetch_csv, write_csv, workload):
     """HBM bytes per launch of each kernel in TRAFFIC_KERNELS that the runs
     dispatched, from the FETCH_SIZE and WRITE_SIZE counters (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB
-    plain copy of --calibrate-copy (1 GiB read, 1 GiB written)."""
+    plain copy of --calibrate-copy (1 GiB read, 1 GiB written): the median
+    of the run's last CALIB_TIMED copy dispatches, by dispatch id (set-up
+    copies earlier in the run can be larger)."""
     import csv
+    import statistics
 
     def load(path, counter, frag):
         sel, copy = [], []
         with open(path) as f:
-            for r in csv.DictReader(f):
+            for i, r in enumerate(csv.DictReader(f)):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
                 if frag in name:
                     sel.append(float(r["Counter_Value"]))
                 elif "copy" in name.lower() and "fsdp" not in name:
-                    copy.append(float(r["Counter_Value"]))
+                    order = int(r["Dispatch_Id"]) if r.get("Dispatch_Id") else i
+                    copy.append((order, float(r["Counter_Value"])))
         if not copy:
             raise SystemExit(f"{path}: no calibration-copy dispatches for {counter}")
-        return (sum(sel) / len(sel) if sel else None), max(copy), len(sel)
+        calib = [v for _, v in sorted(copy)[-CALIB_TIMED:]]
+        if max(calib) > 1.02 * min(calib):
+            raise SystemExit(f"{path}: the last {len(calib)} copy dispatches differ "
+                             f"({min(calib)} to {max(calib)} KiB): not the calibration copy")
+        return (sum(sel) / len(sel) if sel else None), statistics.median(calib), len(sel)
 
     gib_kib = float(1 << 20)
     for key, (frag, desc) in TRAFFIC_KERNELS.items():
@@ -441,11 +454,11 @@ def main():
         for _ in range(3):
             b.copy_(a)
         c0.record(stream)
-        for _ in range(10):
+        for _ in range(CALIB_TIMED):
             b.copy_(a)
         c1.record(stream)
         torch.cuda.synchronize()
-        ms = c0.elapsed_time(c1) / 10
+        ms = c0.elapsed_time(c1) / CALIB_TIMED
         copy_info = dict(bytes=2 * n * 4, ms=ms, gbps=2 * n * 4 / (ms * 1e-3) / 1e9)
         del a, b
 

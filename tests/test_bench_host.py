@@ -39,10 +39,14 @@ def traffic_dir(tmp_path, monkeypatch):
 def test_counter_summary_scales_by_the_calibration_copy(traffic_dir, capsys):
     fetch, write = traffic_dir / "f.csv", traffic_dir / "w.csv"
     gib_kib = float(1 << 20)
-    # FETCH_SIZE reads half of what the 1 GiB copy moves, WRITE_SIZE all of it
-    write_csv(fetch, "FETCH_SIZE", [(FUSED, 100.0), (FUSED, 102.0), (PAIR, 300.0),
-                                    (COPY, gib_kib / 2)])
-    write_csv(write, "WRITE_SIZE", [(FUSED, 50.0), (FUSED, 50.0), (PAIR, 90.0), (COPY, gib_kib)])
+    # FETCH_SIZE reads half of what the 1 GiB copy moves, WRITE_SIZE all of
+    # it; a larger set-up copy comes first in the run and is not the
+    # calibration (the calibration is the run's last 10 copies)
+    calib = bench.CALIB_TIMED
+    write_csv(fetch, "FETCH_SIZE", [(COPY, 0.8 * gib_kib), (FUSED, 100.0), (FUSED, 102.0),
+                                    (PAIR, 300.0)] + [(COPY, gib_kib / 2)] * (3 + calib))
+    write_csv(write, "WRITE_SIZE", [(COPY, 1.6 * gib_kib), (FUSED, 50.0), (FUSED, 50.0),
+                                    (PAIR, 90.0)] + [(COPY, gib_kib)] * (3 + calib))
     bench.summarise_counters(str(fetch), str(write), "wl")
     fused = json.loads((traffic_dir / "traffic_wl_fused.json").read_text())
     pair = json.loads((traffic_dir / "traffic_wl_fused_gather.json").read_text())
@@ -53,6 +57,16 @@ def test_counter_summary_scales_by_the_calibration_copy(traffic_dir, capsys):
     assert pair["dispatches"] == {"FETCH_SIZE": 1, "WRITE_SIZE": 1}
     assert pair["bytes_per_launch"] == pytest.approx((300.0 * 2 + 90.0) * 1024)
     assert fused["kernel_src_sha"] == bench.kernel_src_hash()
+
+
+def test_counter_summary_refuses_copies_that_are_not_the_calibration(traffic_dir):
+    fetch, write = traffic_dir / "f.csv", traffic_dir / "w.csv"
+    gib_kib = float(1 << 20)
+    mixed = [(COPY, gib_kib / 2)] * (bench.CALIB_TIMED - 1) + [(COPY, gib_kib)]
+    write_csv(fetch, "FETCH_SIZE", [(FUSED, 100.0)] + mixed)
+    write_csv(write, "WRITE_SIZE", [(FUSED, 50.0)] + mixed)
+    with pytest.raises(SystemExit):
+        bench.summarise_counters(str(fetch), str(write), "wl")
 
 
 def test_counter_summary_needs_the_calibration_copy(traffic_dir):
