@@ -284,6 +284,36 @@ def test_nan_inf_and_signed_zero_propagate_like_the_oracle():
     assert_bf16_within_ulp(to_host(p_d).reshape(R, S), pp, "param specials")
 
 
+def test_bf16_recast_over_every_fp32_pattern():
+    """The kernels' fp32 -> bf16 rounding (the pack-cast kernel; the fused
+    step stores its parameter through the same device function) on all
+    2^32 fp32 bit patterns, in four launches of 2^30 elements: equal to
+    torch's round-to-nearest-even GPU cast on every non-NaN input, NaN kept
+    NaN; and equal to the oracle, bit for bit including NaN, on a window of
+    2^20 patterns at the start and at the end of each launch (zeros,
+    subnormals, the largest finite values, infinities and NaNs)."""
+    n = 1 << 30
+    pl = F.Plan([(n,)], 1, "flat")            # R = 1: the pack is the cast itself
+    out = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    w = 1 << 20
+    for c in range(4):
+        banner(f"bf16 recast, fp32 patterns {c * n:#x}..{(c + 1) * n - 1:#x}")
+        start = c * n if c * n < (1 << 31) else c * n - (1 << 32)   # as int32 bits
+        bits_ = torch.arange(n, dtype=torch.int32, device=DEV).add_(start)
+        x = bits_.view(torch.float32)
+        F.fsdp_shard_pack(pl, x, out)
+        ref = x.to(torch.bfloat16)
+        nan = torch.isnan(x)
+        diff = (out.view(torch.int16) != ref.view(torch.int16)) & ~nan
+        assert int(diff.sum()) == 0, f"{int(diff.sum())} patterns differ from torch's cast"
+        assert bool(torch.isnan(out.float())[nan].all()), "a NaN lost its class"
+        for lo in (0, n - w):
+            xs = to_host(x[lo:lo + w])
+            assert_bitexact(to_host(out[lo:lo + w]), O.bf16_rne(xs), f"window {c}.{lo}")
+        del bits_, x, ref, nan, diff
+    torch.cuda.synchronize()
+
+
 def test_repeat_runs_are_bit_identical():
     banner("determinism")
     wl = WORKLOADS["block512_r3"]

@@ -479,6 +479,33 @@ def test_bf16_nan_stays_nan():
     assert np.all(np.isnan(back))
 
 
+def test_bf16_rne_over_every_fp32_pattern_matches_torch():
+    """All 2^32 fp32 bit patterns, in 64 chunks on 8 threads (about 20 s):
+    the oracle's recast equals torch's round-to-nearest-even cast (a library
+    routine) on every non-NaN input, and keeps every NaN a NaN (torch
+    returns one canonical NaN, so only the class is compared)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    chunk = 1 << 26
+
+    def check(c):
+        x = (np.arange(chunk, dtype=np.uint32) + np.uint32(c * chunk)).view(np.float32)
+        ours = O.bf16_rne(x)
+        ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(x)
+        return (int(np.count_nonzero(ours[~nan] != ref[~nan])),
+                int(np.count_nonzero((ours[nan] & 0x7FFF) <= 0x7F80)))
+
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with ThreadPoolExecutor(8) as ex:
+            bad = list(ex.map(check, range((1 << 32) // chunk)))
+    finally:
+        torch.set_num_threads(threads)
+    assert all(b == (0, 0) for b in bad), [(i, b) for i, b in enumerate(bad) if b != (0, 0)]
+
+
 # ---------------------------------------------------------------- isolation
 def test_oracle_is_independent_of_the_library():
     here = os.path.dirname(O.__file__)
