@@ -11,9 +11,11 @@ receive buffers.  Default workload: the 12-layer model of TransformerBlocks
 virtual ranks in one GPU's memory (37,761,024 parameters).  Inputs are
 synthetic, seeded and resident in HBM before timing starts.
 
-Prints one JSON line: params/s of the whole step, achieved algorithmic HBM
+Prints one JSON line: params/s of the whole step (the mean over the timed
+steps, with the median and min of blocks of them), achieved algorithmic HBM
 GB/s, the roofline of the step's dominant kernel from HIP events around its
-launches, and the CPU oracle timed on a bounded sample on the host.
+launches, a plain copy of the same bytes in one launch for comparison, and
+the CPU oracle timed on a bounded sample on the host.
 """
 
 from __future__ import annotations
@@ -311,17 +313,23 @@ def main():
     torch.cuda.synchronize()
 
     # ----------------------------------------- timed region: the clean steps
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # K steps between two HIP events; events between blocks of them (a
+    # marker each, no synchronisation) also give the median and the min of
+    # the per-block step times
+    bounds = step_blocks(args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in bounds]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    evs[0].record(stream)
+    for i in range(1, len(bounds)):
+        for _ in range(bounds[i] - bounds[i - 1]):
+            step()
+        evs[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    block_ms = [evs[i - 1].elapsed_time(evs[i]) / (bounds[i] - bounds[i - 1])
+                for i in range(1, len(bounds))]
 
     # ------------- per-kernel durations: HIP events around back-to-back runs
     # of one kernel over all units (an event between every launch would add
@@ -442,6 +450,7 @@ def main():
     dom_key, dom_bytes, dom_ms = dominant
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(args.workload, dom_key)
+    plain = plain_copy(dom_bytes, args.cycle_gib, dev, hs, reps)
 
     copy_info = None
     if args.calibrate_copy:
@@ -475,6 +484,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_blocks": {"blocks": len(block_ms), "median": float(np.median(block_ms)),
+                               "min": min(block_ms)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -515,6 +526,7 @@ def main():
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
         },
+        "plain_copy": plain,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "setup_s": setup_s,
@@ -522,6 +534,45 @@ def main():
     if copy_info:
         line["copy_calibration"] = copy_info
     print(json.dumps(line), flush=True)
+
+
+def step_blocks(steps, n_blocks=10):
+    """Boundaries 0 = b_0 < b_1 < ... < b_n = steps of at most n_blocks
+    near-equal blocks of timed steps."""
+    n = max(1, min(n_blocks, steps))
+    return [round(i * steps / n) for i in range(n + 1)]
+
+
+def plain_copy(bytes_per_launch, cycle_gib, dev, hs, reps):
+    """The simplest stream pattern at the dominant launch's size, for
+    comparison: a plain fp32 copy (one read and one write stream, 16-byte
+    nontemporal lanes, no occupancy cap) moving the same number of bytes in
+    one launch of the library's copy kernel (fsdp_shard_pack of one [n]
+    parameter at R = 1), over enough buffer pairs that the 256 MB last-level
+    cache serves none of it.  Launches are capped at 4 GiB moved, beyond
+    which the rate no longer grows."""
+    import torch
+
+    import fully_sharded_amd as F
+    n = max(1024, int(min(bytes_per_launch, 4 << 30)) // 8)
+    plan = F.Plan([(n,)], 1, "flat")
+    plan.prepare()
+    n_pairs = max(2, min(32, -(-int(cycle_gib * (1 << 30)) // (8 * n))))
+    bufs = [(torch.ones(n, dtype=torch.float32, device=dev),
+             torch.empty(n, dtype=torch.float32, device=dev)) for _ in range(n_pairs)]
+    calls = [F.bind_shard_pack(plan, a, b) for a, b in bufs]
+    for c in calls:
+        c(hs)
+    k = [0]
+
+    def one():
+        calls[k[0] % n_pairs](hs)
+        k[0] += 1
+    ms = _timed(one, max(reps, 2 * n_pairs))
+    del bufs, calls
+    return {"kernel": "k_copy (fsdp_shard_pack: one fp32 parameter, R = 1)",
+            "bytes_per_launch": 8 * n, "avg_ms": ms, "achieved": 8 * n / (ms * 1e-3) / 1e9,
+            "frac": 8 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "buffer_pairs": n_pairs}
 
 
 # ------------------------------------------------------------ other modes

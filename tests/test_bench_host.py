@@ -132,3 +132,11 @@ def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_src_hash() == h0
     (src / "kernels.hip").write_text("int f() { return 2; }\n")
     assert bench.kernel_src_hash() != h0
+
+
+def test_step_blocks_cover_the_timed_steps():
+    for steps in (1, 3, 4, 10, 199, 200):
+        b = bench.step_blocks(steps)
+        assert b[0] == 0 and b[-1] == steps and len(b) - 1 == min(10, steps)
+        sizes = [y - x for x, y in zip(b, b[1:])]
+        assert min(sizes) >= 1 and max(sizes) - min(sizes) <= 1

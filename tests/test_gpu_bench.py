@@ -40,6 +40,14 @@ def test_step_line_contract(capsys, monkeypatch):
     assert 0 < rf["frac"] < 1
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0 and cb["sample"]
+    # 4 steps timed in 4 blocks of one: the mean lies between their min and max
+    bl = d["ms_per_step_blocks"]
+    assert bl["blocks"] == 4 and 0 < bl["min"] <= bl["median"]
+    assert bl["min"] <= d["ms_per_step"] * (1 + 1e-6)
+    cc = d["plain_copy"]
+    assert cc["bytes_per_launch"] == pytest.approx(rf["bytes_per_launch"], rel=1e-4)
+    assert cc["achieved"] == pytest.approx(cc["bytes_per_launch"] / (cc["avg_ms"] * 1e-3) / 1e9)
+    assert 0 < cc["frac"] < 1
 
 
 @pytest.mark.parametrize("mode", ["reshard", "accum", "ddp"])
