@@ -451,6 +451,17 @@ def main():
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(args.workload, dom_key)
     plain = plain_copy(dom_bytes, args.cycle_gib, dev, hs, reps)
+    # every kernel line against a plain copy of its own bytes in one launch:
+    # a short launch loses its ramp and drain whatever it computes
+    copies_by_size = {plain["bytes_per_launch"]: plain}
+    for key, k in kernels.items():
+        if isinstance(k, dict):
+            size = plain_copy_bytes(k["bytes"])
+            if size not in copies_by_size:
+                copies_by_size[size] = plain_copy(k["bytes"], args.cycle_gib, dev, hs, reps)
+            pc = copies_by_size[size]
+            k["plain_copy_gbps"] = pc["achieved"]
+            k["of_plain_copy"] = k["gbps"] / pc["achieved"]
 
     copy_info = None
     if args.calibrate_copy:
@@ -543,6 +554,13 @@ def step_blocks(steps, n_blocks=10):
     return [round(i * steps / n) for i in range(n + 1)]
 
 
+def plain_copy_bytes(bytes_per_launch):
+    """Bytes one launch of the comparison copy moves for a kernel moving
+    bytes_per_launch: the same, in whole fp32 elements (4 read + 4 written
+    each), at least 8 KiB and at most 4 GiB."""
+    return 8 * max(1024, int(min(bytes_per_launch, 4 << 30)) // 8)
+
+
 def plain_copy(bytes_per_launch, cycle_gib, dev, hs, reps):
     """The simplest stream pattern at the dominant launch's size, for
     comparison: a plain fp32 copy (one read and one write stream, 16-byte
@@ -554,7 +572,7 @@ def plain_copy(bytes_per_launch, cycle_gib, dev, hs, reps):
     import torch
 
     import fully_sharded_amd as F
-    n = max(1024, int(min(bytes_per_launch, 4 << 30)) // 8)
+    n = plain_copy_bytes(bytes_per_launch) // 8
     plan = F.Plan([(n,)], 1, "flat")
     plan.prepare()
     n_pairs = max(2, min(32, -(-int(cycle_gib * (1 << 30)) // (8 * n))))
@@ -570,6 +588,7 @@ def plain_copy(bytes_per_launch, cycle_gib, dev, hs, reps):
         k[0] += 1
     ms = _timed(one, max(reps, 2 * n_pairs))
     del bufs, calls
+    torch.cuda.empty_cache()
     return {"kernel": "k_copy (fsdp_shard_pack: one fp32 parameter, R = 1)",
             "bytes_per_launch": 8 * n, "avg_ms": ms, "achieved": 8 * n / (ms * 1e-3) / 1e9,
             "frac": 8 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "buffer_pairs": n_pairs}

@@ -140,3 +140,10 @@ def test_step_blocks_cover_the_timed_steps():
         assert b[0] == 0 and b[-1] == steps and len(b) - 1 == min(10, steps)
         sizes = [y - x for x, y in zip(b, b[1:])]
         assert min(sizes) >= 1 and max(sizes) - min(sizes) <= 1
+
+
+def test_plain_copy_sizes():
+    assert bench.plain_copy_bytes(188805120) == 188805120
+    assert bench.plain_copy_bytes(188805121) == 188805120
+    assert bench.plain_copy_bytes(100) == 8192
+    assert bench.plain_copy_bytes(36642816000) == 4 << 30

@@ -48,6 +48,10 @@ def test_step_line_contract(capsys, monkeypatch):
     assert cc["bytes_per_launch"] == pytest.approx(rf["bytes_per_launch"], rel=1e-4)
     assert cc["achieved"] == pytest.approx(cc["bytes_per_launch"] / (cc["avg_ms"] * 1e-3) / 1e9)
     assert 0 < cc["frac"] < 1
+    for name, k in d["kernels"].items():
+        if isinstance(k, dict):
+            assert k["of_plain_copy"] == pytest.approx(k["gbps"] / k["plain_copy_gbps"]), name
+            assert 0 < k["of_plain_copy"] < 2, name
 
 
 @pytest.mark.parametrize("mode", ["reshard", "accum", "ddp"])
