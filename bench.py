@@ -124,17 +124,10 @@ def load_traffic(workload, key="fused"):
 
 
 def rows(n_rows, n, dtype, device):
-    """n_rows tensors of n elements carved from one buffer.  The row stride
-    is n rounded up to 256 bytes, plus 256 bytes when it would be a multiple
-    of 4 KiB: rows whose bases differ by large powers of two put the same
-    offsets on the same HBM channels at the same time."""
-    import torch
-    es = torch.empty(0, dtype=dtype).element_size()
-    stride = -(-n * es // 256) * 256
-    if stride % 4096 == 0:
-        stride += 256
-    buf = torch.empty(n_rows * stride // es, dtype=dtype, device=device)
-    return [buf[i * stride // es:i * stride // es + n] for i in range(n_rows)]
+    """n_rows tensors of n elements carved from one buffer, with the
+    package's placement rule (fully_sharded_amd.buffers)."""
+    from fully_sharded_amd.buffers import rows as carve
+    return carve(n_rows, n, dtype, device)
 
 
 # Timed dispatches of the --calibrate-copy leg: the last plain copies of a
@@ -236,14 +229,12 @@ def setup_units(wl, dev):
             plans[shapes].prepare()
         pl = plans[shapes]
         full = gen.device_master(wl, u, list(shapes), dev)
-        master, m, v = rows(3, R * pl.S, torch.float32, dev)
+        master, m, v, param, grads = F.unit_buffers(pl, pdt, gdt, dev)
         m.zero_()
         v.zero_()
         F.fsdp_shard_pack(pl, full, master)
-        param = torch.empty(R * pl.S, dtype=pdt, device=dev)
         F.fsdp_shard_pack(pl, full, param)
         del full
-        grads = rows(R, pl.T, gdt, dev)
         for r in range(R):
             grads[r].copy_(gen.device_grad(wl, 1, u, r, pl.T, dev))
         units.append(Unit(pl, master, m, v, param, grads))

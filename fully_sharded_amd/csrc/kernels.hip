@@ -738,7 +738,7 @@ hipError_t launch_work(const void* fn, const Work* work, int64_t n_work, Args& a
 // 5353 / 5300 / 5219; 4 blocks 5767 / 5836 / 5763; 16 blocks (49k items)
 // 5920 / 6136 / 6031; 32 blocks 5704 / 5885 / 6086; 128 blocks (394k items)
 // 5404 / 5641 / 5824; the 872M-parameter group (852k items)
-// 5674 / 5931 / 6205.  Sixteen streams per workgroup (8 gradients, 3 states
+// 5674 / 5931 / 6205.  Fifteen streams per workgroup (8 gradients, 3 states
 // read; 4 arrays written) are far more than the DRAM pages one channel
 // keeps open; fewer workgroups in flight keep fewer pages busy while still
 // covering the latency, once the launch is long enough that its ramp does

@@ -37,6 +37,14 @@
  *   on a device uploads the plan's work tables there (hipMalloc, owned by
  *   the plan, freed by fsdp_plan_destroy); fsdp_plan_prepare does that
  *   upload ahead of time, e.g. before stream capture.
+ *   Placement.  Any placement is correct.  For speed, do not give the
+ *   arrays one kernel touches at the same element offset (the R gradient
+ *   replicas, master, m, v, the parameter shards) base addresses that agree
+ *   modulo a large power of two, as separate 2 MiB-aligned allocations do:
+ *   those accesses then meet on the same HBM channels (on MI355X the fused
+ *   step lost 3-6%).  Carving the replicas from one buffer, and master, m
+ *   and v from another, with row strides that are not multiples of 4 KiB
+ *   avoids it.
  *   Execution.  Operations are enqueued on `stream` (a hipStream_t; NULL is
  *   the null stream), asynchronous, in stream order, with no internal
  *   synchronisation.  Calls with the same plan may run concurrently on

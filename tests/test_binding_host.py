@@ -54,3 +54,23 @@ def test_plan_views_without_a_gpu(plan):
     assert w.shape == (6, 4) and b.shape == (5,)
     assert w.data_ptr() == full.data_ptr()            # views, no copy
     assert torch.equal(b, torch.arange(24, 29, dtype=torch.float32))
+
+
+def test_unit_buffers_carve_rows_off_4k_strides(plan):
+    master, m, v, param, grads = F.unit_buffers(plan, torch.bfloat16, torch.bfloat16, "cpu")
+    n = plan.R * plan.S
+    assert [t.numel() for t in (master, m, v, param)] == [n] * 4
+    assert master.dtype == m.dtype == v.dtype == torch.float32 and param.dtype == torch.bfloat16
+    assert len(grads) == plan.R and all(g.numel() == plan.T for g in grads)
+    assert all(g.dtype == torch.bfloat16 for g in grads)
+    for row in ([master, m, v], grads):
+        bases = [t.data_ptr() for t in row]
+        steps = {b - a for a, b in zip(bases, bases[1:])}
+        assert len(steps) == 1
+        step = steps.pop()
+        assert step % 256 == 0 and step % 4096 != 0 and step >= row[0].numel() * row[0].element_size()
+    # rows of one buffer: 4 KiB rows get 256 B more, short rows round to 256 B
+    a = F.rows(3, 1024, torch.float32, "cpu")
+    assert a[1].data_ptr() - a[0].data_ptr() == 4096 + 256
+    c = F.rows(2, 100, torch.bfloat16, "cpu")
+    assert c[1].data_ptr() - c[0].data_ptr() == 256
