@@ -625,6 +625,17 @@ def _cpu_loop(work, budget_s):
 
 
 def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
+    """Print a widened mode's JSON line; every kernel in it, and the
+    roofline's, is also compared with a plain copy of its bytes."""
+    import torch
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    reps = max(5, args.steps // 4)
+    plain = plain_copy(roofline["bytes_per_launch"], args.cycle_gib, "cuda", hs, reps)
+    for k in kernels.values():
+        pc = (plain if plain_copy_bytes(k["bytes"]) == plain["bytes_per_launch"]
+              else plain_copy(k["bytes"], args.cycle_gib, "cuda", hs, reps))
+        k["plain_copy_gbps"] = pc["achieved"]
+        k["of_plain_copy"] = k["gbps"] / pc["achieved"]
     d = {
         "metric": metric, "value": value, "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -632,7 +643,7 @@ def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
         "data": "synthetic",
         "config": dict({"workload": args.workload, "units": len(wl["units"]), "R": wl["R"],
                         "layout": wl["layout"], "mode": args.mode}, **cfg),
-        "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+        "kernels": kernels, "roofline": roofline, "plain_copy": plain, "cpu_baseline": cpu,
     }
     if extra:
         d.update(extra)
@@ -641,7 +652,8 @@ def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
 
 def _roof(bytes_per_launch, ms):
     gbps = bytes_per_launch / (ms * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+    return {"bytes_per_launch": bytes_per_launch, "avg_ms": ms, "bound": "hbm",
+            "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": gbps / PEAK_HBM_GBPS, "traffic": None}
 
 

@@ -63,3 +63,7 @@ def test_mode_lines(capsys, monkeypatch, mode):
     assert d["value"] > 0 and d["ms_per_step"] > 0
     assert d["roofline"]["bound"] == "hbm" and 0 < d["roofline"]["frac"] < 1
     assert d["config"]["mode"] == mode
+    assert d["plain_copy"]["bytes_per_launch"] == pytest.approx(
+        d["roofline"]["bytes_per_launch"], rel=1e-4)
+    for name, k in d["kernels"].items():
+        assert k["of_plain_copy"] == pytest.approx(k["gbps"] / k["plain_copy_gbps"]), name
