@@ -529,6 +529,7 @@ def main():
             "traffic": traffic,
         },
         "plain_copy": plain,
+        "plan_layout": time_plan_layout(wl),
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "setup_s": setup_s,
@@ -543,6 +544,24 @@ def step_blocks(steps, n_blocks=10):
     near-equal blocks of timed steps."""
     n = max(1, min(n_blocks, steps))
     return [round(i * steps / n) for i in range(n + 1)]
+
+
+def time_plan_layout(wl, budget_s=0.5):
+    """Host time of fsdp_plan_layout for the workload's distinct unit shape
+    lists (the plans the step uses; device upload excluded), averaged over
+    repeats within about budget_s."""
+    import fully_sharded_amd as F
+    from workloads.configs import shapes_of
+    shape_sets = list(dict.fromkeys(tuple(shapes_of(u)) for u in wl["units"]))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for sh in shape_sets:
+            F.fsdp_plan_layout(list(sh), wl["R"], wl["layout"])
+        reps += 1
+        if time.perf_counter() - t0 > budget_s or reps >= 1000:
+            break
+    return {"ms": (time.perf_counter() - t0) / reps * 1e3, "plans": len(shape_sets),
+            "repeats": reps, "where": "host, one thread"}
 
 
 def plain_copy_bytes(bytes_per_launch):

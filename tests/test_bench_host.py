@@ -147,3 +147,9 @@ def test_plain_copy_sizes():
     assert bench.plain_copy_bytes(188805121) == 188805120
     assert bench.plain_copy_bytes(100) == 8192
     assert bench.plain_copy_bytes(36642816000) == 4 << 30
+
+
+def test_plan_layout_timing_on_the_host():
+    from workloads.configs import WORKLOADS
+    t = bench.time_plan_layout(WORKLOADS["model12_r8"], budget_s=0.05)
+    assert t["plans"] == 1 and t["repeats"] >= 1 and t["ms"] > 0
