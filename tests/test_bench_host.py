@@ -153,3 +153,11 @@ def test_plan_layout_timing_on_the_host():
     from workloads.configs import WORKLOADS
     t = bench.time_plan_layout(WORKLOADS["model12_r8"], budget_s=0.05)
     assert t["plans"] == 1 and t["repeats"] >= 1 and t["ms"] > 0
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
