@@ -288,6 +288,21 @@ __device__ __forceinline__ void adamw1(float gf, float& pf, float& mf, float& vf
   vf = static_cast<float>(v1);
 }
 
+// The step's scalars.  Stream launches carry them in the kernel arguments;
+// graph nodes (REC) read the device record written before each replay, in
+// one 72-byte load issued beside the work descriptor's.  A single kernel
+// choosing between the two at run time compiled to nine dependent 8-byte
+// loads before the descriptor's, which slowed every graph node's
+// workgroups; the choice is therefore made at compile time.
+template <bool REC>
+__device__ __forceinline__ AdamScalars scalars_of(const AdamScalars& own,
+                                                  const AdamScalars* __restrict__ rec) {
+  if constexpr (REC)
+    return *rec;
+  else
+    return own;
+}
+
 // ------------------------------------------------------------------ copy
 // Bit copy, W bytes per lane (W/ES elements), from one source to up to R
 // destinations.  With several destinations each workgroup starts its
@@ -517,10 +532,10 @@ struct AdamArgs {
 };
 
 // One pass per workgroup: lane c of the grid owns elements [4c, 4c + 4).
-template <typename P>
+template <typename P, bool REC>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
   P* __restrict__ param = static_cast<P*>(a.param);
-  const AdamScalars sc = a.scp ? *a.scp : a.sc;
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t e0 = c * kEPL;
   if (e0 >= a.n) return;
@@ -598,9 +613,9 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs<ptr_ca
       });
 }
 
-template <typename G, typename P, int RT>
+template <typename G, typename P, int RT, bool REC>
 __device__ __forceinline__ void fused_wg(const Work& w, const FusedArgs<ptr_cap(RT)>& a) {
-  const AdamScalars sc = a.scp ? *a.scp : a.sc;
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
   const int k = static_cast<int>((((w.src - w.dst) % kEPL) + kEPL) % kEPL);
   if (w.src < 0)
     fused_item<G, P, RT, true, false>(w, a, sc, 0);
@@ -610,10 +625,10 @@ __device__ __forceinline__ void fused_wg(const Work& w, const FusedArgs<ptr_cap(
     fused_item<G, P, RT, false, true>(w, a, sc, k);
 }
 
-template <typename G, typename P, int RT>
+template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work,
                                                     FusedArgs<ptr_cap(RT)> a) {
-  fused_wg<G, P, RT>(work[blockIdx.x], a);
+  fused_wg<G, P, RT, REC>(work[blockIdx.x], a);
 }
 
 // The fused step of one unit and the gather of another in one launch:
@@ -622,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ wor
 // gather starts while the step's last workgroups drain instead of after
 // them.  wide: 16-byte gather lanes (else 8).  The gather copies the
 // parameter dtype P.
-template <typename G, typename P, int RT>
+template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restrict__ fwork,
                                                            FusedArgs<ptr_cap(RT)> fa,
                                                            int n_fused,
@@ -630,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restric
                                                            CopyArgs<ptr_cap(RT)> ca, int wide) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < n_fused) {
-    fused_wg<G, P, RT>(fwork[b], fa);
+    fused_wg<G, P, RT, REC>(fwork[b], fa);
     return;
   }
   const int i = b - n_fused;
@@ -784,34 +799,52 @@ const void* pick_allreduce(int R) {
   }
 }
 
-template <typename G, typename P>
+template <typename G, typename P, bool REC>
 const void* pick_fused(int R) {
   switch (R) {
-    case 1: return reinterpret_cast<const void*>(&k_fused<G, P, 1>);
-    case 2: return reinterpret_cast<const void*>(&k_fused<G, P, 2>);
-    case 3: return reinterpret_cast<const void*>(&k_fused<G, P, 3>);
-    case 4: return reinterpret_cast<const void*>(&k_fused<G, P, 4>);
-    case 5: return reinterpret_cast<const void*>(&k_fused<G, P, 5>);
-    case 6: return reinterpret_cast<const void*>(&k_fused<G, P, 6>);
-    case 7: return reinterpret_cast<const void*>(&k_fused<G, P, 7>);
-    case 8: return reinterpret_cast<const void*>(&k_fused<G, P, 8>);
-    default: return reinterpret_cast<const void*>(&k_fused<G, P, 0>);
+    case 1: return reinterpret_cast<const void*>(&k_fused<G, P, 1, REC>);
+    case 2: return reinterpret_cast<const void*>(&k_fused<G, P, 2, REC>);
+    case 3: return reinterpret_cast<const void*>(&k_fused<G, P, 3, REC>);
+    case 4: return reinterpret_cast<const void*>(&k_fused<G, P, 4, REC>);
+    case 5: return reinterpret_cast<const void*>(&k_fused<G, P, 5, REC>);
+    case 6: return reinterpret_cast<const void*>(&k_fused<G, P, 6, REC>);
+    case 7: return reinterpret_cast<const void*>(&k_fused<G, P, 7, REC>);
+    case 8: return reinterpret_cast<const void*>(&k_fused<G, P, 8, REC>);
+    default: return reinterpret_cast<const void*>(&k_fused<G, P, 0, REC>);
   }
 }
 
-template <typename G, typename P>
+template <typename G, typename P, bool REC>
 const void* pick_fused_gather(int R) {
   switch (R) {
-    case 1: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 1>);
-    case 2: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 2>);
-    case 3: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 3>);
-    case 4: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 4>);
-    case 5: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 5>);
-    case 6: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 6>);
-    case 7: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 7>);
-    case 8: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 8>);
-    default: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 0>);
+    case 1: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 1, REC>);
+    case 2: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 2, REC>);
+    case 3: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 3, REC>);
+    case 4: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 4, REC>);
+    case 5: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 5, REC>);
+    case 6: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 6, REC>);
+    case 7: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 7, REC>);
+    case 8: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 8, REC>);
+    default: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 0, REC>);
   }
+}
+
+// The fused kernel (or the fused step + gather kernel) for the dtypes, R
+// and the scalars' source.
+template <bool REC>
+const void* fused_fn(int grad_dt, int param_dt, int R) {
+  if (grad_dt == FSDP_BF16)
+    return param_dt == FSDP_BF16 ? pick_fused<u16, u16, REC>(R) : pick_fused<u16, float, REC>(R);
+  return param_dt == FSDP_BF16 ? pick_fused<float, u16, REC>(R) : pick_fused<float, float, REC>(R);
+}
+
+template <bool REC>
+const void* fused_gather_fn(int grad_dt, int param_dt, int R) {
+  if (grad_dt == FSDP_BF16)
+    return param_dt == FSDP_BF16 ? pick_fused_gather<u16, u16, REC>(R)
+                                 : pick_fused_gather<u16, float, REC>(R);
+  return param_dt == FSDP_BF16 ? pick_fused_gather<float, u16, REC>(R)
+                               : pick_fused_gather<float, float, REC>(R);
 }
 
 }  // namespace
@@ -869,8 +902,11 @@ hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, floa
   const int64_t chunks = (n + kEPL - 1) / kEPL;
   const int64_t blocks = (chunks + kThreads - 1) / kThreads;
   if (blocks > kMaxBlocks) return hipErrorInvalidValue;
-  const void* fn = param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16>)
-                                         : reinterpret_cast<const void*>(&k_adamw<float>);
+  const void* fn =
+      scp ? (param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, true>)
+                                   : reinterpret_cast<const void*>(&k_adamw<float, true>))
+          : (param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, false>)
+                                   : reinterpret_cast<const void*>(&k_adamw<float, false>));
   void* args[] = {&a};
   return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
                        adamw_lds(blocks));
@@ -880,11 +916,8 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
                         int grad_dt, float* master, float* m, float* v, void* param,
                         int param_dt, const AdamScalars& sc, const AdamScalars* scp,
                         bool vec, const Sink& stream) {
-  const void* fn;
-  if (grad_dt == FSDP_BF16)
-    fn = param_dt == FSDP_BF16 ? pick_fused<u16, u16>(R) : pick_fused<u16, float>(R);
-  else
-    fn = param_dt == FSDP_BF16 ? pick_fused<float, u16>(R) : pick_fused<float, float>(R);
+  const void* fn = scp ? fused_fn<true>(grad_dt, param_dt, R)
+                       : fused_fn<false>(grad_dt, param_dt, R);
   if (R <= kSmallPtrs) {
     FusedArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), master, m, v, param, sc, scp, R,
                             vec ? 1 : 0};
@@ -975,12 +1008,8 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
   if (n_fused + n_gather > kMaxBlocks) return hipErrorInvalidValue;
   int nf = static_cast<int>(n_fused);
   int wide = lane_bytes == 16 ? 1 : 0;
-  const void* fn;
-  if (grad_dt == FSDP_BF16)
-    fn = param_dt == FSDP_BF16 ? pick_fused_gather<u16, u16>(R) : pick_fused_gather<u16, float>(R);
-  else
-    fn = param_dt == FSDP_BF16 ? pick_fused_gather<float, u16>(R)
-                               : pick_fused_gather<float, float>(R);
+  const void* fn = scp ? fused_gather_fn<true>(grad_dt, param_dt, R)
+                       : fused_gather_fn<false>(grad_dt, param_dt, R);
   const dim3 grid(static_cast<unsigned>(n_fused + n_gather));
   if (R <= kSmallPtrs) {   // the specialised kernel: 8 slots for both arrays
     if (n_dst > kSmallPtrs) return hipErrorInvalidValue;
