@@ -1,5 +1,5 @@
 """FSDP data-parallel hot path on one MI355X (gfx950): a C-ABI HIP library
-(libfsdp_hip.so, declared in include/fsdp_hip.h) and its ctypes binding.
+(libfsdp_mi355x.so, declared in include/fsdp_mi355x.h) and its ctypes binding.
 
 The binding exposes the library's calls under the same names:
 fsdp_plan_layout, fsdp_shard_pack, fsdp_gather_unflatten,

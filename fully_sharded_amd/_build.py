@@ -1,4 +1,4 @@
-"""Build the HIP library in-tree: hipcc for gfx950 -> fully_sharded_amd/libfsdp_hip.so.
+"""Build the HIP library in-tree: hipcc for gfx950 -> fully_sharded_amd/libfsdp_mi355x.so.
 
 Run ``python -m fully_sharded_amd._build`` (or ``__graft_entry__.build()``).
 It compiles every time it is called.
@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB = os.path.join(PKG, "libfsdp_hip.so")
+LIB = os.path.join(PKG, "libfsdp_mi355x.so")
 SOURCES = ["plan.cpp", "kernels.hip", "abi.cpp", "graph.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -68,7 +68,7 @@ C_DRIVER = os.path.join(ROOT, "tests", "c", "step_from_c")
 def build_c_driver(verbose: bool = True) -> str:
     tmp = C_DRIVER + ".tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
-           "-I", "/opt/rocm/include", C_DRIVER_SRC, "-o", tmp, "-L", PKG, "-lfsdp_hip",
+           "-I", "/opt/rocm/include", C_DRIVER_SRC, "-o", tmp, "-L", PKG, "-lfsdp_mi355x",
            "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../fully_sharded_amd",
            "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:

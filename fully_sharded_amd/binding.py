@@ -1,4 +1,4 @@
-"""Thin ctypes binding of libfsdp_hip.so, with the C ABI's names.
+"""Thin ctypes binding of libfsdp_mi355x.so, with the C ABI's names.
 
 Only argument marshalling happens here: torch tensors become device
 pointers and torch's current HIP stream becomes the stream argument.  Every
@@ -15,7 +15,7 @@ import sys
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfsdp_hip.so")
+LIB_PATH = os.path.join(_HERE, "libfsdp_mi355x.so")
 
 PER_PARAM = 0
 FLAT = 1
@@ -46,7 +46,7 @@ class PlanInfo(ctypes.Structure):
 
 _lib = None
 
-# name -> (restype, argtypes); mirrors include/fsdp_hip.h
+# name -> (restype, argtypes); mirrors include/fsdp_mi355x.h
 _SIGS = {
     "fsdp_plan_layout": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,

@@ -1,6 +1,6 @@
 // extern "C" boundary of the FSDP hot-path library: argument checks, then
 // one kernel launch per call on the caller's stream.  Declarations and the
-// contract of every entry point are in include/fsdp_hip.h.
+// contract of every entry point are in include/fsdp_mi355x.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -8,7 +8,7 @@
 #include <new>
 #include <vector>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 #include "kernels.hpp"
 #include "ops.hpp"
 #include "plan.hpp"

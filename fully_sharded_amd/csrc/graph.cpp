@@ -13,7 +13,7 @@
 
 #include <new>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 #include "kernels.hpp"
 #include "ops.hpp"
 #include "plan.hpp"

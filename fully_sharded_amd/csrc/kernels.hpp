@@ -5,7 +5,7 @@
 
 #include <cstdint>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 #include "plan.hpp"
 
 namespace fsdp {

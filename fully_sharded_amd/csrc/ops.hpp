@@ -4,7 +4,7 @@
 
 #include <new>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 #include "kernels.hpp"
 #include "plan.hpp"
 

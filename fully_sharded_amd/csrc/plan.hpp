@@ -9,7 +9,7 @@
 #include <mutex>
 #include <vector>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 
 namespace fsdp {
 

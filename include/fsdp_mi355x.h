@@ -1,5 +1,5 @@
 /*
- * fsdp_hip.h -- C ABI of the FSDP data-parallel hot path on one MI355X
+ * fsdp_mi355x.h -- C ABI of the FSDP data-parallel hot path on one MI355X
  * (gfx950), with R virtual ranks held in one GPU's memory.
  *
  * A training step of fully sharded data parallelism, per FSDP unit, is:
@@ -58,8 +58,8 @@
  *   policy: bf16 parameters, float32 reduction).  The bf16 recast rounds to
  *   nearest, ties to even.
  */
-#ifndef FSDP_HIP_H
-#define FSDP_HIP_H
+#ifndef FSDP_MI355X_H
+#define FSDP_MI355X_H
 
 #include <stdint.h>
 
@@ -368,4 +368,4 @@ const char* fsdp_status_string(fsdp_status status);
 }
 #endif
 
-#endif /* FSDP_HIP_H */
+#endif /* FSDP_MI355X_H */

@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <stdint.h>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 
 int main(void) {
   const int32_t ndims[6] = {2, 2, 2, 2, 2, 2};

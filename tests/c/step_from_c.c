@@ -20,7 +20,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "fsdp_hip.h"
+#include "fsdp_mi355x.h"
 
 static int fail(const char* what, const char* why) {
   fprintf(stderr, "step_from_c: %s: %s\n", what, why);

@@ -1,5 +1,5 @@
 """Host-side checks of the C-ABI library (no GPU needed): it loads, exports
-every function include/fsdp_hip.h declares, and its shapes-only plan agrees
+every function include/fsdp_mi355x.h declares, and its shapes-only plan agrees
 with the oracle's independently written layout."""
 
 import ctypes
@@ -15,7 +15,7 @@ from oracle import fsdp_oracle as O
 from workloads.configs import WORKLOADS, shapes_of
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fsdp_hip.h")
+HEADER = os.path.join(ROOT, "include", "fsdp_mi355x.h")
 
 
 def declared_functions():
@@ -233,7 +233,7 @@ def test_resharder_rejects_different_units():
 
 
 def test_header_compiles_as_c99_and_plans_from_plain_c(tmp_path):
-    """A plain C99 program includes include/fsdp_hip.h, links the library and
+    """A plain C99 program includes include/fsdp_mi355x.h, links the library and
     plans the TransformerBlock FlatParameter of the 4-GPU example."""
     import shutil
     gcc = shutil.which("gcc") or shutil.which("cc")
@@ -244,7 +244,7 @@ def test_header_compiles_as_c99_and_plans_from_plain_c(tmp_path):
     subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic",
                     "-I", os.path.join(ROOT, "include"),
                     os.path.join(ROOT, "tests", "c", "abi_check.c"), "-o", str(exe),
-                    "-L", libdir, "-l:libfsdp_hip.so", "-Wl,-rpath," + libdir], check=True)
+                    "-L", libdir, "-l:libfsdp_mi355x.so", "-Wl,-rpath," + libdir], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
     assert out[0] == "T 3145728 S 786432 R 4 segments 4"
     assert out[1:5] == ["offset 0", "offset 786432", "offset 1572864", "offset 2359296"]
