@@ -306,10 +306,23 @@ __device__ __forceinline__ AdamScalars scalars_of(const AdamScalars& own,
 
 // ------------------------------------------------------------------ copy
 // Bit copy, W bytes per lane (W/ES elements), from one source to up to R
-// destinations.  With several destinations each workgroup starts its
-// round of stores at a different one (rotation by workgroup), which spreads
-// the concurrent stores over the destinations: +10% for 8-byte lanes on a
-// 100M-element gather, neutral at 16 bytes.
+// destinations.  Each workgroup starts its round of stores at a different
+// destination (rotation by workgroup), which spreads the concurrent stores
+// over the destinations: +10% for 8-byte lanes on a 100M-element gather.
+// The loop waits for each destination's pointer, and then for the previous
+// store, before the next store: a wave keeps one store in flight, which on
+// large gathers is faster than issuing all stores back to back.  With
+// 16-byte lanes and exactly 8 destinations (a gather at R = 8 of a unit of
+// up to 12.6M elements, alone or in the step-and-gather launch) a separate
+// instance unrolls the 8 stores in destination order, still one in flight
+// per wave: on the 12-layer model's 3.1M-element units the gather took
+// 9.63 instead of 10.45 us, the step-and-gather launch 31.9 instead of
+// 33.1 us and the whole step 385.2 instead of 398.6 us (alternating runs on
+// one machine).  Unrolling for any count from 2 to 8 behind a switch
+// (gather 11.3 us), or with the stores back to back after one explicit wait
+// (11.9 us), was slower; so was the unrolled code in the same instance as
+// the single-destination copy, whose scalar registers it raised from 45 to
+// 78 (fp32 pack 3% slower).
 template <int ES>
 struct Raw;
 template <>
@@ -344,9 +357,21 @@ struct CopyArgs {
   int vec;
 };
 
+// v to element e0 of destinations 0..ND-1 (NULL ones skipped), unrolled.
+template <int ND, int ES, int W, typename V, int N_>
+__device__ __forceinline__ void store_each(const CopyArgs<N_>& a, int64_t e0, const V& v) {
+  using E = typename Raw<ES>::E;
+#pragma unroll
+  for (int r = 0; r < ND; ++r) {
+    E* d = static_cast<E*>(const_cast<void*>(a.dst.p[r]));
+    if (d) Lane<W>::store(d + e0, v);
+  }
+}
+
 // One work item of the copy; wg numbers the item (it picks the first
-// destination of the rotation).
-template <int ES, int W, int N_>
+// destination of the rotation).  UNROLL: the unrolled stores for exactly 8
+// destinations (16-byte lanes, 8 pointer slots).
+template <int ES, int W, int N_, bool UNROLL = false>
 __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, unsigned wg) {
   using E = typename Raw<ES>::E;
   using V = typename Lane<W>::V;
@@ -374,10 +399,18 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, 
             v = ld16_shifted(al, k * ES);
         }
       }
-      for (int i = 0, r = first; i < a.n_dst; ++i, r = r + 1 == a.n_dst ? 0 : r + 1) {
-        E* d = static_cast<E*>(const_cast<void*>(a.dst.p[r]));
-        if (d) Lane<W>::store(d + e0, v);
+      bool stored = false;
+      if constexpr (UNROLL && W == 16 && N_ == kSmallPtrs) {
+        if (a.n_dst == kSmallPtrs) {  // 8 receivers: unrolled, in receiver order
+          store_each<kSmallPtrs, ES, W>(a, e0, v);
+          stored = true;
+        }
       }
+      if (!stored)
+        for (int i = 0, r = first; i < a.n_dst; ++i, r = r + 1 == a.n_dst ? 0 : r + 1) {
+          E* d = static_cast<E*>(const_cast<void*>(a.dst.p[r]));
+          if (d) Lane<W>::store(d + e0, v);
+        }
     } else {
       const int64_t lo = e0 > w.dst ? e0 : w.dst;
       const int64_t hi = e0 + N < end ? e0 + N : end;
@@ -392,10 +425,10 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, 
   }
 }
 
-template <int ES, int W, int N>
+template <int ES, int W, int N, bool UNROLL = false>
 __global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work,
                                                    CopyArgs<N> a) {
-  copy_item<ES, W>(work[blockIdx.x], a, blockIdx.x);
+  copy_item<ES, W, N, UNROLL>(work[blockIdx.x], a, blockIdx.x);
 }
 
 // The same copy for up to 64 independent (source, destination) pairs that
@@ -651,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restric
   }
   const int i = b - n_fused;
   if (wide)
-    copy_item<sizeof(P), 16>(gwork[i], ca, static_cast<unsigned>(i));
+    copy_item<sizeof(P), 16, ptr_cap(RT), true>(gwork[i], ca, static_cast<unsigned>(i));
   else
     copy_item<sizeof(P), 8>(gwork[i], ca, static_cast<unsigned>(i));
 }
@@ -863,10 +896,14 @@ hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const 
   const bool wide = lane_bytes != 8;
   if (n_dst <= kSmallPtrs) {
     CopyArgs<kSmallPtrs> a{src, narrow<kSmallPtrs>(dst), n_dst, vec ? 1 : 0};
-    const void* fn = es == 2 ? (wide ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs>)
-                                     : reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs>))
-                             : (wide ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs>)
-                                     : reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs>));
+    const bool unroll = wide && n_dst == kSmallPtrs;
+    const void* fn =
+        es == 2 ? (unroll ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs, true>)
+                   : wide ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs>)
+                          : reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs>))
+                : (unroll ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs, true>)
+                   : wide ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs>)
+                          : reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs>));
     return launch_work(fn, work, n_work, a, stream);
   }
   CopyArgs<FSDP_MAX_RANKS> a{src, narrow<FSDP_MAX_RANKS>(dst), n_dst, vec ? 1 : 0};
