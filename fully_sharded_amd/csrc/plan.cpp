@@ -169,7 +169,8 @@ fsdp_status build_plan(fsdp_plan* pl) {
     expect += s.len;
   }
   if (expect != pl->T) return FSDP_ERR_INVALID_ARG;
-  pl->gather_lane_bytes = pl->T <= kWideGatherMax ? 16 : 8;
+  pl->gather_lane_bytes =
+      pl->T <= kWideGatherMax || (R == 8 && pl->T <= kWideGatherMaxR8) ? 16 : 8;
   const int64_t flat_chunk = pl->gather_lane_bytes == 16 ? kFlatChunk : kFlatChunk / 2;
   if (count_items(pl->flat_runs, flat_chunk) > kMaxItems) return FSDP_ERR_UNSUPPORTED;
   emit_items(pl->flat_runs, flat_chunk, pl->flat_work.host);

@@ -101,6 +101,16 @@ constexpr int64_t kFlatChunk = 2048;
 // 5.26 TB/s at 25M, 4.96 vs 5.68 at 100M).
 constexpr int64_t kWideGatherMax = 12582912;
 
+// At R = 8 the 16-byte gather stores its 8 receivers from an unrolled
+// sequence, which keeps 16-byte lanes ahead further: up to this many
+// elements per unit.  Measured against 8-byte lanes (alternating runs on
+// one machine): the 12-layer model as 4-block units (12.6M elements)
+// gather 42.3 -> 40.1 us and step 393.6 -> 386.3 us (serial), 403.8 ->
+// 385.2 us (overlap, which then pairs each step with the next gather); as
+// one unit (37.8M) gather 129.3 -> 126.2 us.  Larger units keep 8-byte
+// lanes (untested with the unrolled stores).
+constexpr int64_t kWideGatherMaxR8 = 41943040;
+
 // A launch covers at most 2^32 - 1 lanes along x: 16,777,215 workgroups of
 // 256 lanes.  A plan (or re-shard) whose work table would need more items
 // than that is refused with FSDP_ERR_UNSUPPORTED.  The shard space holds at

@@ -528,19 +528,21 @@ def test_group4096_flat_r8_full_size_sampled():
         banner(f"group4096 step {t} ok")
 
 
+@pytest.mark.parametrize("R", [3, 8])
 @pytest.mark.parametrize("layout", ["per_param", "flat"])
-def test_wide_unit_gather_with_misaligned_ranks(layout):
-    """A unit above 12.6M elements (the gather's 8-byte-lane regime); per
-    parameter at R=3 its shard length is odd, so ranks 1 and 2 read
-    misaligned sources.  Gather and pack bit-exact, bf16 and fp32."""
+def test_wide_unit_gather_with_misaligned_ranks(layout, R):
+    """A unit above 12.6M elements: at R=3 the gather's 8-byte-lane regime,
+    at R=8 its 16-byte lanes with the 8 receivers' stores unrolled (units up
+    to 40M elements).  Per parameter the shard length is odd, so every rank
+    but 0 reads a misaligned source.  Gather and pack bit-exact, bf16 and
+    fp32."""
     shapes = [(4099, 4099), (10,)]
-    R = 3
     po = O.plan_layout(shapes, R, layout)
     pg = F.Plan(shapes, R, layout)
-    assert po.T > 12582912
+    assert 12582912 < po.T <= 41943040
     if layout == "per_param":
-        assert po.S % 4 != 0      # ranks 1 and 2 misaligned for 4-element lanes
-    banner(f"wide gather {layout}: T={po.T} S={po.S}")
+        assert po.S % 4 != 0      # ranks after 0 misaligned for 4-element lanes
+    banner(f"wide gather {layout} R={R}: T={po.T} S={po.S}")
     rng = np.random.default_rng(99)
     for dt in ("bf16", "f32"):
         full = rng.standard_normal(po.T).astype(np.float32)
