@@ -312,13 +312,13 @@ __device__ __forceinline__ AdamScalars scalars_of(const AdamScalars& own,
 // The loop waits for each destination's pointer, and then for the previous
 // store, before the next store: a wave keeps one store in flight, which on
 // large gathers is faster than issuing all stores back to back.  With
-// 16-byte lanes and exactly 8 destinations (a gather at R = 8 of a unit of
-// up to 12.6M elements, alone or in the step-and-gather launch) a separate
-// instance unrolls the 8 stores in destination order, still one in flight
-// per wave: on the 12-layer model's 3.1M-element units the gather took
-// 9.63 instead of 10.45 us, the step-and-gather launch 31.9 instead of
-// 33.1 us and the whole step 385.2 instead of 398.6 us (alternating runs on
-// one machine).  Unrolling for any count from 2 to 8 behind a switch
+// exactly 8 destinations (a gather at R = 8, alone or in the step-and-gather
+// launch) a separate instance unrolls the 8 stores in destination order,
+// still one in flight per wave: on the 12-layer model's 3.1M-element units
+// (16-byte lanes) the gather took 9.63 instead of 10.45 us, the
+// step-and-gather launch 31.9 instead of 33.1 us and the whole step 385.2
+// instead of 398.6 us; on the 872M-element group (8-byte lanes) the gather
+// took 2.38-2.61 instead of 2.61-2.74 ms (alternating runs on one machine).  Unrolling for any count from 2 to 8 behind a switch
 // (gather 11.3 us), or with the stores back to back after one explicit wait
 // (11.9 us), was slower; so was the unrolled code in the same instance as
 // the single-destination copy, whose scalar registers it raised from 45 to
@@ -370,7 +370,7 @@ __device__ __forceinline__ void store_each(const CopyArgs<N_>& a, int64_t e0, co
 
 // One work item of the copy; wg numbers the item (it picks the first
 // destination of the rotation).  UNROLL: the unrolled stores for exactly 8
-// destinations (16-byte lanes, 8 pointer slots).
+// destinations (8 pointer slots).
 template <int ES, int W, int N_, bool UNROLL = false>
 __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, unsigned wg) {
   using E = typename Raw<ES>::E;
@@ -400,7 +400,7 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, 
         }
       }
       bool stored = false;
-      if constexpr (UNROLL && W == 16 && N_ == kSmallPtrs) {
+      if constexpr (UNROLL && N_ == kSmallPtrs) {
         if (a.n_dst == kSmallPtrs) {  // 8 receivers: unrolled, in receiver order
           store_each<kSmallPtrs, ES, W>(a, e0, v);
           stored = true;
@@ -896,14 +896,16 @@ hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const 
   const bool wide = lane_bytes != 8;
   if (n_dst <= kSmallPtrs) {
     CopyArgs<kSmallPtrs> a{src, narrow<kSmallPtrs>(dst), n_dst, vec ? 1 : 0};
-    const bool unroll = wide && n_dst == kSmallPtrs;
+    const bool unroll = n_dst == kSmallPtrs;
     const void* fn =
-        es == 2 ? (unroll ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs, true>)
-                   : wide ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs>)
-                          : reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs>))
-                : (unroll ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs, true>)
-                   : wide ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs>)
-                          : reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs>));
+        es == 2 ? (wide ? (unroll ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs, true>)
+                                  : reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs>))
+                        : (unroll ? reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs, true>)
+                                  : reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs>)))
+                : (wide ? (unroll ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs, true>)
+                                  : reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs>))
+                        : (unroll ? reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs, true>)
+                                  : reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs>)));
     return launch_work(fn, work, n_work, a, stream);
   }
   CopyArgs<FSDP_MAX_RANKS> a{src, narrow<FSDP_MAX_RANKS>(dst), n_dst, vec ? 1 : 0};
