@@ -312,13 +312,15 @@ __device__ __forceinline__ AdamScalars scalars_of(const AdamScalars& own,
 // The loop waits for each destination's pointer, and then for the previous
 // store, before the next store: a wave keeps one store in flight, which on
 // large gathers is faster than issuing all stores back to back.  With
-// exactly 8 destinations (a gather at R = 8, alone or in the step-and-gather
-// launch) a separate instance unrolls the 8 stores in destination order,
-// still one in flight per wave: on the 12-layer model's 3.1M-element units
+// exactly 4 or 8 destinations (a gather at R = 4 or 8; in the
+// step-and-gather launch at R = 8) separate instances unroll the stores in
+// destination order, still one in flight per wave: on the 12-layer model's 3.1M-element units
 // (16-byte lanes) the gather took 9.63 instead of 10.45 us, the
 // step-and-gather launch 31.9 instead of 33.1 us and the whole step 385.2
 // instead of 398.6 us; on the 872M-element group (8-byte lanes) the gather
-// took 2.38-2.61 instead of 2.61-2.74 ms (alternating runs on one machine).  Unrolling for any count from 2 to 8 behind a switch
+// took 2.38-2.61 instead of 2.61-2.74 ms; on the hidden-512 block at R = 4
+// the gather took 6.5-7.0 instead of 7.1-8.1 us (alternating runs on one
+// machine).  Unrolling for any count from 2 to 8 behind a switch
 // (gather 11.3 us), or with the stores back to back after one explicit wait
 // (11.9 us), was slower; so was the unrolled code in the same instance as
 // the single-destination copy, whose scalar registers it raised from 45 to
@@ -369,9 +371,9 @@ __device__ __forceinline__ void store_each(const CopyArgs<N_>& a, int64_t e0, co
 }
 
 // One work item of the copy; wg numbers the item (it picks the first
-// destination of the rotation).  UNROLL: the unrolled stores for exactly 8
-// destinations (8 pointer slots).
-template <int ES, int W, int N_, bool UNROLL = false>
+// destination of the rotation).  UNROLL > 0: the unrolled stores for
+// exactly that many destinations (8 pointer slots); 0: the loop.
+template <int ES, int W, int N_, int UNROLL = 0>
 __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, unsigned wg) {
   using E = typename Raw<ES>::E;
   using V = typename Lane<W>::V;
@@ -400,9 +402,9 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, 
         }
       }
       bool stored = false;
-      if constexpr (UNROLL && N_ == kSmallPtrs) {
-        if (a.n_dst == kSmallPtrs) {  // 8 receivers: unrolled, in receiver order
-          store_each<kSmallPtrs, ES, W>(a, e0, v);
+      if constexpr (UNROLL > 0 && N_ == kSmallPtrs) {
+        if (a.n_dst == UNROLL) {  // UNROLL receivers: unrolled, in receiver order
+          store_each<UNROLL, ES, W>(a, e0, v);
           stored = true;
         }
       }
@@ -425,7 +427,7 @@ __device__ __forceinline__ void copy_item(const Work& w, const CopyArgs<N_>& a, 
   }
 }
 
-template <int ES, int W, int N, bool UNROLL = false>
+template <int ES, int W, int N, int UNROLL = 0>
 __global__ __launch_bounds__(kThreads) void k_copy(const Work* __restrict__ work,
                                                    CopyArgs<N> a) {
   copy_item<ES, W, N, UNROLL>(work[blockIdx.x], a, blockIdx.x);
@@ -684,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restric
   }
   const int i = b - n_fused;
   if (wide)
-    copy_item<sizeof(P), 16, ptr_cap(RT), true>(gwork[i], ca, static_cast<unsigned>(i));
+    copy_item<sizeof(P), 16, ptr_cap(RT), kSmallPtrs>(gwork[i], ca, static_cast<unsigned>(i));
   else
     copy_item<sizeof(P), 8>(gwork[i], ca, static_cast<unsigned>(i));
 }
@@ -888,6 +890,17 @@ const void* fused_gather_fn(int grad_dt, int param_dt, int R) {
                                : pick_fused_gather<float, float, REC>(R);
 }
 
+// The copy kernel for up to 8 destinations: the unrolled instance for 4 or
+// 8 of them, the loop otherwise.
+template <int ES, int W>
+const void* copy_fn(int n_dst) {
+  switch (n_dst) {
+    case 4: return reinterpret_cast<const void*>(&k_copy<ES, W, kSmallPtrs, 4>);
+    case 8: return reinterpret_cast<const void*>(&k_copy<ES, W, kSmallPtrs, 8>);
+    default: return reinterpret_cast<const void*>(&k_copy<ES, W, kSmallPtrs, 0>);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const PtrArray& dst,
@@ -896,16 +909,8 @@ hipError_t launch_copy(const Work* work, int64_t n_work, const void* src, const 
   const bool wide = lane_bytes != 8;
   if (n_dst <= kSmallPtrs) {
     CopyArgs<kSmallPtrs> a{src, narrow<kSmallPtrs>(dst), n_dst, vec ? 1 : 0};
-    const bool unroll = n_dst == kSmallPtrs;
-    const void* fn =
-        es == 2 ? (wide ? (unroll ? reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs, true>)
-                                  : reinterpret_cast<const void*>(&k_copy<2, 16, kSmallPtrs>))
-                        : (unroll ? reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs, true>)
-                                  : reinterpret_cast<const void*>(&k_copy<2, 8, kSmallPtrs>)))
-                : (wide ? (unroll ? reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs, true>)
-                                  : reinterpret_cast<const void*>(&k_copy<4, 16, kSmallPtrs>))
-                        : (unroll ? reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs, true>)
-                                  : reinterpret_cast<const void*>(&k_copy<4, 8, kSmallPtrs>)));
+    const void* fn = es == 2 ? (wide ? copy_fn<2, 16>(n_dst) : copy_fn<2, 8>(n_dst))
+                             : (wide ? copy_fn<4, 16>(n_dst) : copy_fn<4, 8>(n_dst));
     return launch_work(fn, work, n_work, a, stream);
   }
   CopyArgs<FSDP_MAX_RANKS> a{src, narrow<FSDP_MAX_RANKS>(dst), n_dst, vec ? 1 : 0};
