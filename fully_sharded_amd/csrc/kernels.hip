@@ -17,9 +17,9 @@
 //     funnel each lane's window out of two aligned vector loads; lanes
 //     whose chunk is cut by the ends of the range take an element-by-element
 //     path with the same arithmetic;
-//   * long fused and unfused AdamW launches, and all-reduce launches of any
-//     length, cap their resident workgroups per CU (fused_lds, adamw_lds,
-//     kAllreduceLds), and a short fused step can share its
+//   * long fused, unfused AdamW and all-reduce launches cap their resident
+//     workgroups per CU (fused_lds, adamw_lds, allreduce_lds), and a short
+//     fused step can share its
 //     launch with the next unit's gather (k_fused_gather), which then
 //     starts while the step drains.
 //
@@ -358,6 +358,11 @@ struct CopyArgs {
   int n_dst;
   int vec;
 };
+
+// s_waitcnt operand: vector memory counter 0, the export and LGKM counters
+// not waited for (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 // v to element e0 of destinations 0..ND-1 (NULL ones skipped), unrolled.
 template <int ND, int ES, int W, typename V, int N_>
@@ -749,8 +754,12 @@ __global__ __launch_bounds__(kThreads) void k_allreduce(ArArgs<ptr_cap(RT)> a) {
   if (a.vec && e0 + kEPL <= a.T) {
     float avg[4];
     grad_avg4<G, RT>(a.g, a.R, e0, 0, avg);
-    for (int r = 0; r < R; ++r)
+    // one store in flight per wave: each waits for the one before (the
+    // loaded gradients are consumed by then, so only stores are counted)
+    for (int r = 0; r < R; ++r) {
       Io<O>::store4(static_cast<O*>(const_cast<void*>(a.out.p[r])) + e0, true, avg);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
   } else {
     const int64_t hi = e0 + kEPL < a.T ? e0 + kEPL : a.T;
     for (int64_t e = e0; e < hi; ++e) {
@@ -810,11 +819,14 @@ unsigned fused_lds(int64_t n_work) {
 unsigned adamw_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 32 * 1024; }
 
 // DDP's all-reduce (R gradient replicas read, R averaged copies written per
-// element) takes 3 workgroups per CU at every size.  Alternating A/B runs on
-// MI355X, R = 8, bf16 gradients, fp32 outputs, uncapped -> capped: 3.1M
-// elements (3,073 workgroups) 28.66 -> 27.90 us; 12.6M 121.0 -> 116.2 us;
-// 37.8M 358-366 -> 348-349 us.
-constexpr unsigned kAllreduceLds = 48 * 1024;
+// element) keeps one of its R stores in flight per wave and, above 4,096
+// workgroups, 3 workgroups per CU.  Alternating A/B runs on MI355X, R = 8,
+// bf16 gradients, fp32 outputs: with stores back to back, capping took
+// 3.1M elements (3,073 workgroups) 28.66 -> 27.90 us, 12.6M 121.0 ->
+// 116.2 us, 37.8M 358-366 -> 348-349 us; pacing the stores then took them
+// (capped) to 27.65, 113.3 and 335.3 us, and uncapped to 27.10, 112.5 and
+// 345.5 us.
+unsigned allreduce_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 48 * 1024; }
 
 template <typename G>
 const void* pick_rs(int R) {
@@ -1019,13 +1031,13 @@ hipError_t launch_allreduce(int64_t T, int R, const PtrArray& grads, int grad_dt
     ArArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), narrow<kSmallPtrs>(out), T, R, vec ? 1 : 0};
     void* args[] = {&a};
     return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
-                         kAllreduceLds);
+                         allreduce_lds(blocks));
   }
   ArArgs<FSDP_MAX_RANKS> a{narrow<FSDP_MAX_RANKS>(grads), narrow<FSDP_MAX_RANKS>(out), T, R,
                            vec ? 1 : 0};
   void* args[] = {&a};
   return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
-                       kAllreduceLds);
+                       allreduce_lds(blocks));
 }
 
 hipError_t launch_copy_pairs(const Work* work, int64_t n_work, const PtrArray& src,
