@@ -21,7 +21,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # IEEE fp32: correctly rounded divide and sqrt, denormals kept, no fast-math,
 # no implicit FMA contraction (the kernels write their FMAs explicitly), and
-# no packed-fp32 instructions.
+# no packed-fp32 instructions.  Kernel arguments preloaded into scalar
+# registers at wave launch (gfx950 supports up to 16): a workgroup then
+# reads its work descriptor without first loading the table's address from
+# the argument segment, one memory round trip fewer before its first data
+# load.  The code object keeps the argument loads as a fallback for a
+# command processor that does not preload.  Measured on MI355X, alternating
+# runs: the 12-layer model's step 383.5 -> 381.5 us, its standalone fused
+# step 23.3 -> 23.1 us.
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -31,6 +38,7 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
 ]
 

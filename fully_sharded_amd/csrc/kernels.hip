@@ -214,6 +214,80 @@ struct Io<u16> {
   }
 };
 
+// ------------------------------------------------- one element per lane
+// A second form of the fused step for short launches at R >= 8 gives each
+// lane one element (every access one naturally aligned 2- or 4-byte
+// element, so no alignment case exists) and each 1024-element work item
+// four workgroups.  A wave's float64 arithmetic after its loads return is
+// then a quarter of what it is with four elements per lane, and that
+// arithmetic of the last workgroups is what a short launch waits for at its
+// end.  Measured on MI355X, back-to-back launches on the 12-layer model's
+// 3.1M-element units (R = 8, bf16 gradients): 23.15 against 24.05 us.  With
+// fewer replicas (R = 4, 3), in the launch shared with a gather, in the
+// reduce-scatter and AdamW kernels alone and in long capped launches, four
+// elements per lane were faster (R = 4 block: 21.2 against 22.1 us; the
+// paired launch 31.9 against 32.5 us).
+template <typename T>
+struct One;
+template <>
+struct One<float> {
+  __device__ __forceinline__ static float load(const float* p) {
+    return __builtin_nontemporal_load(p);
+  }
+  __device__ __forceinline__ static void store(float* p, float x) {
+    __builtin_nontemporal_store(x, p);
+  }
+};
+template <>
+struct One<u16> {
+  __device__ __forceinline__ static float load(const u16* p) {
+    return bf16_to_f32(__builtin_nontemporal_load(p));
+  }
+  __device__ __forceinline__ static void store(u16* p, float x) {
+    __builtin_nontemporal_store(static_cast<u16>(f32_to_bf16(x)), p);
+  }
+};
+
+// Workgroups per shard-space work item in the one-element form: item
+// b / kSplit, its elements [(b % kSplit) * 256, + 256).
+constexpr int kSplit = 1024 / kThreads;
+
+// Ask for a value in scalar registers here.  Placed at the top of a kernel
+// for the work descriptor and the data pointers, it makes the compiler issue
+// all of their scalar loads in one round after the kernel arguments', where
+// it otherwise loads the descriptor's length, tests it, and only then loads
+// its offsets and the pointers: one more memory round trip before the first
+// data load of every workgroup (the one-element fused step was 0.1-0.2 us
+// faster per 3.1M-element launch with it).  An empty asm statement: no
+// instruction is emitted.
+template <typename T>
+__device__ __forceinline__ void in_sgprs(const T& x) {
+  asm volatile("" ::"s"(x));
+}
+__device__ __forceinline__ void in_sgprs(const Work& w) {
+  asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len));
+}
+
+// (g_0[s] + g_1[s] + ... + g_{R-1}[s]) / R, fp32, left to right, every
+// load issued before the first add.
+template <typename G, int RT, typename PA>
+__device__ __forceinline__ float grad_avg_one(const PA& g, int R, int64_t s) {
+  if constexpr (RT > 0) {
+    float x[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) x[q] = One<G>::load(static_cast<const G*>(g.p[q]) + s);
+    float acc = x[0];
+#pragma unroll
+    for (int q = 1; q < RT; ++q) acc = acc + x[q];
+    return acc / static_cast<float>(RT);
+  } else {
+    float acc = One<G>::load(static_cast<const G*>(g.p[0]) + s);
+#pragma unroll 8
+    for (int q = 1; q < R; ++q) acc = acc + One<G>::load(static_cast<const G*>(g.p[q]) + s);
+    return acc / static_cast<float>(R);
+  }
+}
+
 // ------------------------------------------------------ rank-order average
 // avg[k] = (g_0[s+k] + g_1[s+k] + ... + g_{R-1}[s+k]) / R, fp32, left to
 // right.  RT > 0: R known at compile time (all R loads issued before the
@@ -672,6 +746,36 @@ __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ wor
   fused_wg<G, P, RT, REC>(work[blockIdx.x], a);
 }
 
+// The one-element form: part b % kSplit of work item b / kSplit.  master,
+// m and v are loaded, then the R gradient replicas (none for padding, whose
+// gradient is 0), all before the first use.
+template <typename G, typename P, int RT, bool REC>
+__global__ __launch_bounds__(kThreads) void k_fused_one(const Work* __restrict__ work,
+                                                        FusedArgs<ptr_cap(RT)> a) {
+  const Work w = work[blockIdx.x / kSplit];
+  in_sgprs(w);
+  if constexpr (RT > 0) {
+#pragma unroll
+    for (int q = 0; q < RT; ++q) in_sgprs(a.g.p[q]);
+  }
+  in_sgprs(a.master);
+  in_sgprs(a.m);
+  in_sgprs(a.v);
+  in_sgprs(a.param);
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+  const int64_t off = static_cast<int64_t>(blockIdx.x % kSplit) * kThreads + threadIdx.x;
+  if (off >= w.len) return;
+  const int64_t e = w.dst + off;
+  float p = One<float>::load(a.master + e), m = One<float>::load(a.m + e),
+        v = One<float>::load(a.v + e);
+  const float g = w.src < 0 ? 0.0f : grad_avg_one<G, RT>(a.g, a.R, w.src + off);
+  adamw1(g, p, m, v, sc);
+  One<float>::store(a.master + e, p);
+  One<float>::store(a.m + e, m);
+  One<float>::store(a.v + e, v);
+  One<P>::store(static_cast<P*>(a.param) + e, p);
+}
+
 // The fused step of one unit and the gather of another in one launch:
 // workgroups [0, n_fused) take the step's work items, the rest the
 // gather's, in that order.  Dispatch follows the workgroup order, so the
@@ -870,6 +974,25 @@ const void* pick_fused(int R) {
 }
 
 template <typename G, typename P, bool REC>
+const void* pick_fused_one(int R) {
+  return R == 8 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 8, REC>)
+                : reinterpret_cast<const void*>(&k_fused_one<G, P, 0, REC>);
+}
+
+template <bool REC>
+const void* fused_one_fn(int grad_dt, int param_dt, int R) {
+  if (grad_dt == FSDP_BF16)
+    return param_dt == FSDP_BF16 ? pick_fused_one<u16, u16, REC>(R)
+                                 : pick_fused_one<u16, float, REC>(R);
+  return param_dt == FSDP_BF16 ? pick_fused_one<float, u16, REC>(R)
+                               : pick_fused_one<float, float, REC>(R);
+}
+
+// The one-element form runs short standalone fused steps (no workgroup cap)
+// with at least 8 replicas; everything else takes four elements per lane.
+bool fused_one_lane(int64_t n_work, int R) { return R >= 8 && n_work <= kSmallFusedLaunch; }
+
+template <typename G, typename P, bool REC>
 const void* pick_fused_gather(int R) {
   switch (R) {
     case 1: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 1, REC>);
@@ -980,6 +1103,22 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
                         int grad_dt, float* master, float* m, float* v, void* param,
                         int param_dt, const AdamScalars& sc, const AdamScalars* scp,
                         bool vec, const Sink& stream) {
+  if (fused_one_lane(n_work, R)) {
+    if (n_work <= 0) return hipSuccess;
+    if (n_work > kMaxBlocks / kSplit) return hipErrorInvalidValue;
+    const void* fn = scp ? fused_one_fn<true>(grad_dt, param_dt, R)
+                         : fused_one_fn<false>(grad_dt, param_dt, R);
+    const dim3 grid(static_cast<unsigned>(n_work * kSplit));
+    if (R <= kSmallPtrs) {
+      FusedArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), master, m, v, param, sc, scp, R, 1};
+      void* args[] = {const_cast<Work**>(&work), &a};
+      return stream.launch(fn, grid, dim3(kThreads), args, 0);
+    }
+    FusedArgs<FSDP_MAX_RANKS> a{narrow<FSDP_MAX_RANKS>(grads), master, m, v, param, sc, scp, R,
+                                1};
+    void* args[] = {const_cast<Work**>(&work), &a};
+    return stream.launch(fn, grid, dim3(kThreads), args, 0);
+  }
   const void* fn = scp ? fused_fn<true>(grad_dt, param_dt, R)
                        : fused_fn<false>(grad_dt, param_dt, R);
   if (R <= kSmallPtrs) {
