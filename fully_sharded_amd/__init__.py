@@ -14,7 +14,8 @@ kernel touches at one offset do not share HBM channels.
 from .binding import (  # noqa: F401
     BF16, F32, FLAT, PER_PARAM, FsdpError, Plan, Resharder, StepGraph, bind_adamw_shard_step,
     bind_adamw_step_then_gather, bind_gather_unflatten, bind_reduce_scatter_avg, bind_shard_pack,
-    fsdp_adamw_step_then_gather, bind_grad_accumulate, fsdp_adamw_shard_step, fsdp_allreduce_avg,
+    fsdp_adamw_step_then_gather, bind_grad_accumulate, fsdp_adamw_shard_step,
+    fsdp_adamw_shard_step_noalloc, fsdp_allreduce_avg,
     fsdp_gather_unflatten, fsdp_grad_accumulate, fsdp_plan_layout, fsdp_reduce_scatter_avg,
     fsdp_reshard, fsdp_reshard_batch, fsdp_reshard_plan, fsdp_shard_pack, lib,
 )

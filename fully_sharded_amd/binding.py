@@ -74,6 +74,13 @@ _SIGS = {
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_int32, ctypes.c_void_p]),
+    "fsdp_adamw_shard_step_noalloc": (ctypes.c_int, [ctypes.c_void_p,
+                                                     ctypes.POINTER(AdamWHParams), ctypes.c_int64,
+                                                     ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_int32, ctypes.c_void_p]),
     "fsdp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fsdp_plan_work_items": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
@@ -388,12 +395,7 @@ def fsdp_reduce_scatter_avg(plan: Plan, grads, out: torch.Tensor, stream=None):
            lib().fsdp_reduce_scatter_avg(plan.handle, arr, dt, _dev(out, "out"), _stream(stream)))
 
 
-def fsdp_adamw_shard_step(plan: Plan, hp: dict, step: int, grads, master, m, v, param_out,
-                          grads_are_replicas: bool = True, stream=None):
-    """AdamW on the [R, S] fp32 shards (in place) + recast into param_out.
-
-    grads: list of R full-unit replicas [T] (fused reduce-scatter-average) or,
-    with grads_are_replicas=False, one fp32 [R, S] tensor (or a 1-list)."""
+def _adamw_args(plan: Plan, grads, master, m, v, param_out, grads_are_replicas):
     n = plan.R * plan.S
     for t, nm in ((master, "master"), (m, "m"), (v, "v")):
         if t.numel() != n or t.dtype != torch.float32:
@@ -413,13 +415,36 @@ def fsdp_adamw_shard_step(plan: Plan, hp: dict, step: int, grads, master, m, v, 
         if grads[0].numel() != n or grads[0].dtype != torch.float32:
             raise ValueError("reduced gradient must be fp32 [R, S]")
         dt = F32
-    arr = _ptr_array(grads, "grads")
+    return _ptr_array(grads, "grads"), dt
+
+
+def fsdp_adamw_shard_step(plan: Plan, hp: dict, step: int, grads, master, m, v, param_out,
+                          grads_are_replicas: bool = True, stream=None):
+    """AdamW on the [R, S] fp32 shards (in place) + recast into param_out.
+
+    grads: list of R full-unit replicas [T] (fused reduce-scatter-average) or,
+    with grads_are_replicas=False, one fp32 [R, S] tensor (or a 1-list)."""
+    arr, dt = _adamw_args(plan, grads, master, m, v, param_out, grads_are_replicas)
     h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
     _check("fsdp_adamw_shard_step",
            lib().fsdp_adamw_shard_step(plan.handle, ctypes.byref(h), int(step), arr, dt,
                                        int(bool(grads_are_replicas)), _dev(master, "master"),
                                        _dev(m, "m"), _dev(v, "v"), _dev(param_out, "param_out"),
                                        _dtype_code(param_out), _stream(stream)))
+
+
+def fsdp_adamw_shard_step_noalloc(plan: Plan, hp: dict, step: int, grads, master, m, v,
+                                  param_out, grads_are_replicas: bool = True, stream=None):
+    """fsdp_adamw_shard_step through the entry point that allocates no device
+    memory (the plan's work table goes to the library's static buffer)."""
+    arr, dt = _adamw_args(plan, grads, master, m, v, param_out, grads_are_replicas)
+    h = AdamWHParams(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    _check("fsdp_adamw_shard_step_noalloc",
+           lib().fsdp_adamw_shard_step_noalloc(plan.handle, ctypes.byref(h), int(step), arr, dt,
+                                               int(bool(grads_are_replicas)),
+                                               _dev(master, "master"), _dev(m, "m"),
+                                               _dev(v, "v"), _dev(param_out, "param_out"),
+                                               _dtype_code(param_out), _stream(stream)))
 
 
 class BoundCall:

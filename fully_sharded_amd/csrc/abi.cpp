@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -35,7 +36,23 @@ bool overlap(const Range& a, const Range& b) {
   if (a.lo == a.hi || b.lo == b.hi) return false;
   return a.lo < b.hi && b.lo < a.hi;
 }
-bool any_overlap(const std::vector<Range>& rs) {
+// The address ranges one call reads or writes, kept inline: at most 64
+// gradient replicas, receivers or arrays, plus the state arrays.  The
+// argument checks allocate nothing.
+struct Ranges {
+  Range r[FSDP_MAX_RANKS + 8];
+  int n = 0;
+  void push_back(const Range& x) {
+    if (n < FSDP_MAX_RANKS + 8) r[n++] = x;
+  }
+  const Range* begin() const { return r; }
+  const Range* end() const { return r + n; }
+  size_t size() const { return static_cast<size_t>(n); }
+  const Range& operator[](size_t i) const { return r[i]; }
+};
+
+template <typename L>
+bool any_overlap(const L& rs) {
   for (size_t i = 0; i < rs.size(); ++i)
     for (size_t j = i + 1; j < rs.size(); ++j)
       if (overlap(rs[i], rs[j])) return true;
@@ -97,7 +114,7 @@ struct GatherCall {
   int es = 0;
   int lane_bytes = 16;
   bool vec = false;
-  std::vector<Range> reads, writes;
+  Ranges reads, writes;
 };
 
 fsdp_status prep_gather(const fsdp_plan* plan, const void* shards, int32_t dtype,
@@ -116,7 +133,7 @@ fsdp_status prep_gather(const fsdp_plan* plan, const void* shards, int32_t dtype
     c->writes.push_back(range_of(d, plan->T * es));
     ++c->n_dst;
   }
-  std::vector<Range> all = c->writes;
+  Ranges all = c->writes;
   all.push_back(c->reads[0]);
   if (any_overlap(all)) return FSDP_ERR_INVALID_ARG;
   c->plan = plan;
@@ -149,7 +166,7 @@ struct AdamCall {
   bool vec = false;
   const Work* w = nullptr;
   int64_t n_work = 0;
-  std::vector<Range> reads, writes;
+  Ranges reads, writes;
 };
 
 fsdp_status prep_adamw(const fsdp_plan* plan, const void* const* grads, int32_t grad_dtype,
@@ -162,8 +179,10 @@ fsdp_status prep_adamw(const fsdp_plan* plan, const void* const* grads, int32_t 
   const int64_t pes = dtype_size(param_dtype);
   if (!aligned(master, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(param_out, pes))
     return FSDP_ERR_INVALID_ARG;
-  c->writes = {range_of(master, n * 4), range_of(m, n * 4), range_of(v, n * 4),
-               range_of(param_out, n * pes)};
+  c->writes.push_back(range_of(master, n * 4));
+  c->writes.push_back(range_of(m, n * 4));
+  c->writes.push_back(range_of(v, n * 4));
+  c->writes.push_back(range_of(param_out, n * pes));
   c->vec = aligned(master, 16) && aligned(m, 16) && aligned(v, 16) && aligned(param_out, 16);
   if (grads_are_replicas) {
     const int64_t ges = dtype_size(grad_dtype);
@@ -266,6 +285,42 @@ fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
 }
 
 }  // namespace fsdp
+
+// ------------------------------------------ the entry point that allocates
+// fsdp_adamw_shard_step_noalloc keeps the plan's work table in this static
+// device array (one copy per GPU, held until the process ends) instead of
+// device memory the plan allocates.  In host code `scratch` names a
+// host-side stand-in, never the device array: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+namespace {
+constexpr size_t kScratchBytes = size_t(1) << 20;
+constexpr int64_t kScratchItems = static_cast<int64_t>(kScratchBytes / sizeof(Work));
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) Work scratch[kScratchItems];
+
+namespace {
+std::mutex g_scratch_mu;
+Work* g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the
+// first call there (with that device current) and kept.
+fsdp_status scratch_on_current_device(Work** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fsdp::status_of(hipErrorInvalidDevice);
+  if (dev < 0 || dev >= kScratchDevices) return FSDP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fsdp::status_of(e == hipSuccess ? hipErrorUnknown : e);
+    g_scratch_ptr[dev] = static_cast<Work*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return FSDP_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -476,6 +531,38 @@ fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparam
     if (st != FSDP_OK) return st;
     return fsdp::adamw_impl(plan, sc, nullptr, grads, grad_dtype, grads_are_replicas, master, m, v,
                             param_out, param_dtype, fsdp::StreamSink(stream));
+  });
+}
+
+fsdp_status fsdp_adamw_shard_step_noalloc(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
+                                          int64_t step, const void* const* grads,
+                                          int32_t grad_dtype, int32_t grads_are_replicas,
+                                          float* master, float* m, float* v, void* param_out,
+                                          int32_t param_dtype, void* stream) {
+  return fsdp::guarded([&]() -> fsdp_status {
+    if (!plan || !hp) return FSDP_ERR_INVALID_ARG;
+    AdamScalars sc;
+    fsdp_status st = fsdp::adam_scalars(hp, step, &sc);
+    if (st != FSDP_OK) return st;
+    const int64_t n_work = static_cast<int64_t>(plan->shard_work.host.size());
+    if (grads_are_replicas == 1 && n_work > kScratchItems) return FSDP_ERR_UNSUPPORTED;
+    fsdp::AdamCall c;
+    st = fsdp::prep_adamw(plan, grads, grad_dtype, grads_are_replicas, master, m, v, param_out,
+                          param_dtype, &c);
+    if (st != FSDP_OK) return st;
+    if (c.replicas && n_work > 0) {
+      Work* table = nullptr;
+      st = scratch_on_current_device(&table);
+      if (st != FSDP_OK) return st;
+      // the plan's table into the static array, in stream order before the step
+      st = fsdp::status_of(hipMemcpyAsync(table, plan->shard_work.host.data(),
+                                          static_cast<size_t>(n_work) * sizeof(Work),
+                                          hipMemcpyHostToDevice,
+                                          static_cast<hipStream_t>(stream)));
+      if (st != FSDP_OK) return st;
+      c.w = table;
+    }
+    return fsdp::launch(c, sc, nullptr, fsdp::StreamSink(stream));
   });
 }
 

@@ -213,6 +213,28 @@ fsdp_status fsdp_adamw_shard_step(const fsdp_plan* plan, const fsdp_adamw_hparam
                                   int32_t grads_are_replicas, float* master, float* m, float* v,
                                   void* param_out, int32_t param_dtype, void* stream);
 
+/* fsdp_adamw_shard_step for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks and results (bit for bit); the caller
+ * still passes every input and output.  The call allocates nothing: the
+ * plan's work table is copied (hipMemcpyAsync from the plan's host table,
+ * on `stream`, before the step) into a static device buffer of the library
+ * of 1 MiB, one per GPU, held until the process ends, instead of the
+ * device copy the plan otherwise allocates on first use.
+ *   Limit: with grads_are_replicas = 1 the plan's shard-space table must
+ *   hold at most 43,690 work items (fsdp_plan_work_items, space 0: a shard
+ *   space R*S of up to about 44.7M elements); larger plans give
+ *   FSDP_ERR_UNSUPPORTED, checked before the other arguments.
+ *   Every call on one GPU shares that GPU's buffer: calls enqueued on one
+ *   stream are ordered, but calls that can overlap in time on one GPU (on
+ *   different streams or from different threads) race on it.  Its
+ *   contents are the last call's table; nothing in it needs clearing. */
+fsdp_status fsdp_adamw_shard_step_noalloc(const fsdp_plan* plan, const fsdp_adamw_hparams* hp,
+                                          int64_t step, const void* const* grads,
+                                          int32_t grad_dtype, int32_t grads_are_replicas,
+                                          float* master, float* m, float* v, void* param_out,
+                                          int32_t param_dtype, void* stream);
+
 /* ---- Beyond the per-step path: restore at another world size, gradient
  * accumulation, and the DDP all-reduce the pages compare FSDP with. ---- */
 

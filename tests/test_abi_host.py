@@ -377,3 +377,22 @@ def test_c_driver_refuses_bad_input_before_any_device_call(tmp_path):
     (tmp_path / "shape.txt").write_text("2 0 1\n0\n")
     out = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=60)
     assert out.returncode == 1 and "bad ndims" in out.stderr
+
+
+def test_noalloc_step_refuses_a_table_beyond_its_buffer_without_a_device():
+    """The no-allocation AdamW entry point keeps the work table in a 1 MiB
+    static buffer (43,690 items): a larger plan is refused before the other
+    arguments are looked at; a fitting plan goes on to the argument checks."""
+    L = F.lib()
+    h = F.binding.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    arr = (ctypes.c_void_p * 1)(None)
+    big = F.Plan([(50_000_000,)], 1, "flat")
+    assert len(big.work_items(0)) == 48829
+    assert L.fsdp_adamw_shard_step_noalloc(big.handle, ctypes.byref(h), 1, arr, 1, 1,
+                                           None, None, None, None, 1, None) == -2
+    fits = F.Plan([(44_000_000,)], 1, "flat")
+    assert len(fits.work_items(0)) <= 43690
+    assert L.fsdp_adamw_shard_step_noalloc(fits.handle, ctypes.byref(h), 1, arr, 1, 1,
+                                           None, None, None, None, 1, None) == -1
+    assert L.fsdp_adamw_shard_step_noalloc(None, ctypes.byref(h), 1, arr, 1, 1,
+                                           None, None, None, None, 1, None) == -1
