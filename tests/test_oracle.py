@@ -479,6 +479,30 @@ def test_bf16_nan_stays_nan():
     assert np.all(np.isnan(back))
 
 
+def test_bf16_to_f32_over_every_bf16_pattern():
+    """The oracle's bf16 -> fp32 widening on all 65,536 bf16 bit patterns:
+    equal, bit for bit (NaN payloads included), to torch's bfloat16 -> float32
+    conversion (a library routine), and to the value the bf16 fields define
+    on the normal, subnormal, zero and infinite classes:
+    (-1)^s * 2^(e - 127) * (1 + f/128), or 2^-126 * f/128 when e = 0."""
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = O.bf16_to_f32(u)
+    ref = torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(ours.view(np.uint32), ref.view(np.uint32))
+    s = (u >> 15).astype(np.int64)
+    e = ((u >> 7) & 0xFF).astype(np.int64)
+    f = (u & 0x7F).astype(np.int64)
+    fin = e < 0xFF
+    mag = np.where(e > 0, np.ldexp(1.0 + f / 128.0, (e - 127).clip(-126, 127)),
+                   np.ldexp(f / 128.0, -126))
+    want = np.where(s == 1, -mag, mag)
+    np.testing.assert_array_equal(ours[fin].astype(np.float64), want[fin])
+    assert np.all(np.signbit(ours) == (s == 1))
+    inf = (e == 0xFF) & (f == 0)
+    assert np.all(np.isinf(ours[inf])) and np.all(np.isnan(ours[(e == 0xFF) & (f != 0)]))
+    assert ours[0x3F80] == 1.0 and ours[0xC000] == -2.0 and ours[0x0001] == 2.0 ** -133
+
+
 def test_bf16_rne_over_every_fp32_pattern_matches_torch():
     """All 2^32 fp32 bit patterns, in 64 chunks on 8 threads (about 20 s):
     the oracle's recast equals torch's round-to-nearest-even cast (a library
