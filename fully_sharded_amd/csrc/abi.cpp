@@ -720,7 +720,7 @@ fsdp_status fsdp_allreduce_avg(const fsdp_plan* plan, const void* const* grads,
   });
 }
 
-const char* fsdp_status_string(fsdp_status status) {
+const char* fsdp_status_string(int32_t status) {
   switch (status) {
     case FSDP_OK: return "ok";
     case FSDP_ERR_INVALID_ARG: return "invalid argument";

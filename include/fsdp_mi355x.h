@@ -383,8 +383,9 @@ fsdp_status fsdp_step_graph_info(const fsdp_step_graph* graph, int64_t* n_nodes,
  * it (no more nodes).  Must be called on the graph's device. */
 fsdp_status fsdp_step_graph_launch(fsdp_step_graph* graph, int64_t step, void* stream);
 
-/* Static, human-readable name of a status. */
-const char* fsdp_status_string(fsdp_status status);
+/* Static, human-readable name of a status code (an fsdp_status value; any
+ * other number gives "unknown status"). */
+const char* fsdp_status_string(int32_t status);
 
 #ifdef __cplusplus
 }
