@@ -387,8 +387,10 @@ def test_model12_r8_full_step_bench_launch_configuration():
     """The 12-layer R=8 model, 3 steps, in the benchmark's default launch
     configuration: per step the gather of unit 0, then one launch per unit u
     holding u's fused step and unit u+1's gather (two alternating receive
-    buffers), then unit 11's fused step.  Units 0 and 11 are checked whole,
-    the others on sampled elements."""
+    buffers), then unit 11's fused step alone.  Every unit's master, m, v
+    and parameter are checked whole after every step, and every gather
+    (every receiver of every unit, every step) against the oracle's gather
+    of that unit's current parameter, all bit for bit."""
     wl = WORKLOADS["model12_r8"]
     R = wl["R"]
     shapes = shapes_of(wl["units"][0])
@@ -398,10 +400,6 @@ def test_model12_r8_full_step_bench_launch_configuration():
     n_units = len(wl["units"])
     last = n_units - 1
     banner(f"model12_r8: {n_units} units, T={T}, S={S}")
-    rng = np.random.default_rng(12)
-    rs_, js_ = sample_positions(rng, R, S, 4096)
-    fi = flat_index(po, rs_, js_)
-    valid = fi >= 0
     state = []
     oracle = []
     for u in range(n_units):
@@ -417,13 +415,12 @@ def test_model12_r8_full_step_bench_launch_configuration():
             for _ in range(2)]
 
     def check_gather(u, t):
-        """Unit u's receivers hold the gather of its current parameter."""
+        """Every receiver of unit u's buffer holds the gather of u's
+        current parameter (the oracle's, bit for bit)."""
+        torch.cuda.synchronize()
         want, _ = O.gather_unflatten(po, oracle[u][3])
-        got = to_host(recv[u % 2][3])
-        if t == 1:
-            assert_bitexact(got, want, f"gather u={u}")
-        else:
-            assert_bf16_within_ulp(got, want, f"gather u={u}")
+        for r in range(R):
+            assert_bitexact(to_host(recv[u % 2][r]), want, f"gather u={u} t={t} recv {r}")
 
     for t in range(1, wl["steps"] + 1):
         F.fsdp_gather_unflatten(pg, state[0][3], recv[0])
@@ -434,38 +431,79 @@ def test_model12_r8_full_step_bench_launch_configuration():
             if u < last:
                 F.fsdp_adamw_step_then_gather(pg, ADAMW, t, grads, md, m, v, pd, pg,
                                               state[u + 1][3], recv[(u + 1) % 2])
-                if u + 1 == last:
-                    check_gather(last, t)
+                check_gather(u + 1, t)
             else:
                 F.fsdp_adamw_shard_step(pg, ADAMW, t, grads, md, m, v, pd)
             o = oracle[u]
-            if u in (0, last):
-                hg = [to_host(g) for g in grads]
-                o[0], o[1], o[2], o[3] = O.shard_step(po, hg, o[0], o[1], o[2], t, ADAMW, "bf16")
-                gm = to_host(md).reshape(R, S)
-                assert_adamw_close(gm, o[0], f"master u={u} t={t}")
-                assert_adamw_close(to_host(m).reshape(R, S), o[1], f"m u={u}")
-                assert_adamw_close(to_host(v).reshape(R, S), o[2], f"v u={u}")
-                gp = to_host(pd).reshape(R, S)
-                assert_bf16_within_ulp(gp, o[3], f"param u={u}")
-                assert_bitexact(gp, O.bf16_rne(gm), "param = RNE(master)")
-            else:
-                # sampled: the oracle steps only the sampled elements
-                gs = [to_host(g[torch.from_numpy(fi[valid]).to(DEV)]) for g in grads]
-                avg = np.zeros(rs_.shape, np.float32)
-                avg[valid] = O.rank_order_mean(gs)
-                p0, m0, v0 = (o[0][rs_, js_], o[1][rs_, js_], o[2][rs_, js_])
-                p1, m1, v1 = O.adamw_step(p0, m0, v0, avg, t, **ADAMW)
-                o[0][rs_, js_], o[1][rs_, js_], o[2][rs_, js_] = p1, m1, v1
-                idx = torch.from_numpy(rs_ * S + js_).to(DEV)
-                assert_adamw_close(to_host(md[idx]), p1, f"master u={u} sampled")
-                assert_adamw_close(to_host(m[idx]), m1, f"m u={u} sampled")
-                assert_adamw_close(to_host(v[idx]), v1, f"v u={u} sampled")
-                assert_bf16_within_ulp(to_host(pd[idx]), O.bf16_rne(p1), f"param u={u} sampled")
+            hg = [to_host(g) for g in grads]
+            o[0], o[1], o[2], o[3] = O.shard_step(po, hg, o[0], o[1], o[2], t, ADAMW, "bf16")
+            gm = to_host(md).reshape(R, S)
+            assert_adamw_close(gm, o[0], f"master u={u} t={t}")
+            assert_bitexact(gm, o[0], f"master bits u={u} t={t}")
+            assert_bitexact(to_host(m).reshape(R, S), o[1], f"m u={u} t={t}")
+            assert_bitexact(to_host(v).reshape(R, S), o[2], f"v u={u} t={t}")
+            gp = to_host(pd).reshape(R, S)
+            assert_bf16_within_ulp(gp, o[3], f"param u={u} t={t}")
+            assert_bitexact(gp, o[3], f"param bits u={u} t={t}")
         banner(f"model12_r8 step {t} ok")
-    for b in recv:
-        for r in range(1, R):
-            assert torch.equal(b[0].view(torch.int16), b[r].view(torch.int16))
+
+
+def test_group4096_flat_r8_one_step_whole():
+    """One fused step of the 872,448,000-parameter group at R=8 (FSDP1
+    FlatParameter), compared whole with the oracle run chunk by chunk on the
+    host (1 Mi-element slices of the shard space on a thread pool: the
+    oracle's rank-order mean, AdamW step and bf16 recast, element-wise), bit
+    for bit on master, m, v and parameter.  The oracle's input is the
+    FlatParameter's own definition: shard element j of rank r is element
+    r*S + j of the full master."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl = WORKLOADS["group4096_flat_r8"]
+    R = wl["R"]
+    shapes = shapes_of(wl["units"][0])
+    po = O.plan_layout(shapes, R, wl["layout"])
+    pg = F.Plan(shapes, R, wl["layout"])
+    T, S = po.T, po.S
+    assert R * S == T          # no padding at this size
+    banner(f"group4096_flat_r8 whole step: T={T}")
+    full = gen.device_master(wl, 0, shapes, DEV)
+    md = torch.empty(R * S, device=DEV)
+    F.fsdp_shard_pack(pg, full, md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_shard_pack(pg, full, pd)
+    m = torch.zeros_like(md)
+    v = torch.zeros_like(md)
+    grads = [gen.device_grad(wl, 1, 0, r, T, DEV) for r in range(R)]
+    F.fsdp_adamw_shard_step(pg, ADAMW, 1, grads, md, m, v, pd)
+    torch.cuda.synchronize()
+    chunk = 1 << 24
+    sub = 1 << 20
+
+    def oracle_slice(args):
+        g, p0, a, b = args
+        avg = O.rank_order_mean([x[a:b] for x in g])
+        z = np.zeros(b - a, np.float32)
+        p1, m1, v1 = O.adamw_step(p0[a:b], z, z, avg, 1, **ADAMW)
+        return a, p1, m1, v1, O.bf16_rne(p1)
+
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        for lo in range(0, T, chunk):
+            hi = min(T, lo + chunk)
+            g = [to_host(x[lo:hi]) for x in grads]
+            p0 = to_host(full[lo:hi])
+            want_p = np.empty(hi - lo, np.float32)
+            want_m = np.empty_like(want_p)
+            want_v = np.empty_like(want_p)
+            want_q = np.empty(hi - lo, np.uint16)
+            jobs = [(g, p0, a, min(hi - lo, a + sub)) for a in range(0, hi - lo, sub)]
+            for a, p1, m1, v1, q1 in pool.map(oracle_slice, jobs):
+                n = p1.size
+                want_p[a:a + n], want_m[a:a + n], want_v[a:a + n], want_q[a:a + n] = \
+                    p1, m1, v1, q1
+            assert_bitexact(to_host(md[lo:hi]), want_p, f"master [{lo}, {hi})")
+            assert_bitexact(to_host(m[lo:hi]), want_m, f"m [{lo}, {hi})")
+            assert_bitexact(to_host(v[lo:hi]), want_v, f"v [{lo}, {hi})")
+            assert_bitexact(to_host(pd[lo:hi]), want_q, f"param [{lo}, {hi})")
+    banner("group4096 whole step ok")
 
 
 def test_group4096_flat_r8_full_size_sampled():
@@ -558,3 +596,116 @@ def test_wide_unit_gather_with_misaligned_ranks(layout, R):
         want, _ = O.gather_unflatten(po, sh_o)
         for r in range(R):
             assert_bitexact(to_host(recv[r]), want, f"gather {dt} receiver {r}")
+
+
+def two_block_unit():
+    from workloads.configs import BLOCK_512
+    return shapes_of(BLOCK_512) + shapes_of(BLOCK_512)
+
+
+def test_unfused_adamw_above_4096_workgroups_r8():
+    """fsdp_adamw_shard_step with grads_are_replicas=0 (AdamW + recast on the
+    reduce-scatter's fp32 output) on a two-block unit at R = 8: 6,146
+    workgroups, the occupancy-capped launch; checked directly against the
+    oracle's adamw_step of its reduce_scatter_avg, bit for bit, 2 steps."""
+    shapes = two_block_unit()
+    R = 8
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    assert -(-R * S // 1024) > 4096
+    banner(f"unfused AdamW R=8, {R * S} elements")
+    rng = np.random.default_rng(77)
+    master = O.shard_pack(po, rng.uniform(-0.05, 0.05, T).astype(np.float32))
+    md = to_dev(master.reshape(-1))
+    m_d = torch.zeros_like(md)
+    v_d = torch.zeros_like(md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    mo, vo = np.zeros_like(master), np.zeros_like(master)
+    for t in (1, 2):
+        grads = [O.bf16_rne((rng.standard_normal(T) * 1e-3).astype(np.float32))
+                 for _ in range(R)]
+        rs = O.reduce_scatter_avg(po, grads)
+        F.fsdp_adamw_shard_step(pg, ADAMW, t, to_dev(rs.reshape(-1)), md, m_d, v_d, pd,
+                                grads_are_replicas=False)
+        master, mo, vo = O.adamw_step(master, mo, vo, rs, t, **ADAMW)
+        assert_bitexact(to_host(md).reshape(R, S), master, f"master t={t}")
+        assert_bitexact(to_host(m_d).reshape(R, S), mo, f"m t={t}")
+        assert_bitexact(to_host(v_d).reshape(R, S), vo, f"v t={t}")
+        assert_bitexact(to_host(pd).reshape(R, S), O.bf16_rne(master), f"param t={t}")
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+def test_fused_r8_above_4096_items_four_element_form(gdt):
+    """The standalone fused step at R = 8 on a two-block unit (6,146 work
+    items: the four-element kernel with its occupancy cap, where a one-block
+    unit takes the one-element kernel), bit for bit against the oracle, 2
+    steps, bf16 and fp32 gradients."""
+    shapes = two_block_unit()
+    R = 8
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    assert len(pg.work_items(0)) > 4096
+    banner(f"fused R=8 four-element form, {gdt} grads")
+    rng = np.random.default_rng(78)
+    master = O.shard_pack(po, rng.uniform(-0.05, 0.05, T).astype(np.float32))
+    md = to_dev(master.reshape(-1))
+    m_d = torch.zeros_like(md)
+    v_d = torch.zeros_like(md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    mo, vo = np.zeros_like(master), np.zeros_like(master)
+    for t in (1, 2):
+        grads = [(rng.standard_normal(T) * 1e-3).astype(np.float32) for _ in range(R)]
+        if gdt == "bf16":
+            grads = [O.bf16_rne(g) for g in grads]
+        F.fsdp_adamw_shard_step(pg, ADAMW, t, [to_dev(g) for g in grads], md, m_d, v_d, pd)
+        master, mo, vo, po16 = O.shard_step(po, grads, master, mo, vo, t, ADAMW, "bf16")
+        assert_bitexact(to_host(md).reshape(R, S), master, f"master t={t}")
+        assert_bitexact(to_host(m_d).reshape(R, S), mo, f"m t={t}")
+        assert_bitexact(to_host(v_d).reshape(R, S), vo, f"v t={t}")
+        assert_bitexact(to_host(pd).reshape(R, S), po16, f"param t={t}")
+
+
+@pytest.mark.parametrize("R", [8, 11])
+def test_specials_through_the_one_element_fused_step(R):
+    """NaN, +-Inf, -0 and overflow in the gradients of a short launch at
+    R >= 8 (the one-element kernel, specialised at R = 8, generic above):
+    master, m, v and the parameter equal the oracle's bit for bit, NaN
+    compared by class."""
+    shapes = [(16, 5), (3,)]
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    banner(f"specials, one-element fused step, R={R}")
+    rng = np.random.default_rng(90 + R)
+    grads = [(rng.standard_normal(T) * 1e-3).astype(np.float32) for _ in range(R)]
+    for g in grads:
+        g[0] = -0.0
+    grads[0][1] = np.nan
+    grads[1][2], grads[2][2] = np.inf, -np.inf
+    grads[3][3] = np.inf
+    for g in grads:
+        g[4] = 3.0e38
+    grads[0][5] = -0.0
+    grads = [O.bf16_rne(g) for g in grads]
+    master = O.shard_pack(po, rng.uniform(-1, 1, T).astype(np.float32))
+    master[0, 0] = -0.0
+    md = to_dev(master.reshape(-1))
+    m_d = torch.zeros_like(md)
+    v_d = torch.zeros_like(md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_adamw_shard_step(pg, ADAMW, 1, [to_dev(g) for g in grads], md, m_d, v_d, pd)
+    with np.errstate(invalid="ignore", over="ignore"):
+        mo, mm, vv, pp = O.shard_step(po, grads, master, np.zeros_like(master),
+                                      np.zeros_like(master), 1, ADAMW, "bf16")
+    for got, want, name in ((to_host(md).reshape(R, S), mo, "master"),
+                            (to_host(m_d).reshape(R, S), mm, "m"),
+                            (to_host(v_d).reshape(R, S), vv, "v")):
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), name
+        assert_bitexact(np.where(nan, 0, got), np.where(nan, 0, want), name)
+    gq = to_host(pd).reshape(R, S)
+    qnan = (pp & 0x7FFF) > 0x7F80
+    assert np.array_equal((gq & 0x7FFF) > 0x7F80, qnan)
+    assert_bitexact(np.where(qnan, 0, gq), np.where(qnan, 0, pp), "param")
