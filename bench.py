@@ -60,6 +60,11 @@ def parse():
                          "(reshard_after_forward=False); 2: freed after forward and "
                          "gathered again in backward (reshard_after_forward=True)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip the sustained-bandwidth part of the step line (the "
+                         "872M-parameter group's fused step and gather, ~40 GB of HBM)")
+    ap.add_argument("--sustained-workload", default="group4096_flat_r8",
+                    help="the FSDP1 (flat) workload of the sustained-bandwidth part")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -96,24 +101,35 @@ def kernel_src_hash():
     return h.hexdigest()[:16]
 
 
-# Kernels whose traffic the counter runs summarise: key -> the kernel-name
-# fragment that selects their dispatches in a rocprofv3 counter CSV.
+# Kernels whose traffic the counter runs summarise: key -> (kernel-name
+# fragments that select their dispatches in a rocprofv3 counter CSV, what
+# the kernel is).
 TRAFFIC_KERNELS = {
-    "fused": ("::k_fused<", "k_fused (fused reduce-scatter-average + AdamW + bf16 recast)"),
-    "fused_gather": ("::k_fused_gather<", "k_fused_gather (one unit's fused step, then the "
-                                          "next unit's gather, in one launch)"),
+    "fused": (("::k_fused<", "::k_fused_one<"),
+              "k_fused / k_fused_one (fused reduce-scatter-average + AdamW + bf16 recast, "
+              "alone)"),
+    "fused_gather": (("::k_fused_gather<",),
+                     "k_fused_gather (one unit's fused step, then the next unit's gather, in "
+                     "one launch)"),
+    "allreduce": (("::k_allreduce<",), "k_allreduce (DDP all-reduce-average to R receivers)"),
+    "adamw": (("::k_adamw<",), "k_adamw (AdamW + recast on an fp32 gradient)"),
+    "gather": (("::k_copy<2, 16, 8, 8>",),
+               "k_copy (bf16 gather + unflatten to 8 receivers, 16-byte lanes)"),
+    "accumulate": (("::k_accumulate<",), "k_accumulate (fp32 gradient accumulation)"),
+    "copy_pairs": (("::k_copy_pairs<",), "k_copy_pairs (batched re-shard copy)"),
 }
 
 
-def traffic_path(workload, key):
-    name = f"traffic_{workload}.json" if key == "fused" else f"traffic_{workload}_{key}.json"
+def traffic_path(workload, key, mode="step"):
+    tag = workload if mode == "step" else f"{workload}_{mode}"
+    name = f"traffic_{tag}.json" if key == "fused" else f"traffic_{tag}_{key}.json"
     return os.path.join(ROOT, "profiles", name)
 
 
-def load_traffic(workload, key="fused"):
+def load_traffic(workload, key="fused", mode="step"):
     """Counter-measured HBM bytes per launch of a kernel, if taken on the
     current kernel sources, else None."""
-    path = traffic_path(workload, key)
+    path = traffic_path(workload, key, mode)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -135,7 +151,7 @@ def rows(n_rows, n, dtype, device):
 CALIB_TIMED = 10
 
 
-def summarise_counters(fetch_csv, write_csv, workload):
+def summarise_counters(fetch_csv, write_csv, workload, mode="step"):
     """HBM bytes per launch of each kernel in TRAFFIC_KERNELS that the runs
     dispatched, from the FETCH_SIZE and WRITE_SIZE counters (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB
@@ -145,14 +161,14 @@ def summarise_counters(fetch_csv, write_csv, workload):
     import csv
     import statistics
 
-    def load(path, counter, frag):
+    def load(path, counter, frags):
         sel, copy = [], []
         with open(path) as f:
             for i, r in enumerate(csv.DictReader(f)):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                if frag in name:
+                if any(fr in name for fr in frags):
                     sel.append(float(r["Counter_Value"]))
                 elif "copy" in name.lower() and "fsdp" not in name:
                     order = int(r["Dispatch_Id"]) if r.get("Dispatch_Id") else i
@@ -166,15 +182,16 @@ def summarise_counters(fetch_csv, write_csv, workload):
         return (sum(sel) / len(sel) if sel else None), statistics.median(calib), len(sel)
 
     gib_kib = float(1 << 20)
-    for key, (frag, desc) in TRAFFIC_KERNELS.items():
-        fetch, fetch_copy, nf = load(fetch_csv, "FETCH_SIZE", frag)
-        write, write_copy, nw = load(write_csv, "WRITE_SIZE", frag)
+    for key, (frags, desc) in TRAFFIC_KERNELS.items():
+        fetch, fetch_copy, nf = load(fetch_csv, "FETCH_SIZE", frags)
+        write, write_copy, nw = load(write_csv, "WRITE_SIZE", frags)
         if fetch is None or write is None:
             continue
         fs = gib_kib / fetch_copy
         ws = gib_kib / write_copy
         out = {
             "workload": workload,
+            "mode": mode,
             "kernel": desc,
             "kernel_src_sha": kernel_src_hash(),
             "dispatches": {"FETCH_SIZE": nf, "WRITE_SIZE": nw},
@@ -186,7 +203,7 @@ def summarise_counters(fetch_csv, write_csv, workload):
             "write_scale": ws,
             "bytes_per_launch": (fetch * fs + write * ws) * 1024.0,
         }
-        with open(traffic_path(workload, key), "w") as f:
+        with open(traffic_path(workload, key, mode), "w") as f:
             json.dump(out, f, indent=1)
             f.write("\n")
         print(json.dumps(out))
@@ -245,7 +262,7 @@ def setup_units(wl, dev):
 def main():
     args = parse()
     if args.counters:
-        summarise_counters(args.counters[0], args.counters[1], args.workload)
+        summarise_counters(args.counters[0], args.counters[1], args.workload, args.mode)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the R ranks are virtual ranks in one GPU's "
@@ -424,10 +441,14 @@ def main():
                                ("shard_pack_cast", cast_avg_ms, 4 + pes)):
         kernels[key] = {"avg_ms": ms, "bytes": Tm * per_param,
                         "gbps": Tm * per_param / (ms * 1e-3) / 1e9}
-    # the dominant kernel of the step as scheduled: the fused step, or, in
-    # the overlap schedule with short steps, the launch that holds one
-    # unit's fused step and the next unit's gather
-    dominant = ("fused", fused_bytes, fused_avg_ms)
+    # the roofline: the fused reduce-scatter + AdamW + recast kernel alone,
+    # the step the 70% bar is set for; beside it the launch that dominates
+    # the step's time as scheduled (in the overlap schedule with short steps
+    # the launch holding one unit's fused step and the next unit's gather)
+    roofline = roof_entry("fused", fused_bytes, fused_avg_ms, args.workload)
+    roofline["target_frac"] = 0.70
+    roofline["target_met"] = roofline["frac"] >= 0.70
+    dominant = None
     if pair_avg_ms is not None:
         pair_bytes = float(np.mean([fused_bytes_unit[i] + gather_bytes_unit[i + 1]
                                     for i in range(len(units) - 1)]))
@@ -437,11 +458,8 @@ def main():
             "gbps": pair_bytes / (pair_avg_ms * 1e-3) / 1e9,
             "launches": 1 if one_launch else 2}
         if one_launch:
-            dominant = ("fused_gather", pair_bytes, pair_avg_ms)
-    dom_key, dom_bytes, dom_ms = dominant
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, dom_key)
-    plain = plain_copy(dom_bytes, args.cycle_gib, dev, hs, reps)
+            dominant = roof_entry("fused_gather", pair_bytes, pair_avg_ms, args.workload)
+    plain = plain_copy(fused_bytes, args.cycle_gib, dev, hs, reps)
     # every kernel line against a plain copy of its own bytes in one launch:
     # a short launch loses its ramp and drain whatever it computes
     copies_by_size = {plain["bytes_per_launch"]: plain}
@@ -453,6 +471,9 @@ def main():
             pc = copies_by_size[size]
             k["plain_copy_gbps"] = pc["achieved"]
             k["of_plain_copy"] = k["gbps"] / pc["achieved"]
+    roofline["of_plain_copy"] = kernels["fused_rs_adamw"]["of_plain_copy"]
+    if dominant is not None:
+        dominant["of_plain_copy"] = kernels["fused_then_gather"]["of_plain_copy"]
 
     copy_info = None
     if args.calibrate_copy:
@@ -473,10 +494,17 @@ def main():
         copy_info = dict(bytes=2 * n * 4, ms=ms, gbps=2 * n * 4 / (ms * 1e-3) / 1e9)
         del a, b
 
+    # --------------- sustained bandwidth: the 872M-parameter unit group
+    sustained = None
+    group_sample = None
+    if not args.no_sustained:
+        sustained, group_sample = sustained_group(args.sustained_workload, dev, hs,
+                                                  not args.no_cpu_baseline)
+
     # ------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(units, R, wl, args.cpu_seconds)
+        cpu = cpu_baseline(units, R, wl, args.cpu_seconds, group_sample)
 
     line = {
         "metric": "shard-step params/s and achieved HBM GB/s (% of peak), 12-layer R=8",
@@ -491,7 +519,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -517,18 +545,10 @@ def main():
         "step_bytes": step_bytes,
         "kernels": kernels,
         "memory_ledger_per_rank": runner.memory_ledger(pes),
-        "roofline": {
-            "kernel": TRAFFIC_KERNELS[dom_key][1],
-            "bytes_per_launch": dom_bytes,
-            "avg_ms": dom_ms,
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic,
-        },
+        "roofline": roofline,
+        "roofline_dominant_launch": dominant,
         "plain_copy": plain,
+        "sustained": sustained,
         "plan_layout": time_plan_layout(wl),
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
@@ -537,6 +557,98 @@ def main():
     if copy_info:
         line["copy_calibration"] = copy_info
     print(json.dumps(line), flush=True)
+
+
+# What the path computes in: the reduce-scatter sums in fp32, AdamW is
+# evaluated in IEEE double from the fp32 state (parameters and gradients are
+# stored as bf16, the state as fp32).
+DTYPE = "f32 reduce + f64 AdamW"
+
+
+def roof_entry(key, bytes_per_launch, ms, workload, mode="step"):
+    """The roofline object of one kernel: algorithmic bytes per launch over
+    its average launch time (HIP events around back-to-back launches),
+    against MI355X's HBM peak, with the counter-measured bytes when the
+    profiles hold them for the current kernel sources."""
+    gbps = bytes_per_launch / (ms * 1e-3) / 1e9
+    return {"kernel": TRAFFIC_KERNELS[key][1], "bytes_per_launch": bytes_per_launch,
+            "avg_ms": ms, "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+            "traffic": load_traffic(workload, key, mode)}
+
+
+def sustained_group(name, dev, hs, want_sample, launches=8):
+    """The sustained-bandwidth workload beside the headline: one 872M-parameter
+    group of four hidden-4096 blocks as one FSDP1 FlatParameter at R = 8.
+    Its fused step and its gather, each timed with HIP events around
+    `launches` back-to-back launches on the stream they run on (after one
+    warm-up launch each), with a plain copy of 4 GiB for comparison.  With
+    want_sample, also returns host copies of a few 1 Mi-element chunks of its
+    inputs for the oracle's chunk-wise leg.  Frees its buffers on return."""
+    import numpy as np
+    import torch
+
+    import fully_sharded_amd as F
+    from workloads.configs import ADAMW, WORKLOADS
+
+    wl = WORKLOADS[name]
+    if wl["layout"] != "flat" or len(wl["units"]) != 1:
+        raise SystemExit(f"--sustained-workload {name}: needs one FSDP1 (flat) unit")
+    R = wl["R"]
+    pdt = torch.bfloat16 if wl["param_dtype"] == "bf16" else torch.float32
+    _, units = setup_units(wl, dev)
+    u = units[0]
+    T = u.plan.T
+    recv = rows(R, T, pdt, dev)
+    fused = F.bind_adamw_shard_step(u.plan, ADAMW, u.grads, u.master, u.m, u.v, u.param)
+    gather = F.bind_gather_unflatten(u.plan, u.param, recv)
+    t = [0]
+
+    def fstep():
+        t[0] += 1
+        fused(t[0], hs)
+    fstep()
+    gather(hs)
+    fused_ms = _timed(fstep, launches)
+    gather_ms = _timed(lambda: gather(hs), launches)
+    ges = 2 if wl["grad_dtype"] == "bf16" else 4
+    pes = 2 if wl["param_dtype"] == "bf16" else 4
+    fb = float(T * (ges * R + 24 + pes))
+    gb = float(T * (pes + pes * R))
+    out = {"workload": name, "params": T, "R": R, "layout": wl["layout"],
+           "launches_timed": launches}
+    for key, b, ms in (("fused_rs_adamw", fb, fused_ms), ("gather_unflatten", gb, gather_ms)):
+        gbps = b / (ms * 1e-3) / 1e9
+        out[key] = {"avg_ms": ms, "bytes": b, "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+    out["step_ms"] = fused_ms + gather_ms
+    out["step_gbps"] = (fb + gb) / (out["step_ms"] * 1e-3) / 1e9
+    out["fused_rs_adamw"]["target_met"] = out["fused_rs_adamw"]["frac"] >= 0.70
+    sample = None
+    if want_sample:
+        # chunks of 1 Mi elements at 16 places of the shard space; the
+        # FlatParameter's shard element j of rank r is flat element r*S + j
+        S = u.plan.S
+        n = min(1 << 20, S)
+        sample = {"workload": name, "R": R, "grad_dtype": wl["grad_dtype"],
+                  "param_dtype": wl["param_dtype"], "chunks": []}
+        for c in range(16):
+            r = (5 * c) % R
+            j0 = int(((c * 0.618) % 1.0) * (S - n))
+            lo = r * S + j0
+            hi = min(lo + n, T)
+            if hi <= lo:
+                continue
+            sample["chunks"].append({
+                "grads": [_host(g[lo:hi]) for g in u.grads],
+                "master": _host(u.master[lo:hi]), "m": _host(u.m[lo:hi]),
+                "v": _host(u.v[lo:hi])})
+    del fused, gather, recv, units, u
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    plain = plain_copy(min(fb, 4 << 30), 4.0, dev, hs, 4)
+    out["plain_copy"] = plain
+    out["fused_rs_adamw"]["of_plain_copy"] = out["fused_rs_adamw"]["gbps"] / plain["achieved"]
+    return out, sample
 
 
 def step_blocks(steps, n_blocks=10):
@@ -658,7 +770,7 @@ def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
     d = {
         "metric": metric, "value": value, "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic",
         "config": dict({"workload": args.workload, "units": len(wl["units"]), "R": wl["R"],
                         "layout": wl["layout"], "mode": args.mode}, **cfg),
@@ -667,13 +779,6 @@ def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
     if extra:
         d.update(extra)
     print(json.dumps(d), flush=True)
-
-
-def _roof(bytes_per_launch, ms):
-    gbps = bytes_per_launch / (ms * 1e-3) / 1e9
-    return {"bytes_per_launch": bytes_per_launch, "avg_ms": ms, "bound": "hbm",
-            "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": gbps / PEAK_HBM_GBPS, "traffic": None}
 
 
 def run_mode(args, wl, plans, units):
@@ -754,7 +859,7 @@ def run_mode(args, wl, plans, units):
               {"reshard_fp32_batch": {"avg_ms": ms_launch, "bytes": bytes_launch,
                                       "arrays": len(big[1]),
                                 "gbps": bytes_launch / (ms_launch * 1e-3) / 1e9}},
-              _roof(bytes_launch, ms_launch), cpu,
+              roof_entry("copy_pairs", bytes_launch, ms_launch, args.workload, "reshard"), cpu,
               {"hbm_gbps": P * 28 / (ms * 1e-3) / 1e9})
         return
 
@@ -804,7 +909,7 @@ def run_mode(args, wl, plans, units):
               P / (ms * 1e-3), ms, {"micro_batches": K, "params": P},
               {"accumulate": {"avg_ms": ms_acc, "bytes": acc_bytes,
                               "gbps": acc_bytes / (ms_acc * 1e-3) / 1e9}},
-              _roof(acc_bytes, ms_acc), cpu,
+              roof_entry("accumulate", acc_bytes, ms_acc, args.workload, "accum"), cpu,
               {"hbm_gbps": step_bytes / (ms * 1e-3) / 1e9, "step_bytes": step_bytes})
         return
 
@@ -842,8 +947,18 @@ def run_mode(args, wl, plans, units):
         ms = _timed(step, args.steps)
         ms_ar = _timed(lambda: [F.fsdp_allreduce_avg(j[0].plan, j[0].grads, j[3], hs)
                                 for j in jobs], max(5, args.steps)) / len(jobs)
+        tt = [10 ** 6]
+
+        def adamw_pass():
+            tt[0] += 1
+            for u, rep, avg, outs, (rp, master, m, v, param) in jobs:
+                F.fsdp_adamw_shard_step(rp, ADAMW, tt[0], avg, master, m, v, param,
+                                        grads_are_replicas=False, stream=hs)
+        ms_adamw = _timed(adamw_pass, max(5, args.steps)) / len(jobs)
         Tm = float(np.mean([u.plan.T for u in units]))
         ar_bytes = Tm * (2 * R + 4 * R)
+        pes = 2 if units[0].param.dtype == torch.bfloat16 else 4
+        adamw_bytes = Tm * R * (4 + 24 + pes)
         step_bytes = P * (6 * R + 30 * R)
         # the FSDP step on the same model, same run, for the comparison
         recv = rows(R, max(p.T for p in plans.values()), units[0].param.dtype, dev)
@@ -857,6 +972,22 @@ def run_mode(args, wl, plans, units):
             fstep()
         ms_fsdp = _timed(fstep, args.steps)
         S_tot = sum(u.plan.S for u in units)
+        n_units = len(units)
+        # HBM bytes per step from the counter runs of this mode (FETCH_SIZE +
+        # WRITE_SIZE per launch, scaled by a plain copy), where the profiles
+        # hold them for the current kernels
+        tr = {k: load_traffic(args.workload, k, "ddp")
+              for k in ("allreduce", "adamw", "fused", "gather")}
+        measured = {
+            "ddp": (n_units * (tr["allreduce"] + tr["adamw"])
+                    if tr["allreduce"] and tr["adamw"] else None),
+            "fsdp": (n_units * (tr["fused"] + tr["gather"])
+                     if tr["fused"] and tr["gather"] else None),
+            "source": "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch of bench.py --mode ddp "
+                      "(profiles/traffic_<workload>_ddp_*.json), times the units per step",
+        }
+        if measured["ddp"] and measured["fsdp"]:
+            measured["ddp_over_fsdp"] = measured["ddp"] / measured["fsdp"]
         ledger = {
             "state_bytes_per_rank": {"ddp": 16 * P, "fsdp": 16 * S_tot},
             "comm_elems_per_rank_per_step": {
@@ -867,6 +998,7 @@ def run_mode(args, wl, plans, units):
                                                for u in units)},
             "hbm_bytes_per_step": {"ddp": step_bytes,
                                    "fsdp": P * (4 * R + 28)},
+            "hbm_bytes_per_step_measured": measured,
         }
         u0 = units[0]
         hg = [_host(g) for g in u0.grads]
@@ -887,8 +1019,10 @@ def run_mode(args, wl, plans, units):
         _line(args, wl, "DDP-comparator step params/s (all-reduce + AdamW on every replica)",
               P / (ms * 1e-3), ms, {"params": P},
               {"allreduce_avg": {"avg_ms": ms_ar, "bytes": ar_bytes,
-                                 "gbps": ar_bytes / (ms_ar * 1e-3) / 1e9}},
-              _roof(ar_bytes, ms_ar), cpu,
+                                 "gbps": ar_bytes / (ms_ar * 1e-3) / 1e9},
+               "adamw_replicas": {"avg_ms": ms_adamw, "bytes": adamw_bytes,
+                                  "gbps": adamw_bytes / (ms_adamw * 1e-3) / 1e9}},
+              roof_entry("allreduce", ar_bytes, ms_ar, args.workload, "ddp"), cpu,
               {"hbm_gbps": step_bytes / (ms * 1e-3) / 1e9, "step_bytes": step_bytes,
                "fsdp_ms_per_step_same_run": ms_fsdp, "ddp_over_fsdp_time": ms / ms_fsdp,
                "ledger": ledger})
@@ -896,22 +1030,96 @@ def run_mode(args, wl, plans, units):
     raise SystemExit(f"unknown mode {args.mode}")
 
 
-def cpu_baseline(state, R, wl, budget_s):
-    """The oracle, as it stands, on the same inputs (copied back to the host):
-    per unit, R gathers (one per receiving rank) then the shard step; units in
-    order, step after step, until about budget_s seconds of CPU work."""
+def cpu_workers():
+    """Host processes for the oracle's all-cores leg: the cores this process
+    may run on, at most 16 (one GPU's share of a shared host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_model():
     import platform
+    name = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return name
+
+
+def oracle_unit_worker(job):
+    """One oracle process of the all-cores leg: one unit's training steps, as
+    the one-core leg runs them (R gathers, then the shard step), repeated
+    until budget_s of compute; returns (params, seconds, steps, the first
+    step's results or None)."""
+    shapes, R, layout, grads, master, param, pdt, budget_s, want_first = job
+    import numpy as np
+
+    from oracle import fsdp_oracle as O
+    from workloads.configs import ADAMW
+    po = O.plan_layout(shapes, R, layout)
+    m = np.zeros_like(master)
+    v = np.zeros_like(master)
+    first = None
+    done, secs, t = 0, 0.0, 0
+    while secs < budget_s and t < 1000:
+        t += 1
+        t0 = time.perf_counter()
+        for _ in range(R):
+            O.gather_unflatten(po, param)
+        master, m, v, param = O.shard_step(po, grads, master, m, v, t, ADAMW, pdt)
+        secs += time.perf_counter() - t0
+        done += po.T
+        if want_first and first is None:
+            first = (master, m, v, param)
+    return done, secs, t, first
+
+
+def oracle_chunk_worker(job):
+    """One oracle process of the group leg: the step's element-wise work
+    (rank-order mean, AdamW, recast) on one chunk, repeated until budget_s."""
+    chunk, pdt, budget_s = job
+    from oracle import fsdp_oracle as O
+    from workloads.configs import ADAMW
+    done, secs, t = 0, 0.0, 0
+    while secs < budget_s and t < 1000:
+        t += 1
+        t0 = time.perf_counter()
+        g = O.rank_order_mean(chunk["grads"])
+        p2, _, _ = O.adamw_step(chunk["master"], chunk["m"], chunk["v"], g, t, ADAMW["lr"],
+                                ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"],
+                                ADAMW["weight_decay"])
+        if pdt == "bf16":
+            O.bf16_rne(p2)
+        secs += time.perf_counter() - t0
+        done += chunk["master"].size
+    return done, secs, t
+
+
+def cpu_baseline(state, R, wl, budget_s, group_sample=None):
+    """The oracle, as it stands, on the same inputs (copied back to the host),
+    timed on the host in three legs:
+      one core:   per unit, R gathers (one per receiving rank) then the shard
+                  step, units in order, step after step, in this process
+                  (NumPy's element-wise loops run on one thread);
+      all cores:  the same per-unit steps, one spawned process per unit (at
+                  most one per usable core, 16 at most), all at once; the
+                  first step of unit 0 is checked bit for bit against the
+                  one-core leg's; rate = parameters stepped / the longest
+                  process's compute time;
+      group:      chunks of the sustained workload's inputs (when that part
+                  ran), one process per chunk: the step's element-wise work.
+    `value` and `cores` are the all-cores leg's.  The worker processes start
+    fresh interpreters (they never touch the GPU)."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
 
     import numpy as np
 
     from oracle import fsdp_oracle as O
     from workloads.configs import ADAMW
-
-    def host(t):
-        import torch
-        if t.dtype == torch.bfloat16:
-            return t.view(torch.int16).cpu().numpy().view(np.uint16)
-        return t.cpu().numpy()
 
     if max(u.plan.T for u in state) * R > (1 << 26):
         return None   # the oracle copies whole units to the host: too large here
@@ -923,15 +1131,22 @@ def cpu_baseline(state, R, wl, budget_s):
         if key not in plans:
             plans[key] = O.plan_layout(list(pl.shapes), R, wl["layout"])
         po = plans[key]
-        units.append(dict(po=po, grads=[host(g) for g in s.grads],
-                          master=host(s.master).reshape(R, po.S).copy(),
+        units.append(dict(po=po, shapes=list(pl.shapes), grads=[_host(g) for g in s.grads],
+                          master=_host(s.master).reshape(R, po.S).copy(),
                           m=np.zeros((R, po.S), np.float32), v=np.zeros((R, po.S), np.float32),
-                          param=host(s.param).reshape(R, po.S).copy()))
+                          param=_host(s.param).reshape(R, po.S).copy()))
+    init = [(u["master"].copy(), u["param"].copy()) for u in units]
+    pdt = wl["param_dtype"]
+    share = {"one": 0.4, "all": 0.35, "group": 0.25} if group_sample else \
+        {"one": 0.55, "all": 0.45, "group": 0.0}
+
+    # ---- one core
     done = 0
     secs = 0.0
     unit_steps = 0
     t = 0
-    while secs < budget_s and t < 1000:
+    first = None
+    while secs < share["one"] * budget_s and t < 1000:
         t += 1
         for u in units:
             po = u["po"]
@@ -939,30 +1154,67 @@ def cpu_baseline(state, R, wl, budget_s):
             for _ in range(R):
                 O.gather_unflatten(po, u["param"])
             u["master"], u["m"], u["v"], u["param"] = O.shard_step(
-                po, u["grads"], u["master"], u["m"], u["v"], t, ADAMW, wl["param_dtype"])
+                po, u["grads"], u["master"], u["m"], u["v"], t, ADAMW, pdt)
             secs += time.perf_counter() - t0
+            if first is None:
+                first = (u["master"], u["m"], u["v"], u["param"])
             done += po.T
             unit_steps += 1
-            if secs >= budget_s:
+            if secs >= share["one"] * budget_s:
                 break
-    cpu_model = platform.processor()
-    try:
-        with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    cpu_model = ln.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    one = {"value": done / secs, "unit": "params/s", "cores": 1,
+           "sample": f"{unit_steps} unit-steps over {t} step(s) of the {len(state)}-unit "
+                     f"model (per unit: {R} gathers + reduce-scatter-average + AdamW + "
+                     f"recast), {done} params in {secs:.2f} s, one process"}
+
+    # ---- all cores: one process per unit
+    nproc = min(cpu_workers(), len(units))
+    ctx = multiprocessing.get_context("spawn")
+    jobs = [(u["shapes"], R, wl["layout"], u["grads"], m0, p0, pdt, share["all"] * budget_s,
+             i == 0) for i, (u, (m0, p0)) in enumerate(zip(units[:nproc], init))]
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=nproc, mp_context=ctx) as pool:
+        res = list(pool.map(oracle_unit_worker, jobs))
+        wall = time.perf_counter() - t0
+        got = res[0][3]
+        for a, b, name in zip(got, first, ("master", "m", "v", "param")):
+            if not np.array_equal(a.view(np.uint8), b.view(np.uint8)):
+                raise SystemExit(f"oracle all-cores leg differs from the one-core leg ({name})")
+        done = sum(r[0] for r in res)
+        secs = max(r[1] for r in res)
+        allc = {"value": done / secs, "unit": "params/s", "cores": nproc,
+                "sample": f"{nproc} processes, one unit of the {len(state)}-unit model each, "
+                          f"running its steps as the one-core leg does "
+                          f"({sum(r[2] for r in res)} unit-steps; unit 0's first step "
+                          f"bit-identical to the one-core leg's), {done} params, longest "
+                          f"process {secs:.2f} s of compute ({wall:.2f} s wall with start-up)"}
+
+        # ---- the sustained workload, chunk by chunk
+        grp = None
+        if group_sample and group_sample["chunks"]:
+            ch = group_sample["chunks"]
+            gjobs = [(c, group_sample["param_dtype"], share["group"] * budget_s) for c in ch]
+            with ProcessPoolExecutor(max_workers=min(cpu_workers(), len(ch)),
+                                     mp_context=ctx) as gpool:
+                gres = list(gpool.map(oracle_chunk_worker, gjobs))
+            gdone = sum(r[0] for r in gres)
+            gsecs = max(r[1] for r in gres)
+            grp = {"value": gdone / gsecs, "unit": "params/s",
+                   "cores": min(cpu_workers(), len(ch)),
+                   "sample": f"{len(ch)} chunks of up to 1 Mi elements of the "
+                             f"{group_sample['workload']} shard space (R={group_sample['R']}"
+                             f"), one process each: reduce-scatter-average + AdamW + "
+                             f"recast, {sum(r[2] for r in gres)} chunk passes, {gdone} params, "
+                             f"longest process {gsecs:.2f} s"}
     return {
-        "value": done / secs,
+        "value": allc["value"],
         "unit": "params/s",
-        "cores": 1,
+        "cores": nproc,
         "kind": "oracle",
-        "sample": f"{unit_steps} unit-steps over {t} step(s) of the {len(state)}-unit model "
-                  f"(per unit: {R} gathers + reduce-scatter-average + AdamW + recast), "
-                  f"{done} params in {secs:.2f} s; NumPy element-wise ops, one thread; "
-                  f"{cpu_model}",
+        "sample": allc["sample"],
+        "cpu_model": cpu_model(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "legs": {"one_core": one, "all_cores": allc, "sustained_workload_chunks": grp},
     }
 
 

@@ -32,7 +32,7 @@ def write_csv(path, counter, rows):
 @pytest.fixture
 def traffic_dir(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_path",
-                        lambda wl, key: str(tmp_path / f"traffic_{wl}_{key}.json"))
+                        lambda wl, key, mode="step": str(tmp_path / f"traffic_{wl}_{key}.json"))
     return tmp_path
 
 

@@ -23,7 +23,8 @@ def run_bench(capsys, monkeypatch, *argv):
 def test_step_line_contract(capsys, monkeypatch):
     print("[gpu] bench step block512_r4", flush=True)
     d = run_bench(capsys, monkeypatch, "--workload", "block512_r4", "--steps", "4",
-                  "--warmup", "1", "--cpu-seconds", "0.5", "--cycle-gib", "0.25")
+                  "--warmup", "1", "--cpu-seconds", "1.0", "--cycle-gib", "0.25",
+                  "--sustained-workload", "block512_flat_r4")
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline"):
@@ -38,8 +39,21 @@ def test_step_line_contract(capsys, monkeypatch):
     assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert rf["achieved"] == pytest.approx(rf["bytes_per_launch"] / (rf["avg_ms"] * 1e-3) / 1e9)
     assert 0 < rf["frac"] < 1
+    assert rf["target_frac"] == 0.70 and rf["target_met"] == (rf["frac"] >= 0.70)
+    assert rf["kernel"].startswith("k_fused")
     cb = d["cpu_baseline"]
-    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0 and cb["sample"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["sample"]
+    legs = cb["legs"]
+    assert legs["one_core"]["cores"] == 1 and legs["one_core"]["value"] > 0
+    assert cb["cores"] == legs["all_cores"]["cores"] >= 1
+    assert cb["value"] == legs["all_cores"]["value"]
+    assert legs["sustained_workload_chunks"]["value"] > 0
+    su = d["sustained"]
+    assert su["workload"] == "block512_flat_r4" and su["R"] == 4
+    for key in ("fused_rs_adamw", "gather_unflatten"):
+        k = su[key]
+        assert k["gbps"] == pytest.approx(k["bytes"] / (k["avg_ms"] * 1e-3) / 1e9)
+        assert 0 < k["frac"] < 1
     # 4 steps timed in 4 blocks of one: the mean lies between their min and max
     bl = d["ms_per_step_blocks"]
     assert bl["blocks"] == 4 and 0 < bl["min"] <= bl["median"]
