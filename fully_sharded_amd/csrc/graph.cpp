@@ -8,7 +8,10 @@
 // enqueues, on the caller's stream, a one-lane kernel that writes step t's
 // record (computed on the host exactly as the stream entry point computes
 // it).  Stream order puts that write after the previous replay and before
-// this one; no node's arguments change after instantiation.
+// this one; a launch on another stream than the previous one first waits
+// for an event recorded after that replay, so the write never races a
+// replay still reading the record.  No node's arguments change after
+// instantiation.
 #include <hip/hip_runtime.h>
 
 #include <new>
@@ -27,6 +30,9 @@ struct fsdp_step_graph {
   hipGraphNode_t last = nullptr;
   int64_t n_nodes = 0;
   int64_t n_adamw = 0;
+  hipEvent_t replayed = nullptr;       // recorded after each launch's replay
+  hipStream_t last_stream = nullptr;   // the stream of the previous launch
+  bool launched = false;
 };
 
 namespace {
@@ -71,6 +77,7 @@ fsdp_status check_open(const fsdp_step_graph* g) {
 void destroy(fsdp_step_graph* g) {
   if (g->exec) (void)hipGraphExecDestroy(g->exec);
   if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->replayed) (void)hipEventDestroy(g->replayed);
   if (g->scalars) (void)hipFree(g->scalars);
   delete g;
 }
@@ -91,6 +98,7 @@ fsdp_status fsdp_step_graph_create(const fsdp_adamw_hparams* hp, fsdp_step_graph
   if (e == hipSuccess)
     e = hipMalloc(reinterpret_cast<void**>(&g->scalars), sizeof(fsdp::AdamScalars));
   if (e == hipSuccess) e = hipGraphCreate(&g->graph, 0);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&g->replayed, hipEventDisableTiming);
   if (e != hipSuccess) {
     destroy(g);
     return fsdp::status_of(e);
@@ -170,12 +178,25 @@ fsdp_status fsdp_step_graph_launch(fsdp_step_graph* g, int64_t step, void* strea
       return st;
     }
   }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the previous replay, if it ran on another stream, ends before this
+  // launch rewrites the scalar record
+  if (g->launched && s != g->last_stream) {
+    st = fsdp::status_of(hipStreamWaitEvent(s, g->replayed, 0));
+    if (st != FSDP_OK) return st;
+  }
   const fsdp::StreamSink sink(stream);
   if (g->n_adamw > 0) {
     st = fsdp::status_of(fsdp::launch_set_scalars(g->scalars, sc, sink));
     if (st != FSDP_OK) return st;
   }
-  return fsdp::status_of(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+  st = fsdp::status_of(hipGraphLaunch(g->exec, s));
+  if (st != FSDP_OK) return st;
+  st = fsdp::status_of(hipEventRecord(g->replayed, s));
+  if (st != FSDP_OK) return st;
+  g->launched = true;
+  g->last_stream = s;
+  return FSDP_OK;
 }
 
 }  // extern "C"

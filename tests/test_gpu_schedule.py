@@ -134,6 +134,27 @@ def test_step_graph_steps_need_not_be_consecutive():
             assert torch.equal(x, y)
 
 
+def test_step_graph_launches_on_alternating_streams():
+    """Consecutive replays enqueued on two streams, with no host
+    synchronisation between them: each launch on another stream waits for
+    the previous replay (both read the graph's one record of AdamW
+    scalars), so the state matches the stream calls bit for bit."""
+    print("[gpu] step graph on alternating streams", flush=True)
+    ref_units, ref_recv = build("model12_r8")
+    units, recv = build("model12_r8")
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial")
+    run = StepRunner(units, ADAMW, recv, "graph")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    torch.cuda.synchronize()
+    for t in range(1, 7):
+        run.graph.launch(t, streams[t % 2])
+        ref.step(t)
+    torch.cuda.synchronize()
+    for a, b in zip(state_of(ref_units), state_of(units)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
 def test_step_graph_errors():
     units, recv = build("block512_r4")
     u = units[0]
