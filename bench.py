@@ -116,7 +116,7 @@ TRAFFIC_KERNELS = {
     "gather": (("::k_copy<2, 16, 8, 8>",),
                "k_copy (bf16 gather + unflatten to 8 receivers, 16-byte lanes)"),
     "accumulate": (("::k_accumulate<",), "k_accumulate (fp32 gradient accumulation)"),
-    "copy_pairs": (("::k_copy_pairs<",), "k_copy_pairs (batched re-shard copy)"),
+    "copy_pairs": (("::k_copy_pairs<4>",), "k_copy_pairs<4> (batched re-shard copy, fp32 arrays)"),
 }
 
 
@@ -475,24 +475,7 @@ def main():
     if dominant is not None:
         dominant["of_plain_copy"] = kernels["fused_then_gather"]["of_plain_copy"]
 
-    copy_info = None
-    if args.calibrate_copy:
-        n = 1 << 28  # 1 GiB of fp32
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(3):
-            b.copy_(a)
-        c0.record(stream)
-        for _ in range(CALIB_TIMED):
-            b.copy_(a)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        ms = c0.elapsed_time(c1) / CALIB_TIMED
-        copy_info = dict(bytes=2 * n * 4, ms=ms, gbps=2 * n * 4 / (ms * 1e-3) / 1e9)
-        del a, b
+    copy_info = calibration_copy(dev) if args.calibrate_copy else None
 
     # --------------- sustained bandwidth: the 872M-parameter unit group
     sustained = None
@@ -563,6 +546,30 @@ def main():
 # evaluated in IEEE double from the fp32 state (parameters and gradients are
 # stored as bf16, the state as fp32).
 DTYPE = "f32 reduce + f64 AdamW"
+
+
+def calibration_copy(dev):
+    """A plain 1 GiB device copy (torch's copy kernel), 3 untimed then
+    CALIB_TIMED timed launches: the run's reference for the FETCH_SIZE and
+    WRITE_SIZE counters (1 GiB read and 1 GiB written per launch)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        b.copy_(a)
+    c0.record(stream)
+    for _ in range(CALIB_TIMED):
+        b.copy_(a)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ms = c0.elapsed_time(c1) / CALIB_TIMED
+    del a, b
+    return dict(bytes=2 * n * 4, ms=ms, gbps=2 * n * 4 / (ms * 1e-3) / 1e9)
 
 
 def roof_entry(key, bytes_per_launch, ms, workload, mode="step"):
@@ -767,6 +774,8 @@ def _line(args, wl, metric, value, ms, cfg, kernels, roofline, cpu, extra=None):
               else plain_copy(k["bytes"], args.cycle_gib, "cuda", hs, reps))
         k["plain_copy_gbps"] = pc["achieved"]
         k["of_plain_copy"] = k["gbps"] / pc["achieved"]
+    if args.calibrate_copy:
+        extra = dict(extra or {}, copy_calibration=calibration_copy("cuda"))
     d = {
         "metric": metric, "value": value, "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -887,9 +896,12 @@ def run_mode(args, wl, plans, units):
         for _ in range(args.warmup):
             step()
         ms = _timed(step, args.steps)
-        ms_acc = _timed(lambda: [c[0](False, hs) for c in calls], max(5, args.steps)) / len(calls)
+        # the accumulate launches of whole passes (K per unit: the first
+        # copies, 6 bytes per element and rank; the others add, 10), per launch
+        ms_acc = _timed(lambda: [c[0](k == 0, hs) for c in calls for k in range(K)],
+                        max(5, args.steps)) / (len(calls) * K)
         Tm = float(np.mean([u.plan.T for u in units]))
-        acc_bytes = Tm * R * (2 + 4 + 4)
+        acc_bytes = Tm * R * (6 + 10 * (K - 1)) / K
         step_bytes = P * (R * 6 + (K - 1) * R * 10 + (2 + 2 * R) + (4 * R + 26))
         u0 = units[0]
         po = O.plan_layout(list(u0.plan.shapes), R, wl["layout"])
