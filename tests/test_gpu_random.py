@@ -1,9 +1,18 @@
 """Randomised sequences through the C ABI against the oracle: random small
 units (1-4 parameters, 1-3 dims, dims 1-70), random R (1-16) and layouts;
-per case pack, two steps through the paired step-then-gather call, a
-re-shard of the trained state to another R and layout, the averaged
-all-reduce and a two-micro-batch accumulation.  Bit-exact wherever the
-contract says so, AdamW to its tolerance."""
+per case pack, two steps through the paired step-then-gather call and a
+third through the standalone fused step, a re-shard of the trained state to
+another R and layout, the averaged all-reduce and a two-micro-batch
+accumulation.  Bit-exact wherever the contract says so, AdamW to its
+tolerance and, since the kernels evaluate it as the oracle does, bit for
+bit.
+
+The environment can widen the run: FSDP_RANDOM_SEEDS (number of sequences,
+24 by default), FSDP_RANDOM_RMAX (largest R, 16) and FSDP_RANDOM_DMAX
+(largest leading dimension, 70), e.g.
+FSDP_RANDOM_SEEDS=1000 python -m pytest -m gpu tests/test_gpu_random.py."""
+
+import os
 
 import numpy as np
 import pytest
@@ -27,11 +36,19 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+N_SEEDS = int(os.environ.get("FSDP_RANDOM_SEEDS", "24"))
+R_MAX = int(os.environ.get("FSDP_RANDOM_RMAX", "16"))
+D_MAX = int(os.environ.get("FSDP_RANDOM_DMAX", "70"))
+
+
 def random_shapes(rng):
+    """1-4 parameters; the leading dimension up to D_MAX, the others up to 70
+    (at most two dimensions when D_MAX > 70, to bound the size)."""
     out = []
     for _ in range(int(rng.integers(1, 5))):
-        nd = int(rng.integers(1, 4))
-        out.append(tuple(int(x) for x in rng.integers(1, 71, nd)))
+        nd = int(rng.integers(1, 4 if D_MAX <= 70 else 3))
+        out.append((int(rng.integers(1, D_MAX + 1)),) +
+                   tuple(int(x) for x in rng.integers(1, 71, nd - 1)))
     return out
 
 
@@ -44,10 +61,10 @@ def random_unit(rng, R, layout):
     return shapes, po, full, grads
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", list(range(N_SEEDS)))
 def test_random_sequence_matches_the_oracle(seed):
     rng = np.random.default_rng(9000 + seed)
-    R = int(rng.integers(1, 17))
+    R = int(rng.integers(1, R_MAX + 1))
     layout = ["per_param", "flat"][int(rng.integers(0, 2))]
     print(f"[gpu] random seed={seed} R={R} {layout}", flush=True)
     shapes, po, full, grads = random_unit(rng, R, layout)
@@ -81,12 +98,24 @@ def test_random_sequence_matches_the_oracle(seed):
         gp = to_host(param).reshape(R, po.S)
         assert_bf16_within_ulp(gp, po_param, f"param t={t}")
         assert_bitexact(gp, O.bf16_rne(gm), "param = RNE(master)")
+        assert_bitexact(gm, mo, f"master bits t={t}")
+        assert_bitexact(gp, po_param, f"param bits t={t}")
         want, _ = O.gather_unflatten(npo, O.bf16_rne(O.shard_pack(npo, nfull)))
         for r in recv:
             assert_bitexact(to_host(r), want, "next unit's gather")
 
+    # a third step through the standalone fused call (at R >= 8 and this
+    # size, the one-element kernel)
+    F.fsdp_adamw_shard_step(pg, ADAMW, 3, g_d, master, m, v, param)
+    mo, om, ov, po_param = O.shard_step(po, grads, mo, om, ov, 3, ADAMW, "bf16")
+    torch.cuda.synchronize()
+    assert_bitexact(to_host(master).reshape(R, po.S), mo, "master t=3")
+    assert_bitexact(to_host(m).reshape(R, po.S), om, "m t=3")
+    assert_bitexact(to_host(v).reshape(R, po.S), ov, "v t=3")
+    assert_bitexact(to_host(param).reshape(R, po.S), po_param, "param t=3")
+
     # re-shard the trained fp32 state to another world size and layout
-    R2 = int(rng.integers(1, 17))
+    R2 = int(rng.integers(1, R_MAX + 1))
     l2 = ["per_param", "flat"][int(rng.integers(0, 2))]
     po2 = O.plan_layout(shapes, R2, l2)
     rs = F.Resharder(pg, F.Plan(shapes, R2, l2))
