@@ -252,20 +252,28 @@ struct One<u16> {
 // b / kSplit, its elements [(b % kSplit) * 256, + 256).
 constexpr int kSplit = 1024 / kThreads;
 
-// Ask for a value in scalar registers here.  Placed at the top of a kernel
-// for the work descriptor and the data pointers, it makes the compiler issue
-// all of their scalar loads in one round after the kernel arguments', where
-// it otherwise loads the descriptor's length, tests it, and only then loads
-// its offsets and the pointers: one more memory round trip before the first
-// data load of every workgroup (the one-element fused step was 0.1-0.2 us
-// faster per 3.1M-element launch with it).  An empty asm statement: no
-// instruction is emitted.
-template <typename T>
-__device__ __forceinline__ void in_sgprs(const T& x) {
-  asm volatile("" ::"s"(x));
-}
-__device__ __forceinline__ void in_sgprs(const Work& w) {
-  asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len));
+// Ask for the work descriptor and the data pointers in scalar registers at
+// the top of a kernel, in one asm statement: the compiler then issues all
+// of their scalar loads in one round after the kernel arguments', where it
+// otherwise loads the descriptor's length, tests it, and only then loads
+// its offsets and the pointers -- one more memory round trip before the
+// first data load of every workgroup.  One statement, because each
+// volatile asm is a scheduling barrier: with one per value the loads for
+// the later ones were issued a round after the descriptor's.  An empty asm
+// statement: no instruction is emitted.
+template <int RT, bool REC, typename A>
+__device__ __forceinline__ void args_in_sgprs(const Work& w, const A& a) {
+  // REC: the address of the scalar record too (the record itself is only
+  // needed for the arithmetic, so its load is not waited for here)
+  const void* rec = REC ? static_cast<const void*>(a.scp) : static_cast<const void*>(a.param);
+  if constexpr (RT == 8) {
+    asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.g.p[0]), "s"(a.g.p[1]),
+                 "s"(a.g.p[2]), "s"(a.g.p[3]), "s"(a.g.p[4]), "s"(a.g.p[5]), "s"(a.g.p[6]),
+                 "s"(a.g.p[7]), "s"(a.master), "s"(a.m), "s"(a.v), "s"(a.param), "s"(rec));
+  } else {
+    asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.master), "s"(a.m), "s"(a.v),
+                 "s"(a.param), "s"(rec));
+  }
 }
 
 // (g_0[s] + g_1[s] + ... + g_{R-1}[s]) / R, fp32, left to right, every
@@ -753,16 +761,10 @@ template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused_one(const Work* __restrict__ work,
                                                         FusedArgs<ptr_cap(RT)> a) {
   const Work w = work[blockIdx.x / kSplit];
-  in_sgprs(w);
-  if constexpr (RT > 0) {
-#pragma unroll
-    for (int q = 0; q < RT; ++q) in_sgprs(a.g.p[q]);
-  }
-  in_sgprs(a.master);
-  in_sgprs(a.m);
-  in_sgprs(a.v);
-  in_sgprs(a.param);
+  // the step's scalars first: read before any asm statement, the device
+  // record (REC) is known unclobbered and comes in the same scalar round
   const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+  args_in_sgprs<RT, REC>(w, a);
   const int64_t off = static_cast<int64_t>(blockIdx.x % kSplit) * kThreads + threadIdx.x;
   if (off >= w.len) return;
   const int64_t e = w.dst + off;
