@@ -8,10 +8,12 @@
 // enqueues, on the caller's stream, a one-lane kernel that writes step t's
 // record (computed on the host exactly as the stream entry point computes
 // it).  Stream order puts that write after the previous replay and before
-// this one; a launch on another stream than the previous one first waits
-// for an event recorded after that replay, so the write never races a
-// replay still reading the record.  No node's arguments change after
-// instantiation.
+// this one; a launch on another stream than the previous one first makes
+// its stream wait for an event recorded, at that moment, on the previous
+// launch's stream (so after that replay), and the write never races a
+// replay still reading the record.  Launches on one stream record nothing:
+// an event after every replay cost 4-5 us per step on the 12-layer model.
+// No node's arguments change after instantiation.
 #include <hip/hip_runtime.h>
 
 #include <new>
@@ -30,7 +32,7 @@ struct fsdp_step_graph {
   hipGraphNode_t last = nullptr;
   int64_t n_nodes = 0;
   int64_t n_adamw = 0;
-  hipEvent_t replayed = nullptr;       // recorded after each launch's replay
+  hipEvent_t replayed = nullptr;       // marks the previous launch's stream
   hipStream_t last_stream = nullptr;   // the stream of the previous launch
   bool launched = false;
 };
@@ -182,7 +184,8 @@ fsdp_status fsdp_step_graph_launch(fsdp_step_graph* g, int64_t step, void* strea
   // the previous replay, if it ran on another stream, ends before this
   // launch rewrites the scalar record
   if (g->launched && s != g->last_stream) {
-    st = fsdp::status_of(hipStreamWaitEvent(s, g->replayed, 0));
+    st = fsdp::status_of(hipEventRecord(g->replayed, g->last_stream));
+    if (st == FSDP_OK) st = fsdp::status_of(hipStreamWaitEvent(s, g->replayed, 0));
     if (st != FSDP_OK) return st;
   }
   const fsdp::StreamSink sink(stream);
@@ -191,8 +194,6 @@ fsdp_status fsdp_step_graph_launch(fsdp_step_graph* g, int64_t step, void* strea
     if (st != FSDP_OK) return st;
   }
   st = fsdp::status_of(hipGraphLaunch(g->exec, s));
-  if (st != FSDP_OK) return st;
-  st = fsdp::status_of(hipEventRecord(g->replayed, s));
   if (st != FSDP_OK) return st;
   g->launched = true;
   g->last_stream = s;

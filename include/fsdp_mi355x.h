@@ -382,10 +382,11 @@ fsdp_status fsdp_step_graph_info(const fsdp_step_graph* graph, int64_t* n_nodes,
  * (>= 1), on `stream`.  The first launch instantiates the graph and seals
  * it (no more nodes).  Must be called on the graph's device.  Consecutive
  * launches may use different streams: a launch on another stream than the
- * previous one first waits (on the device, not the host) for the previous
- * replay to end, since both use the graph's one record of AdamW scalars.
- * Launches of one graph from several host threads at once are not
- * supported. */
+ * previous one first makes its stream wait (on the device, not the host)
+ * for the work enqueued so far on the previous launch's stream, which must
+ * therefore still exist; both replays use the graph's one record of AdamW
+ * scalars.  Launches of one graph from several host threads at once are
+ * not supported. */
 fsdp_status fsdp_step_graph_launch(fsdp_step_graph* graph, int64_t step, void* stream);
 
 /* Static, human-readable name of a status code (an fsdp_status value; any
