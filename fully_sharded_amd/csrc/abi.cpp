@@ -98,6 +98,13 @@ fsdp_status adam_scalars(const fsdp_adamw_hparams* hp, int64_t step, AdamScalars
   sc->lr = lr;
   sc->eps = eps;
   if (!(sc->bc1 > 0) || !(sc->bc2 > 0)) return FSDP_ERR_INVALID_ARG;
+  // 1 / bc to about 2^-106: hi = RN(1 / bc); 1 - bc hi is exact in one
+  // fused multiply-add (|1 - bc hi| <= 2^-53 and its bits fit 53), and
+  // lo = RN((1 - bc hi) / bc).  The kernels divide by bc with these.
+  sc->rbc1_hi = 1.0 / sc->bc1;
+  sc->rbc1_lo = std::fma(-sc->bc1, sc->rbc1_hi, 1.0) / sc->bc1;
+  sc->rbc2_hi = 1.0 / sc->bc2;
+  sc->rbc2_lo = std::fma(-sc->bc2, sc->rbc2_hi, 1.0) / sc->bc2;
   return FSDP_OK;
 }
 

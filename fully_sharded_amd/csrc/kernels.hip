@@ -346,25 +346,54 @@ __device__ __forceinline__ float grad_avg1(const PA& g, int R, int64_t s) {
 }
 
 // ------------------------------------------------------------------ AdamW
+// a / b, correctly rounded, for b one of the step's bias corrections
+// (2^-53 <= b <= 1) and 1 / b = hi + lo to about 2^-106 (hi = RN(1 / b)):
+//   q0 = RN(a hi + RN(a lo))  is within 1/2 ulp + 2^-104 |a/b| of a / b, so
+//                             it is one of the two doubles around a / b;
+//   r  = RN(a - b q0)         is then exact (the remainder of a faithful
+//                             quotient fits a double);
+//   q  = RN(q0 + r hi)        is RN(a / b) by Markstein's theorem (hi within
+//                             1/2 ulp of 1 / b, q0 within 1 ulp of a / b).
+// A multiply and three fused multiply-adds, where an IEEE division is a
+// reciprocal estimate, two scaling steps, five multiply-adds and a fix-up.
+// The steps need a lo and r in the normal range.  Here a is m' or v', made
+// from fp32 values and betas in [0, 1): a nonzero a is at least 2^-404 in
+// magnitude (at most 2^257) unless the gradient is zero and a beta is below
+// 2^-651, and then b = 1 - beta^t rounds to 1, hi = 1, lo = 0 and q = a
+// exactly.  Zero, infinity and NaN, for which a / b is a itself, take a.
+constexpr int kZeroInfNan = 0x267;  // v_cmp_class: +-0, +-inf, quiet and signalling NaN
+
+__device__ __forceinline__ double div_bias(double a, double b, double hi, double lo) {
+  const double q0 = fma(a, hi, a * lo);
+  const double r = fma(-b, q0, a);
+  const double q = fma(r, hi, q0);
+  return __builtin_amdgcn_class(a, kZeroInfNan) ? a : q;
+}
+
 // One element, in float64 from the fp32 state, in the order the update is
 // defined:
 //   p1 = p (1 - lr wd);  m' = b1 m + (1-b1) g;  v' = b2 v + ((1-b2) g) g;
 //   m^ = m' / (1 - b1^t);  v^ = v' / (1 - b2^t);
 //   p' = p1 - (lr m^) / (sqrt(v^) + eps)
-// with IEEE double operations (correctly rounded divide and sqrt, no
-// contraction), then each result rounded once to fp32, which makes the
-// result the definition's exactly.  About 70 double operations per element
-// against 42 bytes of HBM traffic: the same kernels with the update in fp32
-// were 1.6% faster on the 12-layer step (the divides and square root of
-// the last workgroups of each short launch), a price paid for exactness.
+// with correctly rounded double operations (no contraction), then each
+// result rounded once to fp32, which makes the result the definition's
+// exactly.  The two divisions by the bias corrections are IEEE divisions
+// (FASTDIV false) or div_bias (true): the same bits, 55 instead of 65
+// double operations per element.  Which one a kernel takes was measured on
+// MI355X in alternating runs of both: div_bias made the one-element fused
+// step 1% and the short unfused AdamW 2-4% faster; in the four-element
+// fused forms it gained nothing on the 872M-parameter group (within 0.5%)
+// and made the step-and-gather launch slower (31.9-32.2 against 31.7-32.0
+// us), so those and the long AdamW launches keep IEEE division.
+template <bool FASTDIV>
 __device__ __forceinline__ void adamw1(float gf, float& pf, float& mf, float& vf,
                                        const AdamScalars& c) {
   const double g = gf;
   const double p1 = static_cast<double>(pf) * c.decay;
   const double m1 = c.beta1 * static_cast<double>(mf) + c.omb1 * g;
   const double v1 = c.beta2 * static_cast<double>(vf) + (c.omb2 * g) * g;
-  const double mh = m1 / c.bc1;
-  const double vh = v1 / c.bc2;
+  const double mh = FASTDIV ? div_bias(m1, c.bc1, c.rbc1_hi, c.rbc1_lo) : m1 / c.bc1;
+  const double vh = FASTDIV ? div_bias(v1, c.bc2, c.rbc2_hi, c.rbc2_lo) : v1 / c.bc2;
   const double p2 = p1 - (c.lr * mh) / (sqrt(vh) + c.eps);
   pf = static_cast<float>(p2);
   mf = static_cast<float>(m1);
@@ -373,17 +402,38 @@ __device__ __forceinline__ void adamw1(float gf, float& pf, float& mf, float& vf
 
 // The step's scalars.  Stream launches carry them in the kernel arguments;
 // graph nodes (REC) read the device record written before each replay, in
-// one 72-byte load issued beside the work descriptor's.  A single kernel
+// scalar loads issued beside the work descriptor's.  A single kernel
 // choosing between the two at run time compiled to nine dependent 8-byte
 // loads before the descriptor's, which slowed every graph node's
 // workgroups; the choice is therefore made at compile time.
 template <bool REC>
 __device__ __forceinline__ AdamScalars scalars_of(const AdamScalars& own,
                                                   const AdamScalars* __restrict__ rec) {
-  if constexpr (REC)
-    return *rec;
-  else
+  if constexpr (REC) {
+    // Only a separate launch writes the record, so it is constant for the
+    // whole kernel: read through the constant address space, whose uniform
+    // loads the compiler always issues as scalar loads (through a global
+    // pointer it proves that only where no store can precede the load).
+    using ConstScalars = const __attribute__((address_space(4))) AdamScalars;
+    const ConstScalars* c = reinterpret_cast<const ConstScalars*>(reinterpret_cast<uintptr_t>(rec));
+    AdamScalars r;
+    r.decay = c->decay;
+    r.beta1 = c->beta1;
+    r.omb1 = c->omb1;
+    r.beta2 = c->beta2;
+    r.omb2 = c->omb2;
+    r.bc1 = c->bc1;
+    r.bc2 = c->bc2;
+    r.lr = c->lr;
+    r.eps = c->eps;
+    r.rbc1_hi = c->rbc1_hi;
+    r.rbc1_lo = c->rbc1_lo;
+    r.rbc2_hi = c->rbc2_hi;
+    r.rbc2_lo = c->rbc2_lo;
+    return r;
+  } else {
     return own;
+  }
 }
 
 // ------------------------------------------------------------------ copy
@@ -655,7 +705,7 @@ struct AdamArgs {
 };
 
 // One pass per workgroup: lane c of the grid owns elements [4c, 4c + 4).
-template <typename P, bool REC>
+template <typename P, bool REC, bool FASTDIV>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
   P* __restrict__ param = static_cast<P*>(a.param);
   const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
@@ -669,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
     Io<float>::load4(a.m + e0, true, m);
     Io<float>::load4(a.v + e0, true, v);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) adamw1(g[k], p[k], m[k], v[k], sc);
+    for (int k = 0; k < 4; ++k) adamw1<FASTDIV>(g[k], p[k], m[k], v[k], sc);
     Io<float>::store4(a.master + e0, true, p);
     Io<float>::store4(a.m + e0, true, m);
     Io<float>::store4(a.v + e0, true, v);
@@ -678,7 +728,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
     const int64_t hi = e0 + kEPL < a.n ? e0 + kEPL : a.n;
     for (int64_t e = e0; e < hi; ++e) {
       float p = a.master[e], m = a.m[e], v = a.v[e];
-      adamw1(a.g[e], p, m, v, sc);
+      adamw1<FASTDIV>(a.g[e], p, m, v, sc);
       a.master[e] = p;
       a.m[e] = m;
       a.v[e] = v;
@@ -719,7 +769,7 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs<ptr_ca
         float g[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (!PAD) grad_avg4<G, RT, SHIFT>(a.g, a.R, e0 + delta, k, g);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) adamw1(g[j], p[j], m[j], v[j], sc);
+        for (int j = 0; j < 4; ++j) adamw1<false>(g[j], p[j], m[j], v[j], sc);
         Io<float>::store4(a.master + e0, true, p);
         Io<float>::store4(a.m + e0, true, m);
         Io<float>::store4(a.v + e0, true, v);
@@ -728,7 +778,7 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs<ptr_ca
       [&](int64_t e) {
         const float g = PAD ? 0.0f : grad_avg1<G, RT>(a.g, a.R, e + delta);
         float p = a.master[e], m = a.m[e], v = a.v[e];
-        adamw1(g, p, m, v, sc);
+        adamw1<false>(g, p, m, v, sc);
         a.master[e] = p;
         a.m[e] = m;
         a.v[e] = v;
@@ -736,9 +786,9 @@ __device__ __forceinline__ void fused_item(const Work& w, const FusedArgs<ptr_ca
       });
 }
 
-template <typename G, typename P, int RT, bool REC>
-__device__ __forceinline__ void fused_wg(const Work& w, const FusedArgs<ptr_cap(RT)>& a) {
-  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+template <typename G, typename P, int RT>
+__device__ __forceinline__ void fused_wg(const Work& w, const FusedArgs<ptr_cap(RT)>& a,
+                                         const AdamScalars& sc) {
   const int k = static_cast<int>((((w.src - w.dst) % kEPL) + kEPL) % kEPL);
   if (w.src < 0)
     fused_item<G, P, RT, true, false>(w, a, sc, 0);
@@ -751,7 +801,8 @@ __device__ __forceinline__ void fused_wg(const Work& w, const FusedArgs<ptr_cap(
 template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused(const Work* __restrict__ work,
                                                     FusedArgs<ptr_cap(RT)> a) {
-  fused_wg<G, P, RT, REC>(work[blockIdx.x], a);
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+  fused_wg<G, P, RT>(work[blockIdx.x], a, sc);
 }
 
 // The one-element form: part b % kSplit of work item b / kSplit.  master,
@@ -761,8 +812,8 @@ template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused_one(const Work* __restrict__ work,
                                                         FusedArgs<ptr_cap(RT)> a) {
   const Work w = work[blockIdx.x / kSplit];
-  // the step's scalars first: read before any asm statement, the device
-  // record (REC) is known unclobbered and comes in the same scalar round
+  // the step's scalars (REC: the record's scalar loads, which the compiler
+  // issues after the data loads, while they are in flight)
   const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
   args_in_sgprs<RT, REC>(w, a);
   const int64_t off = static_cast<int64_t>(blockIdx.x % kSplit) * kThreads + threadIdx.x;
@@ -771,7 +822,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_one(const Work* __restrict__
   float p = One<float>::load(a.master + e), m = One<float>::load(a.m + e),
         v = One<float>::load(a.v + e);
   const float g = w.src < 0 ? 0.0f : grad_avg_one<G, RT>(a.g, a.R, w.src + off);
-  adamw1(g, p, m, v, sc);
+  adamw1<true>(g, p, m, v, sc);
   One<float>::store(a.master + e, p);
   One<float>::store(a.m + e, m);
   One<float>::store(a.v + e, v);
@@ -792,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restric
                                                            CopyArgs<ptr_cap(RT)> ca, int wide) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < n_fused) {
-    fused_wg<G, P, RT, REC>(fwork[b], fa);
+    fused_wg<G, P, RT>(fwork[b], fa, scalars_of<REC>(fa.sc, fa.scp));
     return;
   }
   const int i = b - n_fused;
@@ -933,6 +984,15 @@ unsigned adamw_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 32
 // (capped) to 27.65, 113.3 and 335.3 us, and uncapped to 27.10, 112.5 and
 // 345.5 us.
 unsigned allreduce_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 48 * 1024; }
+
+template <bool FASTDIV>
+const void* adamw_fn(int param_dt, bool rec) {
+  if (rec)
+    return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, true, FASTDIV>)
+                                 : reinterpret_cast<const void*>(&k_adamw<float, true, FASTDIV>);
+  return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, false, FASTDIV>)
+                               : reinterpret_cast<const void*>(&k_adamw<float, false, FASTDIV>);
+}
 
 template <typename G>
 const void* pick_rs(int R) {
@@ -1091,11 +1151,8 @@ hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, floa
   const int64_t chunks = (n + kEPL - 1) / kEPL;
   const int64_t blocks = (chunks + kThreads - 1) / kThreads;
   if (blocks > kMaxBlocks) return hipErrorInvalidValue;
-  const void* fn =
-      scp ? (param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, true>)
-                                   : reinterpret_cast<const void*>(&k_adamw<float, true>))
-          : (param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, false>)
-                                   : reinterpret_cast<const void*>(&k_adamw<float, false>));
+  const void* fn = blocks <= kSmallFusedLaunch ? adamw_fn<true>(param_dt, scp != nullptr)
+                                               : adamw_fn<false>(param_dt, scp != nullptr);
   void* args[] = {&a};
   return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
                        adamw_lds(blocks));

@@ -22,7 +22,11 @@ struct AdamScalars {
   double beta2, omb2;  // b2, 1 - b2
   double bc1, bc2;     // 1 - b1^t, 1 - b2^t
   double lr, eps;
+  // 1 / bc1 and 1 / bc2 as unevaluated sums hi + lo: hi the correctly
+  // rounded reciprocal, lo the correctly rounded (1 - bc hi) / bc
+  double rbc1_hi, rbc1_lo, rbc2_hi, rbc2_lo;
 };
+static_assert(sizeof(AdamScalars) == 13 * sizeof(double), "AdamScalars: 13 doubles, no padding");
 
 // Where a launcher sends its kernel: enqueued on a stream, or appended to a
 // graph under construction.  args follows hipLaunchKernel: one pointer per

@@ -709,3 +709,92 @@ def test_specials_through_the_one_element_fused_step(R):
     qnan = (pp & 0x7FFF) > 0x7F80
     assert np.array_equal((gq & 0x7FFF) > 0x7F80, qnan)
     assert_bitexact(np.where(qnan, 0, gq), np.where(qnan, 0, pp), "param")
+
+
+# AdamW hyper-parameters that give the kernels' divisions by the bias
+# corrections 1 - b1^t and 1 - b2^t many different divisors: exact
+# reciprocals (b = 1, powers of two), tiny ones (b near 2^-40) and generic
+# ones, over steps from 1 to 123,457.
+HP_SETS = [
+    dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01),
+    dict(lr=3e-4, beta1=0.95, beta2=0.98, eps=1e-6, weight_decay=0.1),
+    dict(lr=1e-2, beta1=0.5, beta2=0.9, eps=1e-12, weight_decay=0.0),
+    dict(lr=2e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.05),
+    dict(lr=1e-3, beta1=0.987654321, beta2=0.99987654321, eps=1e-8, weight_decay=0.01),
+    dict(lr=1e-3, beta1=1 - 2.0**-20, beta2=1 - 2.0**-40, eps=1e-8, weight_decay=0.01),
+]
+HP_STEPS = (1, 2, 7, 1000, 123457)
+
+
+def adamw_state(rng, po, T):
+    """Master, m and v shards with nonzero moments, and R bf16 gradient
+    replicas of which about 5% are exact zeros; the first 64 elements of
+    the unit have zero gradient, m and v (m' = v' = 0)."""
+    R = po.R
+    master = O.shard_pack(po, rng.uniform(-1, 1, T).astype(np.float32))
+    m = O.shard_pack(po, (rng.standard_normal(T) * 1e-3).astype(np.float32))
+    v = O.shard_pack(po, np.abs(rng.standard_normal(T) * 1e-6).astype(np.float32))
+    grads = []
+    for _ in range(R):
+        g = (rng.standard_normal(T) * 1e-3).astype(np.float32)
+        g[rng.random(T) < 0.05] = 0.0
+        g[:64] = 0.0
+        grads.append(O.bf16_rne(g))
+    for r in range(R):   # where rank r's shard holds the unit's first elements
+        lo = r * po.S
+        if lo < 64:
+            n = min(64 - lo, po.S)
+            m[r, :n] = 0.0
+            v[r, :n] = 0.0
+    return master, m, v, grads
+
+
+def run_three_forms(hp, t, seed):
+    """One step at step count t through the one-element fused kernel (R = 8,
+    short launch), the four-element fused kernel (R = 3) and the unfused
+    AdamW (R = 8, fp32 reduced gradient), each from its own random state,
+    checked bit for bit against the oracle (master, m, v, parameter)."""
+    shapes = [(512, 200), (777,)]
+    for R, fused in ((8, True), (3, True), (8, False)):
+        po = O.plan_layout(shapes, R, O.PER_PARAM)
+        pg = F.Plan(shapes, R, O.PER_PARAM)
+        T, S = po.T, po.S
+        rng = np.random.default_rng(seed + 10 * R + int(fused))
+        master, m, v, grads = adamw_state(rng, po, T)
+        md, m_d, v_d = to_dev(master.reshape(-1)), to_dev(m.reshape(-1)), to_dev(v.reshape(-1))
+        pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+        if fused:
+            F.fsdp_adamw_shard_step(pg, hp, t, [to_dev(g) for g in grads], md, m_d, v_d, pd)
+        else:
+            rs = O.reduce_scatter_avg(po, grads)
+            F.fsdp_adamw_shard_step(pg, hp, t, to_dev(rs.reshape(-1)), md, m_d, v_d, pd,
+                                    grads_are_replicas=False)
+        mo, mm, vv, pp = O.shard_step(po, grads, master, m, v, t, hp, "bf16")
+        tag = f"R={R} {'fused' if fused else 'unfused'} t={t} b1={hp['beta1']} b2={hp['beta2']}"
+        assert_bitexact(to_host(md).reshape(R, S), mo, "master " + tag)
+        assert_bitexact(to_host(m_d).reshape(R, S), mm, "m " + tag)
+        assert_bitexact(to_host(v_d).reshape(R, S), vv, "v " + tag)
+        assert_bitexact(to_host(pd).reshape(R, S), pp, "param " + tag)
+
+
+@pytest.mark.parametrize("k", range(len(HP_SETS)))
+def test_adamw_bias_corrections_over_hparams_and_steps(k):
+    """The division by each bias correction (a multiply and three fused
+    multiply-adds with the host's two-part reciprocal) equals IEEE division:
+    every kernel form bit for bit against the oracle over the step counts
+    1, 2, 7, 1000 and 123,457."""
+    hp = HP_SETS[k]
+    banner(f"AdamW divisions, hparams {k}: {hp}")
+    for t in HP_STEPS:
+        run_three_forms(hp, t, 1000 * k + t)
+
+
+def test_adamw_extreme_betas_take_the_ieee_division():
+    """beta1 = beta2 = 2^-1000: where the gradient is zero, m' = b1 m and
+    v' = b2 v fall below 2^-800 (v' into float64's subnormals), outside the
+    fast division's range; those lanes branch to IEEE division, mixed in one
+    wave with lanes that do not.  Bit for bit against the oracle."""
+    hp = dict(lr=1e-3, beta1=2.0**-1000, beta2=2.0**-1000, eps=1e-8, weight_decay=0.01)
+    banner("AdamW extreme betas")
+    for t in (1, 3):
+        run_three_forms(hp, t, 5000 + t)
