@@ -667,10 +667,11 @@ def test_fused_r8_above_4096_items_four_element_form(gdt):
         assert_bitexact(to_host(pd).reshape(R, S), po16, f"param t={t}")
 
 
-@pytest.mark.parametrize("R", [8, 11])
+@pytest.mark.parametrize("R", [4, 8, 11])
 def test_specials_through_the_one_element_fused_step(R):
     """NaN, +-Inf, -0 and overflow in the gradients of a short launch at
-    R >= 8 (the one-element kernel, specialised at R = 8, generic above):
+    R = 4 or R >= 8 (the one-element kernel, specialised at R = 4 and 8,
+    generic above):
     master, m, v and the parameter equal the oracle's bit for bit, NaN
     compared by class."""
     shapes = [(16, 5), (3,)]

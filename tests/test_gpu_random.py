@@ -104,7 +104,7 @@ def test_random_sequence_matches_the_oracle(seed):
         for r in recv:
             assert_bitexact(to_host(r), want, "next unit's gather")
 
-    # a third step through the standalone fused call (at R >= 8 and this
+    # a third step through the standalone fused call (at R = 4 or R >= 8 and this
     # size, the one-element kernel)
     F.fsdp_adamw_shard_step(pg, ADAMW, 3, g_d, master, m, v, param)
     mo, om, ov, po_param = O.shard_step(po, grads, mo, om, ov, 3, ADAMW, "bf16")
