@@ -3,10 +3,12 @@
 One step = for every FSDP unit of the model, in order: all-gather +
 unflatten its bf16 shards into R full-unit receivers, then the fused
 reduce-scatter-average of the R bf16 gradient replicas + AdamW on the fp32
-master/m/v shards + bf16 recast.  Default schedule "overlap": each unit's
-fused step is enqueued together with the next unit's gather (FSDP's
-prefetch; one launch per unit for units this size), into two alternating
-receive buffers.  Default workload: the 12-layer model of TransformerBlocks
+master/m/v shards + bf16 recast.  Default schedule "auto": after the
+warm-up the overlap sequence (each unit's fused step enqueued together with
+the next unit's gather, FSDP's prefetch: one launch per unit for units this
+size, into two alternating receive buffers) and the serial one are timed
+in alternating rounds on the same buffers, and the faster runs the timed
+steps; the line reports the choice and both times.  Default workload: the 12-layer model of TransformerBlocks
 (hidden 512, ffn 2048), one FSDP2 per-parameter unit per block, R = 8
 virtual ranks in one GPU's memory (37,761,024 parameters).  Inputs are
 synthetic, seeded and resident in HBM before timing starts.
@@ -41,10 +43,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="model12_r8")
-    ap.add_argument("--schedule", choices=("serial", "prefetch", "graph", "overlap",
+    ap.add_argument("--schedule", choices=("auto", "serial", "prefetch", "graph", "overlap",
                                            "graph-overlap"),
                     default=None,
-                    help="default overlap; "
+                    help="default auto: after the warm-up, time the overlap and the serial "
+                         "sequence in alternating rounds on the same buffers and keep the "
+                         "faster for the timed steps (both give the same bits); "
                          "serial: per unit gather then fused step on one stream; prefetch: "
                          "gathers on their own stream run ahead of the fused steps, into a "
                          "double receive buffer; graph: the serial sequence replayed as one "
@@ -82,7 +86,7 @@ def parse():
                          "and exit (no GPU needed)")
     args = ap.parse_args()
     if args.schedule is None:
-        args.schedule = "overlap"
+        args.schedule = "auto"
     return args
 
 
@@ -274,7 +278,7 @@ def main():
     import torch
 
     import fully_sharded_amd as F
-    from fully_sharded_amd.step import StepRunner, Unit
+    from fully_sharded_amd.step import StepRunner, Unit, choose_schedule
     from workloads import gen
     from workloads.configs import ADAMW, WORKLOADS, shapes_of
 
@@ -299,7 +303,7 @@ def main():
     n_copies = 1 if ws >= cycle else min(32, -(-cycle // ws))
     copies = [units] + [setup_units(wl, dev)[1] for _ in range(n_copies - 1)]
     T_max = max(p.T for p in plans.values())
-    n_recv = 2 if args.schedule in ("prefetch", "overlap", "graph-overlap") else 1
+    n_recv = 2 if args.schedule in ("prefetch", "overlap", "graph-overlap", "auto") else 1
     runners = []
     for cu in copies:
         recv = [rows(R, T_max, pdt, dev) for _ in range(n_recv)]
@@ -319,6 +323,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # "auto": both sequences timed on these buffers (ordinary training
+    # steps, outside the timed region), the faster one kept
+    schedule_choice = None
+    if args.schedule == "auto":
+        schedule_choice = choose_schedule(runners, step)
+        args.schedule = schedule_choice["chosen"]
+        schedule_choice["requested"] = "auto"
 
     # ----------------------------------------- timed region: the clean steps
     # K steps between two HIP events; events between blocks of them (a
@@ -371,7 +382,7 @@ def main():
     fused_avg_ms = timed(fused_pass)
     gather_avg_ms = timed(gather_pass)
     pair_avg_ms = None
-    if args.schedule in ("overlap", "graph-overlap") and len(units) > 1:
+    if hasattr(runner, "pairs") and len(units) > 1:
         pp = [0]
 
         def pair_pass():
@@ -452,12 +463,14 @@ def main():
     if pair_avg_ms is not None:
         pair_bytes = float(np.mean([fused_bytes_unit[i] + gather_bytes_unit[i + 1]
                                     for i in range(len(units) - 1)]))
-        one_launch = launches_per_step(args, units) == len(units) + 1
+        # a step of more than 65,536 work items keeps its gather in a
+        # second launch
+        one_launch = all(len(u.plan.work_items(0)) <= 65536 for u in units[:-1])
         kernels["fused_then_gather"] = {
             "avg_ms": pair_avg_ms, "bytes": pair_bytes,
             "gbps": pair_bytes / (pair_avg_ms * 1e-3) / 1e9,
             "launches": 1 if one_launch else 2}
-        if one_launch:
+        if one_launch and args.schedule in ("overlap", "graph-overlap"):
             dominant = roof_entry("fused_gather", pair_bytes, pair_avg_ms, args.workload)
     plain = plain_copy(fused_bytes, args.cycle_gib, dev, hs, reps)
     # every kernel line against a plain copy of its own bytes in one launch:
@@ -514,6 +527,7 @@ def main():
             "grad_dtype": wl["grad_dtype"],
             "state_dtype": "f32",
             "schedule": args.schedule,
+            "schedule_choice": schedule_choice,
             "gathers_per_step": args.gathers_per_step,
             "launches_per_step": launches_per_step(args, units),
             "host_calls_per_step": 2 if args.schedule in ("graph", "graph-overlap")

@@ -3,7 +3,7 @@
 AdamW + recast of its gradients ("FSDP Training Step Walkthrough", steps 1-6;
 zwjcode FSDP2 page, section 05: one communication group per block).
 
-Five schedules, same results bit for bit:
+Five schedules (and an automatic choice between two), same results bit for bit:
   serial    one stream: gather(u), step(u), gather(u+1), ...
   overlap   one stream: gather(0), then step(u) together with gather(u+1)
             (fsdp_adamw_step_then_gather: one launch for short steps), into
@@ -17,6 +17,9 @@ Five schedules, same results bit for bit:
             replayed each step with one launch
   graph-overlap  the overlap sequence (one gather per step) recorded as a
             HIP graph the same way
+  auto      built like overlap; choose_schedule then times the overlap and
+            serial sequences on the caller's own steps and keeps the faster
+            (set_schedule switches between them at any step boundary)
   prefetch  gathers on their own stream run ahead of the steps, into two
             alternating receive buffers (zwjcode FSDP2 page, section 07:
             all-gather block k+1 while block k computes, at the price of a
@@ -62,8 +65,14 @@ class StepRunner:
 
     def __init__(self, units, hp: dict, receivers, schedule: str = "serial",
                  gathers_per_step: int = 1):
-        if schedule not in ("serial", "prefetch", "graph", "overlap", "graph-overlap"):
+        if schedule not in ("serial", "prefetch", "graph", "overlap", "graph-overlap", "auto"):
             raise ValueError(schedule)
+        # "auto": the overlap schedule's resources (two receive buffers, the
+        # paired calls), so that the serial and the overlap sequence can both
+        # run; it starts as overlap
+        self.switchable = ("overlap", "serial") if schedule == "auto" else (schedule,)
+        if schedule == "auto":
+            schedule = "overlap"
         if schedule == "graph-overlap" and gathers_per_step != 1:
             raise ValueError("the graph-overlap schedule gathers once per step")
         if schedule in ("prefetch", "overlap", "graph-overlap") and len(receivers) < 2:
@@ -158,6 +167,13 @@ class StepRunner:
         self.stream.wait_stream(self.s_gather)
         self.stream.wait_stream(self.s_step)
 
+    def set_schedule(self, schedule: str) -> None:
+        """Switch between the sequences the runner was built for (an "auto"
+        runner: "overlap" and "serial"), at a step boundary."""
+        if schedule not in self.switchable:
+            raise ValueError(f"{schedule} is not one of {self.switchable}")
+        self.schedule = schedule
+
     def memory_ledger(self, param_bytes: int = 2) -> dict:
         """Bytes one rank holds ("FSDP2 ... memory peak", section 01): its
         sharded state (16 per shard element per unit), the largest unsharded
@@ -166,7 +182,36 @@ class StepRunner:
         and temporaries excluded."""
         shard = sum(u.plan.state_bytes_per_rank() for u in self.units)
         largest = max(u.plan.T for u in self.units) * param_bytes
-        prefetch = (largest if self.schedule in ("prefetch", "overlap", "graph-overlap")
-                    and len(self.units) > 1 else 0)
+        two = self.schedule in ("prefetch", "overlap", "graph-overlap") or len(self.switchable) > 1
+        prefetch = largest if two and len(self.units) > 1 else 0
         return dict(sharded_state=shard, largest_unsharded_group=largest, prefetch=prefetch,
                     peak_lower_bound=shard + largest + prefetch)
+
+
+def choose_schedule(runners, step, candidates=("overlap", "serial"), steps: int = 20,
+                    rounds: int = 3) -> dict:
+    """Time each candidate schedule on `step` (a callable running one
+    training step over `runners`, e.g. cycling buffer copies) for `steps`
+    steps, in `rounds` alternating rounds on the current stream, and switch
+    every runner to the fastest by median.  Every candidate gives the same
+    results bit for bit, so the steps run here are ordinary training steps.
+    Returns {"chosen": name, "ms_per_step": {name: [round times]}}."""
+    stream = torch.cuda.current_stream()
+    times = {c: [] for c in candidates}
+    for _ in range(rounds):
+        for c in candidates:
+            for r in runners:
+                r.set_schedule(c)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times[c].append(a.elapsed_time(b) / steps)
+    med = {c: sorted(v)[len(v) // 2] for c, v in times.items()}
+    chosen = min(candidates, key=lambda c: med[c])
+    for r in runners:
+        r.set_schedule(chosen)
+    return {"chosen": chosen, "ms_per_step": times}

@@ -32,6 +32,10 @@ def test_step_line_contract(capsys, monkeypatch):
     assert d["n_gpus"] == 1 and d["steps"] == 4 and d["warmup"] == 1
     assert d["higher_is_better"] is True and d["data"] == "synthetic"
     assert d["config"]["workload"] == "block512_r4" and d["config"]["R"] == 4
+    # the default schedule is chosen by timing: the line names the choice
+    sc = d["config"]["schedule_choice"]
+    assert sc["requested"] == "auto" and d["config"]["schedule"] == sc["chosen"]
+    assert set(sc["ms_per_step"]) == {"overlap", "serial"}
     # value is the step's parameters over its time
     assert d["value"] == pytest.approx(d["config"]["params"] / (d["ms_per_step"] * 1e-3))
     rf = d["roofline"]

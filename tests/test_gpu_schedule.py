@@ -313,3 +313,40 @@ def test_step_graph_at_world_sizes_above_eight(R, layout, schedule, ref_schedule
                 assert torch.equal(bits(recv[k][r]), bits(ref_recv[k][r])), f"step {t}"
     # the replays did the work
     assert bool((units[0].m != 0).any())
+
+
+def test_auto_schedule_choice_and_switching_keep_the_results():
+    """An "auto" runner: choose_schedule times the overlap and serial
+    sequences on ordinary steps and keeps the faster; switching between them
+    at step boundaries leaves the state bit-identical to serial steps."""
+    from fully_sharded_amd.step import choose_schedule
+    print("[gpu] auto schedule", flush=True)
+    ref_units, ref_recv = build("model12_r8", n_units=4)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial", 1)
+    units, recv = build("model12_r8", n_units=4)
+    run = StepRunner(units, ADAMW, recv, "auto", 1)
+    assert run.schedule == "overlap"
+    with pytest.raises(ValueError):
+        run.set_schedule("prefetch")
+    t = [0]
+
+    def step():
+        t[0] += 1
+        run.step(t[0])
+
+    info = choose_schedule([run], step, steps=2, rounds=2)
+    assert info["chosen"] in ("overlap", "serial") and run.schedule == info["chosen"]
+    assert all(len(v) == 2 and min(v) > 0 for v in info["ms_per_step"].values())
+    run.set_schedule("serial")
+    step()
+    run.set_schedule("overlap")
+    step()
+    assert t[0] == 10
+    for s in range(1, t[0] + 1):
+        ref.step(s)
+    torch.cuda.synchronize()
+    for a, b in zip(state_of(ref_units), state_of(units)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+    led = run.memory_ledger()
+    assert led["prefetch"] == 2 * units[0].plan.T
