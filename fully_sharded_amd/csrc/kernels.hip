@@ -270,6 +270,9 @@ __device__ __forceinline__ void args_in_sgprs(const Work& w, const A& a) {
     asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.g.p[0]), "s"(a.g.p[1]),
                  "s"(a.g.p[2]), "s"(a.g.p[3]), "s"(a.g.p[4]), "s"(a.g.p[5]), "s"(a.g.p[6]),
                  "s"(a.g.p[7]), "s"(a.master), "s"(a.m), "s"(a.v), "s"(a.param), "s"(rec));
+  } else if constexpr (RT == 3) {
+    asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.g.p[0]), "s"(a.g.p[1]),
+                 "s"(a.g.p[2]), "s"(a.master), "s"(a.m), "s"(a.v), "s"(a.param), "s"(rec));
   } else if constexpr (RT == 4) {
     asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.g.p[0]), "s"(a.g.p[1]),
                  "s"(a.g.p[2]), "s"(a.g.p[3]), "s"(a.master), "s"(a.m), "s"(a.v), "s"(a.param),
@@ -1043,6 +1046,7 @@ template <typename G, typename P, bool REC>
 const void* pick_fused_one(int R) {
   return R == 8 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 8, REC>)
        : R == 4 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 4, REC>)
+       : R == 3 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 3, REC>)
                 : reinterpret_cast<const void*>(&k_fused_one<G, P, 0, REC>);
 }
 
@@ -1056,13 +1060,14 @@ const void* fused_one_fn(int grad_dt, int param_dt, int R) {
 }
 
 // The one-element form runs short standalone fused steps (no workgroup cap)
-// with 4 or at least 8 replicas; everything else takes four elements per
-// lane.  At R = 4 (hidden-512 block, 3.1M parameters) it took the fused
-// step alone 20.7-21.5 -> 19.9-20.1 us (FSDP1 layout 20.8-23.1 -> 20.6 us),
-// alternating runs on one machine; R = 5..7 keep their measured
-// four-element instances.
+// with 3, 4 or at least 8 replicas; everything else takes four elements per
+// lane.  On the hidden-512 block (3.1M parameters), alternating runs on one
+// machine, it took the fused step alone at R = 4 from 20.7-21.5 to
+// 19.9-20.1 us (FSDP1 layout 20.8-23.1 -> 20.6 us) and at R = 3 from
+// 20.4-20.5 to 19.6-19.7 us (FSDP1 19.4-19.8 -> 19.1-19.4 us).  R = 5..7,
+// unmeasured, keep their four-element instances.
 bool fused_one_lane(int64_t n_work, int R) {
-  return (R == 4 || R >= 8) && n_work <= kSmallFusedLaunch;
+  return (R == 3 || R == 4 || R >= 8) && n_work <= kSmallFusedLaunch;
 }
 
 template <typename G, typename P, bool REC>

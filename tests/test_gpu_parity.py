@@ -667,11 +667,44 @@ def test_fused_r8_above_4096_items_four_element_form(gdt):
         assert_bitexact(to_host(pd).reshape(R, S), po16, f"param t={t}")
 
 
-@pytest.mark.parametrize("R", [4, 8, 11])
+def test_fused_r3_above_4096_items_misaligned_four_element_form():
+    """The standalone fused step at R = 3 on a two-block per-parameter unit:
+    6,147 work items, so the four-element kernel with its occupancy cap
+    (short steps at R = 3 take the one-element kernel), whose ranks after 0
+    read their gradient windows off the lane alignment (the funnelled
+    loads).  Bit for bit against the oracle, 2 steps."""
+    shapes = two_block_unit()
+    R = 3
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    items = pg.work_items(0)
+    assert len(items) > 4096
+    assert any((int(w[1]) - int(w[0])) % 4 != 0 for w in items if int(w[1]) >= 0)
+    banner(f"fused R=3 four-element form, misaligned, {len(items)} items")
+    rng = np.random.default_rng(79)
+    master = O.shard_pack(po, rng.uniform(-0.05, 0.05, T).astype(np.float32))
+    md = to_dev(master.reshape(-1))
+    m_d = torch.zeros_like(md)
+    v_d = torch.zeros_like(md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    mo, vo = np.zeros_like(master), np.zeros_like(master)
+    for t in (1, 2):
+        grads = [O.bf16_rne((rng.standard_normal(T) * 1e-3).astype(np.float32))
+                 for _ in range(R)]
+        F.fsdp_adamw_shard_step(pg, ADAMW, t, [to_dev(g) for g in grads], md, m_d, v_d, pd)
+        master, mo, vo, po16 = O.shard_step(po, grads, master, mo, vo, t, ADAMW, "bf16")
+        assert_bitexact(to_host(md).reshape(R, S), master, f"master t={t}")
+        assert_bitexact(to_host(m_d).reshape(R, S), mo, f"m t={t}")
+        assert_bitexact(to_host(v_d).reshape(R, S), vo, f"v t={t}")
+        assert_bitexact(to_host(pd).reshape(R, S), po16, f"param t={t}")
+
+
+@pytest.mark.parametrize("R", [3, 4, 8, 11])
 def test_specials_through_the_one_element_fused_step(R):
     """NaN, +-Inf, -0 and overflow in the gradients of a short launch at
-    R = 4 or R >= 8 (the one-element kernel, specialised at R = 4 and 8,
-    generic above):
+    R = 3, 4 or R >= 8 (the one-element kernel, specialised at R = 3, 4 and
+    8, generic above):
     master, m, v and the parameter equal the oracle's bit for bit, NaN
     compared by class."""
     shapes = [(16, 5), (3,)]
@@ -685,7 +718,7 @@ def test_specials_through_the_one_element_fused_step(R):
         g[0] = -0.0
     grads[0][1] = np.nan
     grads[1][2], grads[2][2] = np.inf, -np.inf
-    grads[3][3] = np.inf
+    grads[min(3, R - 1)][3] = np.inf
     for g in grads:
         g[4] = 3.0e38
     grads[0][5] = -0.0
@@ -752,11 +785,11 @@ def adamw_state(rng, po, T):
 
 def run_three_forms(hp, t, seed):
     """One step at step count t through the one-element fused kernel (R = 8,
-    short launch), the four-element fused kernel (R = 3) and the unfused
+    short launch), the four-element fused kernel (R = 5) and the unfused
     AdamW (R = 8, fp32 reduced gradient), each from its own random state,
     checked bit for bit against the oracle (master, m, v, parameter)."""
     shapes = [(512, 200), (777,)]
-    for R, fused in ((8, True), (3, True), (8, False)):
+    for R, fused in ((8, True), (5, True), (8, False)):
         po = O.plan_layout(shapes, R, O.PER_PARAM)
         pg = F.Plan(shapes, R, O.PER_PARAM)
         T, S = po.T, po.S
