@@ -215,18 +215,17 @@ struct Io<u16> {
 };
 
 // ------------------------------------------------- one element per lane
-// A second form of the fused step for short launches at R >= 8 gives each
-// lane one element (every access one naturally aligned 2- or 4-byte
-// element, so no alignment case exists) and each 1024-element work item
-// four workgroups.  A wave's float64 arithmetic after its loads return is
-// then a quarter of what it is with four elements per lane, and that
-// arithmetic of the last workgroups is what a short launch waits for at its
-// end.  Measured on MI355X, back-to-back launches on the 12-layer model's
-// 3.1M-element units (R = 8, bf16 gradients): 23.15 against 24.05 us.  With
-// fewer replicas (R = 4, 3), in the launch shared with a gather, in the
+// A second form of the fused step for short launches (R = 3, 4 or >= 8:
+// fused_one_lane) gives each lane one element (every access one naturally
+// aligned 2- or 4-byte element, so no alignment case exists) and each
+// 1024-element work item four workgroups.  A wave's float64 arithmetic
+// after its loads return is then a quarter of what it is with four elements
+// per lane, and that arithmetic of the last workgroups is what a short
+// launch waits for at its end.  Measured on MI355X, back-to-back launches
+// on the 12-layer model's 3.1M-element units (R = 8, bf16 gradients): 23.15
+// against 24.05 us.  In the launch shared with a gather, in the
 // reduce-scatter and AdamW kernels alone and in long capped launches, four
-// elements per lane were faster (R = 4 block: 21.2 against 22.1 us; the
-// paired launch 31.9 against 32.5 us).
+// elements per lane stayed faster (the paired launch 31.8 against 32.1 us).
 template <typename T>
 struct One;
 template <>
