@@ -112,9 +112,9 @@ TRAFFIC_KERNELS = {
     "fused": (("::k_fused<", "::k_fused_one<"),
               "k_fused / k_fused_one (fused reduce-scatter-average + AdamW + bf16 recast, "
               "alone)"),
-    "fused_gather": (("::k_fused_gather<",),
-                     "k_fused_gather (one unit's fused step, then the next unit's gather, in "
-                     "one launch)"),
+    "fused_gather": (("::k_fused_two_gather<", "::k_fused_gather<"),
+                     "k_fused_two_gather / k_fused_gather (one unit's fused step, then the "
+                     "next unit's gather, in one launch)"),
     "allreduce": (("::k_allreduce<",), "k_allreduce (DDP all-reduce-average to R receivers)"),
     "adamw": (("::k_adamw<",), "k_adamw (AdamW + recast on an fp32 gradient)"),
     "gather": (("::k_copy<2, 16, 8, 8>",),

@@ -20,8 +20,8 @@
 //   * long fused, unfused AdamW and all-reduce launches cap their resident
 //     workgroups per CU (fused_lds, adamw_lds, allreduce_lds), and a short
 //     fused step can share its
-//     launch with the next unit's gather (k_fused_gather), which then
-//     starts while the step drains.
+//     launch with the next unit's gather (k_fused_two_gather at R >= 8,
+//     else k_fused_gather), which then starts while the step drains.
 //
 // Reductions are fp32, in rank order 0..R-1 starting from rank 0's value,
 // then one correctly rounded division by R: one lane owns an element and
@@ -223,9 +223,10 @@ struct Io<u16> {
 // per lane, and that arithmetic of the last workgroups is what a short
 // launch waits for at its end.  Measured on MI355X, back-to-back launches
 // on the 12-layer model's 3.1M-element units (R = 8, bf16 gradients): 23.15
-// against 24.05 us.  In the launch shared with a gather, in the
-// reduce-scatter and AdamW kernels alone and in long capped launches, four
-// elements per lane stayed faster (the paired launch 31.8 against 32.1 us).
+// against 24.05 us.  In the reduce-scatter and AdamW kernels alone and in
+// long capped launches four elements per lane stayed faster, and in the
+// launch shared with a gather two elements per lane (31.3 us, against 31.8
+// with one or four).
 template <typename T>
 struct One;
 template <>
@@ -387,10 +388,11 @@ __device__ __forceinline__ double div_bias(double a, double b, double hi, double
 // (FASTDIV false) or div_bias (true): the same bits, 55 instead of 65
 // double operations per element.  Which one a kernel takes was measured on
 // MI355X in alternating runs of both: div_bias made the one-element fused
-// step 1% and the short unfused AdamW 2-4% faster; in the four-element
-// fused forms it gained nothing on the 872M-parameter group (within 0.5%)
-// and made the step-and-gather launch slower (31.9-32.2 against 31.7-32.0
-// us), so those and the long AdamW launches keep IEEE division.
+// step 1%, the short unfused AdamW 2-4% and the two-element step-and-gather
+// launch 0.6% faster; in the four-element fused forms it gained nothing on
+// the 872M-parameter group (within 0.5%) and made their step-and-gather
+// launch slower (31.9-32.2 against 31.7-32.0 us), so those and the long
+// AdamW launches keep IEEE division.
 template <bool FASTDIV>
 __device__ __forceinline__ void adamw1(float gf, float& pf, float& mf, float& vf,
                                        const AdamScalars& c) {
@@ -835,12 +837,77 @@ __global__ __launch_bounds__(kThreads) void k_fused_one(const Work* __restrict__
   One<P>::store(static_cast<P*>(a.param) + e, p);
 }
 
+// The fused step with NE elements per lane at off, off + 256, ...: each
+// 1024-element work item takes 1024 / (256 NE) workgroups; every access is
+// one naturally aligned element.  A lane past the end of its item reloads
+// its first element (in range) and skips the stores.  FD: the division of
+// div_bias (else IEEE division).
+template <typename G, typename P, int RT, bool REC, int NE, bool FD>
+__device__ __forceinline__ void fused_ne_wg(const Work* __restrict__ work,
+                                            const FusedArgs<ptr_cap(RT)>& a, int b) {
+  constexpr int kS = 1024 / (kThreads * NE);
+  const Work w = work[b / kS];
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+  args_in_sgprs<RT, REC>(w, a);
+  const int64_t base = static_cast<int64_t>(b % kS) * kThreads * NE + threadIdx.x;
+  if (base >= w.len) return;
+  float p[NE], m[NE], v[NE], g[NE];
+  int64_t off[NE];
+  bool ok[NE];
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    const int64_t o = base + j * kThreads;
+    ok[j] = o < w.len;
+    off[j] = ok[j] ? o : base;
+    const int64_t e = w.dst + off[j];
+    p[j] = One<float>::load(a.master + e);
+    m[j] = One<float>::load(a.m + e);
+    v[j] = One<float>::load(a.v + e);
+  }
+#pragma unroll
+  for (int j = 0; j < NE; ++j)
+    g[j] = w.src < 0 ? 0.0f : grad_avg_one<G, RT>(a.g, a.R, w.src + off[j]);
+#pragma unroll
+  for (int j = 0; j < NE; ++j) adamw1<FD>(g[j], p[j], m[j], v[j], sc);
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    if (!ok[j]) continue;
+    const int64_t e = w.dst + off[j];
+    One<float>::store(a.master + e, p[j]);
+    One<float>::store(a.m + e, m[j]);
+    One<float>::store(a.v + e, v[j]);
+    One<P>::store(static_cast<P*>(a.param) + e, p[j]);
+  }
+}
+
 // The fused step of one unit and the gather of another in one launch:
 // workgroups [0, n_fused) take the step's work items, the rest the
 // gather's, in that order.  Dispatch follows the workgroup order, so the
 // gather starts while the step's last workgroups drain instead of after
 // them.  wide: 16-byte gather lanes (else 8).  The gather copies the
 // parameter dtype P.
+// The pairing with the fused step in the two-element form (fused_ne_wg,
+// NE = 2, div_bias): workgroups [0, n_fused) are two per work item of the
+// step.  On the 12-layer model's units at R = 8, alternating runs on two
+// machines: 31.3-31.4 us against 31.7-31.8 us for the four-element form
+// (31.5 with IEEE division), the step 377.5-378.1 against 381.3-381.9 us;
+// four elements per lane strided by 256 took 32.1 us.
+template <typename G, typename P, int RT, bool REC>
+__global__ __launch_bounds__(kThreads) void k_fused_two_gather(
+    const Work* __restrict__ fwork, FusedArgs<ptr_cap(RT)> fa, int n_fused,
+    const Work* __restrict__ gwork, CopyArgs<ptr_cap(RT)> ca, int wide) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < n_fused) {
+    fused_ne_wg<G, P, RT, REC, 2, true>(fwork, fa, b);
+    return;
+  }
+  const int i = b - n_fused;
+  if (wide)
+    copy_item<sizeof(P), 16, ptr_cap(RT), kSmallPtrs>(gwork[i], ca, static_cast<unsigned>(i));
+  else
+    copy_item<sizeof(P), 8>(gwork[i], ca, static_cast<unsigned>(i));
+}
+
 template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused_gather(const Work* __restrict__ fwork,
                                                            FusedArgs<ptr_cap(RT)> fa,
@@ -1093,6 +1160,21 @@ const void* fused_fn(int grad_dt, int param_dt, int R) {
   return param_dt == FSDP_BF16 ? pick_fused<float, u16, REC>(R) : pick_fused<float, float, REC>(R);
 }
 
+template <typename G, typename P, bool REC>
+const void* pick_fused_two_gather(int R) {
+  return R == 8 ? reinterpret_cast<const void*>(&k_fused_two_gather<G, P, 8, REC>)
+                : reinterpret_cast<const void*>(&k_fused_two_gather<G, P, 0, REC>);
+}
+
+template <bool REC>
+const void* fused_two_gather_fn(int grad_dt, int param_dt, int R) {
+  if (grad_dt == FSDP_BF16)
+    return param_dt == FSDP_BF16 ? pick_fused_two_gather<u16, u16, REC>(R)
+                                 : pick_fused_two_gather<u16, float, REC>(R);
+  return param_dt == FSDP_BF16 ? pick_fused_two_gather<float, u16, REC>(R)
+                               : pick_fused_two_gather<float, float, REC>(R);
+}
+
 template <bool REC>
 const void* fused_gather_fn(int grad_dt, int param_dt, int R) {
   if (grad_dt == FSDP_BF16)
@@ -1284,12 +1366,18 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                                const void* shards, const PtrArray& dst, int n_dst,
                                int lane_bytes, bool vec_g, const Sink& stream) {
   if (n_fused <= 0 || n_gather <= 0 || n_dst < 1) return hipErrorInvalidValue;
-  if (n_fused + n_gather > kMaxBlocks) return hipErrorInvalidValue;
-  int nf = static_cast<int>(n_fused);
+  // short steps at R >= 8: the two-element form, two workgroups per item
+  const bool two = R >= 8 && n_fused <= kSmallFusedLaunch;
+  const int64_t fused_blocks = two ? n_fused * 2 : n_fused;
+  if (fused_blocks + n_gather > kMaxBlocks) return hipErrorInvalidValue;
+  int nf = static_cast<int>(fused_blocks);
   int wide = lane_bytes == 16 ? 1 : 0;
-  const void* fn = scp ? fused_gather_fn<true>(grad_dt, param_dt, R)
-                       : fused_gather_fn<false>(grad_dt, param_dt, R);
-  const dim3 grid(static_cast<unsigned>(n_fused + n_gather));
+  const void* fn = two ? (scp ? fused_two_gather_fn<true>(grad_dt, param_dt, R)
+                              : fused_two_gather_fn<false>(grad_dt, param_dt, R))
+                       : (scp ? fused_gather_fn<true>(grad_dt, param_dt, R)
+                              : fused_gather_fn<false>(grad_dt, param_dt, R));
+  const unsigned lds = two ? 0 : fused_lds(n_fused);
+  const dim3 grid(static_cast<unsigned>(fused_blocks + n_gather));
   if (R <= kSmallPtrs) {   // the specialised kernel: 8 slots for both arrays
     if (n_dst > kSmallPtrs) return hipErrorInvalidValue;
     FusedArgs<kSmallPtrs> fa{narrow<kSmallPtrs>(grads), master, m, v, param, sc, scp, R,
@@ -1297,13 +1385,13 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
     CopyArgs<kSmallPtrs> ca{shards, narrow<kSmallPtrs>(dst), n_dst, vec_g ? 1 : 0};
     void* args[] = {const_cast<Work**>(&fwork), &fa, &nf, const_cast<Work**>(&gwork), &ca,
                     &wide};
-    return stream.launch(fn, grid, dim3(kThreads), args, fused_lds(n_fused));
+    return stream.launch(fn, grid, dim3(kThreads), args, lds);
   }
   FusedArgs<FSDP_MAX_RANKS> fa{narrow<FSDP_MAX_RANKS>(grads), master, m, v, param, sc, scp, R,
                                vec_f ? 1 : 0};
   CopyArgs<FSDP_MAX_RANKS> ca{shards, narrow<FSDP_MAX_RANKS>(dst), n_dst, vec_g ? 1 : 0};
   void* args[] = {const_cast<Work**>(&fwork), &fa, &nf, const_cast<Work**>(&gwork), &ca, &wide};
-  return stream.launch(fn, grid, dim3(kThreads), args, fused_lds(n_fused));
+  return stream.launch(fn, grid, dim3(kThreads), args, lds);
 }
 
 }  // namespace fsdp
