@@ -888,10 +888,13 @@ __device__ __forceinline__ void fused_ne_wg(const Work* __restrict__ work,
 // parameter dtype P.
 // The pairing with the fused step in the two-element form (fused_ne_wg,
 // NE = 2, div_bias): workgroups [0, n_fused) are two per work item of the
-// step.  On the 12-layer model's units at R = 8, alternating runs on two
-// machines: 31.3-31.4 us against 31.7-31.8 us for the four-element form
-// (31.5 with IEEE division), the step 377.5-378.1 against 381.3-381.9 us;
-// four elements per lane strided by 256 took 32.1 us.
+// step.  On the 12-layer model's per-parameter units at R = 8, alternating
+// runs on three machines: 31.3-31.4 us against 31.7-31.8 us for the
+// four-element form (31.5 with IEEE division), the step 376.7-378.1
+// against 381.3-381.9 us; four elements per lane strided by 256 took 32.1
+// us.  Over one contiguous gradient range per rank (FSDP1 units) the
+// four-element form stayed faster (step 377.3-378.8 against 379.1-382.2
+// us), so only scattered windows take this form.
 template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused_two_gather(
     const Work* __restrict__ fwork, FusedArgs<ptr_cap(RT)> fa, int n_fused,
@@ -1362,12 +1365,13 @@ hipError_t StreamSink::launch(const void* fn, dim3 grid, dim3 block, void** args
 hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArray& grads, int R,
                                int grad_dt, float* master, float* m, float* v, void* param,
                                int param_dt, const AdamScalars& sc, const AdamScalars* scp,
-                               bool vec_f, const Work* gwork, int64_t n_gather,
+                               bool vec_f, bool scattered, const Work* gwork, int64_t n_gather,
                                const void* shards, const PtrArray& dst, int n_dst,
                                int lane_bytes, bool vec_g, const Sink& stream) {
   if (n_fused <= 0 || n_gather <= 0 || n_dst < 1) return hipErrorInvalidValue;
-  // short steps at R >= 8: the two-element form, two workgroups per item
-  const bool two = R >= 8 && n_fused <= kSmallFusedLaunch;
+  // short steps at R >= 8 over scattered gradient windows: the two-element
+  // form, two workgroups per item
+  const bool two = scattered && R >= 8 && n_fused <= kSmallFusedLaunch;
   const int64_t fused_blocks = two ? n_fused * 2 : n_fused;
   if (fused_blocks + n_gather > kMaxBlocks) return hipErrorInvalidValue;
   int nf = static_cast<int>(fused_blocks);
