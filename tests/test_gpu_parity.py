@@ -832,3 +832,46 @@ def test_adamw_extreme_betas_take_the_ieee_division():
     banner("AdamW extreme betas")
     for t in (1, 3):
         run_three_forms(hp, t, 5000 + t)
+
+
+@pytest.mark.parametrize("layout", [O.PER_PARAM, O.FLAT])
+def test_sharded_step_equals_the_single_card_step(layout):
+    """The equivalence check the FSDP2 page recommends (section 12: one card
+    against the sharded ranks, the shards gathered back), on the GPU and
+    through the library alone: R = 4 ranks stepping their shards on the R
+    gradient replicas, then gathering master and parameter back to full
+    tensors, equal bit for bit the R = 1 step on the rank-order mean of the
+    replicas (the all-reduce's output), over 3 steps."""
+    shapes = [(512, 96), (96, 130), (130,)]
+    R = 4
+    p4 = F.Plan(shapes, R, layout)
+    p1 = F.Plan(shapes, 1, layout)
+    T = p4.T
+    banner(f"sharded vs single-card step, {layout}")
+    rng = np.random.default_rng(123)
+    full = torch.from_numpy(rng.uniform(-0.1, 0.1, T).astype(np.float32)).to(DEV)
+    # R ranks: shards of master, m, v, parameter
+    m4 = torch.empty(R * p4.S, device=DEV)
+    F.fsdp_shard_pack(p4, full, m4)
+    mm4, vv4 = torch.zeros_like(m4), torch.zeros_like(m4)
+    pp4 = torch.empty(R * p4.S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_shard_pack(p4, full, pp4)
+    # one card: the full tensors
+    m1 = full.clone()
+    mm1, vv1 = torch.zeros_like(m1), torch.zeros_like(m1)
+    pp1 = torch.empty(T, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_shard_pack(p1, full, pp1)
+    for t in (1, 2, 3):
+        grads = [to_dev(O.bf16_rne((rng.standard_normal(T) * 1e-3).astype(np.float32)))
+                 for _ in range(R)]
+        avg = [torch.empty(T, device=DEV) for _ in range(R)]
+        F.fsdp_allreduce_avg(p4, grads, avg)
+        F.fsdp_adamw_shard_step(p4, ADAMW, t, grads, m4, mm4, vv4, pp4)
+        F.fsdp_adamw_shard_step(p1, ADAMW, t, avg[0], m1, mm1, vv1, pp1,
+                                grads_are_replicas=False)
+        for shards, one, dt in ((m4, m1, torch.float32), (mm4, mm1, torch.float32),
+                                (vv4, vv1, torch.float32), (pp4, pp1, torch.bfloat16)):
+            back = [torch.empty(T, dtype=dt, device=DEV)]
+            F.fsdp_gather_unflatten(p4, shards, back + [None] * (R - 1))
+            torch.cuda.synchronize()
+            assert_bitexact(to_host(back[0]), to_host(one), f"{layout} t={t} {dt}")
