@@ -315,16 +315,19 @@ def test_step_graph_at_world_sizes_above_eight(R, layout, schedule, ref_schedule
     assert bool((units[0].m != 0).any())
 
 
-def test_auto_schedule_choice_and_switching_keep_the_results():
+@pytest.mark.parametrize("gathers", [1, 2])
+def test_auto_schedule_choice_and_switching_keep_the_results(gathers):
     """An "auto" runner: choose_schedule times the overlap and serial
     sequences on ordinary steps and keeps the faster; switching between them
-    at step boundaries leaves the state bit-identical to serial steps."""
+    at step boundaries leaves the state bit-identical to serial steps (with
+    two gathers per step the overlap sequence runs the backward from the
+    last unit)."""
     from fully_sharded_amd.step import choose_schedule
-    print("[gpu] auto schedule", flush=True)
+    print(f"[gpu] auto schedule, {gathers} gathers", flush=True)
     ref_units, ref_recv = build("model12_r8", n_units=4)
-    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial", 1)
+    ref = StepRunner(ref_units, ADAMW, ref_recv, "serial", gathers)
     units, recv = build("model12_r8", n_units=4)
-    run = StepRunner(units, ADAMW, recv, "auto", 1)
+    run = StepRunner(units, ADAMW, recv, "auto", gathers)
     assert run.schedule == "overlap"
     with pytest.raises(ValueError):
         run.set_schedule("prefetch")
