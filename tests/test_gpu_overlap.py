@@ -84,7 +84,7 @@ def assert_same(x, y):
 
 @pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "capped_pair",
                                   "capped_pair_flat", "short_mixed_world", "mixed_world_wide",
-                                  "wide_world", "f32_grads_bf16_params"])
+                                  "wide_world", "f32_grads_bf16_params", "f32_params_r8"])
 def test_pair_equals_the_two_calls(case):
     print(f"[gpu] step_then_gather {case}", flush=True)
     blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
@@ -104,6 +104,9 @@ def test_pair_equals_the_two_calls(case):
     elif case == "f32_grads_bf16_params":  # e.g. accumulated fp32 gradients
         a = HostUnit(blk, 8, "per_param", 17, pdt="bf16", gdt="f32")
         b = HostUnit(blk, 8, "per_param", 18)
+    elif case == "f32_params_r8":     # fp32 parameters, scattered windows at R = 8
+        a = HostUnit(blk, 8, "per_param", 19, pdt="f32")
+        b = HostUnit(lin, 8, "per_param", 21, pdt="f32")
     elif case == "capped_pair":       # > 4,096 work items: one launch, 4 per CU
         a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
     else:                             # capped_pair_flat
