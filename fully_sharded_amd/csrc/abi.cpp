@@ -287,8 +287,7 @@ fsdp_status adamw_gather_impl(const fsdp_plan* plan, const AdamScalars& sc,
     return st != FSDP_OK ? st : launch(g, next->R, sink);
   }
   return status_of(launch_fused_gather(a.w, a.n_work, a.g, plan->R, grad_dtype, master, m, v,
-                                       param_out, param_dtype, sc, scp, a.vec,
-                                       plan->shard_src_scattered, g.w, g.n_work,
+                                       param_out, param_dtype, sc, scp, a.vec, g.w, g.n_work,
                                        g.src, g.dst, next->R, g.lane_bytes, g.vec, sink));
 }
 

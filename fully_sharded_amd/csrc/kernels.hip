@@ -8,7 +8,10 @@
 //   * the arithmetic kernels move 4 consecutive elements per lane per pass
 //     (8-byte bf16 and 16-byte fp32 accesses), the copy kernels 16 bytes per
 //     lane; 4 elements per lane beat 8 because twice as many waves keep
-//     requests in flight for the same registers;
+//     requests in flight for the same registers.  The fused step takes one
+//     element per lane in short launches of its own (k_fused_one) and two
+//     adjacent ones in the launch it shares with a gather at R >= 8
+//     (k_fused_two_gather), where those measured faster;
 //   * every streaming access is nontemporal: the data is touched once, and
 //     keeping it out of the caches raised the fused kernel from 4.8 to
 //     5.6 TB/s in isolation (the overlapping word pairs of misaligned
@@ -18,10 +21,10 @@
 //     whose chunk is cut by the ends of the range take an element-by-element
 //     path with the same arithmetic;
 //   * long fused, unfused AdamW and all-reduce launches cap their resident
-//     workgroups per CU (fused_lds, adamw_lds, allreduce_lds), and a short
-//     fused step can share its
-//     launch with the next unit's gather (k_fused_two_gather at R >= 8,
-//     else k_fused_gather), which then starts while the step drains.
+//     workgroups per CU (fused_lds, adamw_lds, allreduce_lds), and a fused
+//     step of up to 65,536 work items can share its launch with the next
+//     unit's gather (k_fused_two_gather at R >= 8, else k_fused_gather),
+//     which then starts while the step drains.
 //
 // Reductions are fp32, in rank order 0..R-1 starting from rank 0's value,
 // then one correctly rounded division by R: one lane owns an element and
@@ -225,8 +228,8 @@ struct Io<u16> {
 // on the 12-layer model's 3.1M-element units (R = 8, bf16 gradients): 23.15
 // against 24.05 us.  In the reduce-scatter and AdamW kernels alone and in
 // long capped launches four elements per lane stayed faster, and in the
-// launch shared with a gather two elements per lane (31.3 us, against 31.8
-// with one or four).
+// launch shared with a gather two adjacent elements per lane (31.2 us,
+// against 31.8 with one or four).
 template <typename T>
 struct One;
 template <>
@@ -245,6 +248,34 @@ struct One<u16> {
   }
   __device__ __forceinline__ static void store(u16* p, float x) {
     __builtin_nontemporal_store(static_cast<u16>(f32_to_bf16(x)), p);
+  }
+};
+
+// Two adjacent elements [e, e + 2) of T <-> 2 floats, e even: one naturally
+// aligned nontemporal access of 4 (bf16) or 8 (fp32) bytes.
+template <typename T>
+struct Two;
+template <>
+struct Two<float> {
+  __device__ __forceinline__ static void load(const float* p, float (&x)[2]) {
+    const u32x2 u = ld_nt8(p);
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&x)[2]) {
+    st_nt8(p, u32x2{__float_as_uint(x[0]), __float_as_uint(x[1])});
+  }
+};
+template <>
+struct Two<u16> {
+  __device__ __forceinline__ static void load(const u16* p, float (&x)[2]) {
+    const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    x[0] = __uint_as_float(u << 16);
+    x[1] = __uint_as_float(u & 0xffff0000u);
+  }
+  __device__ __forceinline__ static void store(u16* p, const float (&x)[2]) {
+    __builtin_nontemporal_store(f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16),
+                                reinterpret_cast<uint32_t*>(p));
   }
 };
 
@@ -300,6 +331,36 @@ __device__ __forceinline__ float grad_avg_one(const PA& g, int R, int64_t s) {
 #pragma unroll 8
     for (int q = 1; q < R; ++q) acc = acc + One<G>::load(static_cast<const G*>(g.p[q]) + s);
     return acc / static_cast<float>(R);
+  }
+}
+
+// The same for the two adjacent elements s, s + 1 (s even), each replica's
+// pair in one access.
+template <typename G, int RT, typename PA>
+__device__ __forceinline__ void grad_avg_two(const PA& g, int R, int64_t s, float (&avg)[2]) {
+  if constexpr (RT > 0) {
+    float x[RT][2];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) Two<G>::load(static_cast<const G*>(g.p[q]) + s, x[q]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float acc = x[0][j];
+#pragma unroll
+      for (int q = 1; q < RT; ++q) acc = acc + x[q][j];
+      avg[j] = acc / static_cast<float>(RT);
+    }
+  } else {
+    float acc[2];
+    Two<G>::load(static_cast<const G*>(g.p[0]) + s, acc);
+#pragma unroll 8
+    for (int q = 1; q < R; ++q) {
+      float x[2];
+      Two<G>::load(static_cast<const G*>(g.p[q]) + s, x);
+      acc[0] = acc[0] + x[0];
+      acc[1] = acc[1] + x[1];
+    }
+    avg[0] = acc[0] / static_cast<float>(R);
+    avg[1] = acc[1] / static_cast<float>(R);
   }
 }
 
@@ -880,28 +941,64 @@ __device__ __forceinline__ void fused_ne_wg(const Work* __restrict__ work,
   }
 }
 
+// The fused step with two adjacent elements per lane: workgroup b takes
+// elements [512 (b % 2), + 512) of work item b / 2, lane t the pair at
+// 2t, so every state, gradient and parameter access moves a lane's two
+// elements at once (8 or 4 bytes, naturally aligned).  That needs an even
+// destination offset, length and source offset; an item without them (an
+// odd-sized piece of a parameter) takes fused_ne_wg's two strided
+// elements, on the same workgroup-to-item mapping.  div_bias divides.
+template <typename G, typename P, int RT, bool REC>
+__device__ __forceinline__ void fused_pair_wg(const Work* __restrict__ work,
+                                              const FusedArgs<ptr_cap(RT)>& a, int b) {
+  const Work w = work[b / 2];
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+  args_in_sgprs<RT, REC>(w, a);
+  const bool even = ((w.dst | w.len) & 1) == 0 && (w.src < 0 || (w.src & 1) == 0);
+  if (!even) {
+    fused_ne_wg<G, P, RT, REC, 2, true>(work, a, b);
+    return;
+  }
+  const int64_t off = static_cast<int64_t>(b % 2) * (2 * kThreads) + 2 * threadIdx.x;
+  if (off >= w.len) return;
+  const int64_t e = w.dst + off;
+  float p[2], m[2], v[2], g[2] = {0.0f, 0.0f};
+  Two<float>::load(a.master + e, p);
+  Two<float>::load(a.m + e, m);
+  Two<float>::load(a.v + e, v);
+  if (w.src >= 0) grad_avg_two<G, RT>(a.g, a.R, w.src + off, g);
+  adamw1<true>(g[0], p[0], m[0], v[0], sc);
+  adamw1<true>(g[1], p[1], m[1], v[1], sc);
+  Two<float>::store(a.master + e, p);
+  Two<float>::store(a.m + e, m);
+  Two<float>::store(a.v + e, v);
+  Two<P>::store(static_cast<P*>(a.param) + e, p);
+}
+
 // The fused step of one unit and the gather of another in one launch:
 // workgroups [0, n_fused) take the step's work items, the rest the
 // gather's, in that order.  Dispatch follows the workgroup order, so the
 // gather starts while the step's last workgroups drain instead of after
 // them.  wide: 16-byte gather lanes (else 8).  The gather copies the
 // parameter dtype P.
-// The pairing with the fused step in the two-element form (fused_ne_wg,
-// NE = 2, div_bias): workgroups [0, n_fused) are two per work item of the
-// step.  On the 12-layer model's per-parameter units at R = 8, alternating
-// runs on three machines: 31.3-31.4 us against 31.7-31.8 us for the
-// four-element form (31.5 with IEEE division), the step 376.7-378.1
-// against 381.3-381.9 us; four elements per lane strided by 256 took 32.1
-// us.  Over one contiguous gradient range per rank (FSDP1 units) the
-// four-element form stayed faster (step 377.3-378.8 against 379.1-382.2
-// us), so only scattered windows take this form.
+// The pairing with the fused step in the two-element form (fused_pair_wg,
+// adjacent pairs, div_bias): workgroups [0, n_fused) are two per work item
+// of the step.  On the 12-layer model's per-parameter units at R = 8,
+// alternating runs on one machine: 31.2 us against 31.35 with two elements
+// strided by 256 (fused_ne_wg) and 31.7-31.8 with four per lane, the step
+// 375.5-375.6 against 377.5-377.8 us (two strided) and 381.3-381.9 (four).
+// Two strided elements had lost to four on FSDP1 units and on longer steps;
+// adjacent pairs gain there too: the FSDP1 12-layer step 374.3-374.4
+// against 374.8-375.5 us, the model in 4-block units (12,520 items, capped
+// at 4 per CU) 381.3-381.6 against 382.9-383.6 us; in 2-block units (6,260
+// items) 376.3-376.8 against 375.9-376.4 us.
 template <typename G, typename P, int RT, bool REC>
 __global__ __launch_bounds__(kThreads) void k_fused_two_gather(
     const Work* __restrict__ fwork, FusedArgs<ptr_cap(RT)> fa, int n_fused,
     const Work* __restrict__ gwork, CopyArgs<ptr_cap(RT)> ca, int wide) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < n_fused) {
-    fused_ne_wg<G, P, RT, REC, 2, true>(fwork, fa, b);
+    fused_pair_wg<G, P, RT, REC>(fwork, fa, b);
     return;
   }
   const int i = b - n_fused;
@@ -1365,13 +1462,12 @@ hipError_t StreamSink::launch(const void* fn, dim3 grid, dim3 block, void** args
 hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArray& grads, int R,
                                int grad_dt, float* master, float* m, float* v, void* param,
                                int param_dt, const AdamScalars& sc, const AdamScalars* scp,
-                               bool vec_f, bool scattered, const Work* gwork, int64_t n_gather,
+                               bool vec_f, const Work* gwork, int64_t n_gather,
                                const void* shards, const PtrArray& dst, int n_dst,
                                int lane_bytes, bool vec_g, const Sink& stream) {
   if (n_fused <= 0 || n_gather <= 0 || n_dst < 1) return hipErrorInvalidValue;
-  // short steps at R >= 8 over scattered gradient windows: the two-element
-  // form, two workgroups per item
-  const bool two = scattered && R >= 8 && n_fused <= kSmallFusedLaunch;
+  // R >= 8: the two-element form of the step, two workgroups per item
+  const bool two = R >= 8;
   const int64_t fused_blocks = two ? n_fused * 2 : n_fused;
   if (fused_blocks + n_gather > kMaxBlocks) return hipErrorInvalidValue;
   int nf = static_cast<int>(fused_blocks);
@@ -1380,7 +1476,7 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                               : fused_two_gather_fn<false>(grad_dt, param_dt, R))
                        : (scp ? fused_gather_fn<true>(grad_dt, param_dt, R)
                               : fused_gather_fn<false>(grad_dt, param_dt, R));
-  const unsigned lds = two ? 0 : fused_lds(n_fused);
+  const unsigned lds = fused_lds(n_fused);
   const dim3 grid(static_cast<unsigned>(fused_blocks + n_gather));
   if (R <= kSmallPtrs) {   // the specialised kernel: 8 slots for both arrays
     if (n_dst > kSmallPtrs) return hipErrorInvalidValue;

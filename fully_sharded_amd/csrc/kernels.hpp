@@ -99,13 +99,10 @@ hipError_t launch_set_scalars(AdamScalars* dst, const AdamScalars& sc, const Sin
 // launch_fused's step of one unit (n_fused work items), then in the same
 // launch launch_copy's gather of another (n_gather items, n_dst
 // destinations, elements of the parameter dtype).  Both counts > 0.
-// scattered: the step's pieces read scattered gradient windows (the plan's
-// shard_src_scattered), which selects the two-element form of the step at
-// R >= 8.
 hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArray& grads, int R,
                                int grad_dt, float* master, float* m, float* v, void* param,
                                int param_dt, const AdamScalars& sc, const AdamScalars* scp,
-                               bool vec_f, bool scattered, const Work* gwork, int64_t n_gather,
+                               bool vec_f, const Work* gwork, int64_t n_gather,
                                const void* shards, const PtrArray& dst, int n_dst,
                                int lane_bytes, bool vec_g, const Sink& stream);
 

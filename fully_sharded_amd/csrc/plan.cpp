@@ -156,14 +156,6 @@ fsdp_status build_plan(fsdp_plan* pl) {
   }
   if (count_items(pl->shard_runs, kShardChunk) > kMaxItems) return FSDP_ERR_UNSUPPORTED;
   emit_items(pl->shard_runs, kShardChunk, pl->shard_work.host);
-  {
-    int64_t next_src = -1;  // where the previous piece's source ended
-    for (const Work& w : pl->shard_runs) {
-      if (w.src < 0) continue;
-      if (next_src >= 0 && w.src != next_src) pl->shard_src_scattered = true;
-      next_src = w.src + w.len;
-    }
-  }
 
   // flat-space runs: the same segments ordered by flat offset; they tile
   // [0, T) exactly

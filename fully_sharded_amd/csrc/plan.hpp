@@ -73,9 +73,6 @@ struct fsdp_plan {
   fsdp::WorkTable shard_work;           // shard_runs cut into work items
   fsdp::WorkTable flat_work;            // flat_runs cut into work items
   int32_t gather_lane_bytes = 16;       // bytes per lane of the gather copy
-  // the shard space's pieces, in order, do not read one contiguous range of
-  // the gradient (per-parameter pieces: one window per parameter and rank)
-  bool shard_src_scattered = false;
 };
 
 struct fsdp_resharder {

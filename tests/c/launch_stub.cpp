@@ -43,8 +43,7 @@ hipError_t launch_set_scalars(AdamScalars*, const AdamScalars&, const Sink&) {
 }
 hipError_t launch_fused_gather(const Work*, int64_t, const PtrArray&, int, int, float*, float*,
                                float*, void*, int, const AdamScalars&, const AdamScalars*, bool,
-                               bool, const Work*, int64_t, const void*, const PtrArray&, int, int,
-                               bool,
+                               const Work*, int64_t, const void*, const PtrArray&, int, int, bool,
                                const Sink&) {
   return hipErrorNoDevice;
 }

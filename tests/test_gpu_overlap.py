@@ -84,7 +84,8 @@ def assert_same(x, y):
 
 @pytest.mark.parametrize("case", ["short_bf16", "short_ragged_r3", "short_fp32", "capped_pair",
                                   "capped_pair_flat", "short_mixed_world", "mixed_world_wide",
-                                  "wide_world", "f32_grads_bf16_params", "f32_params_r8"])
+                                  "wide_world", "f32_grads_bf16_params", "f32_params_r8",
+                                  "flat_r16", "odd_pieces_r9"])
 def test_pair_equals_the_two_calls(case):
     print(f"[gpu] step_then_gather {case}", flush=True)
     blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
@@ -107,6 +108,10 @@ def test_pair_equals_the_two_calls(case):
     elif case == "f32_params_r8":     # fp32 parameters, scattered windows at R = 8
         a = HostUnit(blk, 8, "per_param", 19, pdt="f32")
         b = HostUnit(lin, 8, "per_param", 21, pdt="f32")
+    elif case == "flat_r16":          # R > 8, every item even: adjacent pairs, 64 slots
+        a, b = HostUnit(lin, 16, "flat", 22), HostUnit(blk, 16, "per_param", 23)
+    elif case == "odd_pieces_r9":     # R = 9: even pieces and odd LayerNorm pieces in one step
+        a, b = HostUnit(blk, 9, "per_param", 24), HostUnit(lin, 9, "flat", 25)
     elif case == "capped_pair":       # > 4,096 work items: one launch, 4 per CU
         a, b = HostUnit(blk * 2, 8, "per_param", 7), HostUnit(blk, 8, "per_param", 8)
     else:                             # capped_pair_flat
@@ -165,6 +170,60 @@ def test_pair_rejects_memory_the_two_share():
                                       da["v"], da["param"], b.pl, db["param"], recv)
     torch.cuda.synchronize()
     assert (recv[0] == 3).all()          # nothing was enqueued
+
+
+@pytest.mark.parametrize("R", [8, 16])
+def test_specials_through_the_paired_step(R):
+    """NaN, +-Inf, -0 and overflow in the gradients of the step half of the
+    paired launch, in a rank's even piece of the first parameter (adjacent
+    element pairs) and in the 1-element pieces of the second (the strided
+    form): master, m, v and the parameter equal the oracle's bit for bit,
+    NaN compared by class; the gather half equals the oracle's gather."""
+    print(f"[gpu] step_then_gather specials R={R}", flush=True)
+    shapes = [(2 * R, 6), (R // 2,)]
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pl = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    rng = np.random.default_rng(300 + R)
+    grads = [(rng.standard_normal(T) * 1e-3).astype(np.float32) for _ in range(R)]
+    w0 = 12 * R                    # the second parameter's first element
+    for base in (0, w0):
+        for g in grads:
+            g[base] = -0.0
+        grads[0][base + 1] = np.nan
+        grads[1][base + 2], grads[2][base + 2] = np.inf, -np.inf
+        grads[3][base + 3] = np.inf
+    for g in grads:
+        g[4] = 3.0e38
+    grads[0][5] = -0.0
+    grads = [O.bf16_rne(g) for g in grads]
+    master = O.shard_pack(po, rng.uniform(-1, 1, T).astype(np.float32))
+    master[0, 0] = -0.0
+    nb = HostUnit([(33, 4), (5,)], R, "flat", 60 + R)
+    md = to_dev(master.reshape(-1))
+    m_d, v_d = torch.zeros_like(md), torch.zeros_like(md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    recv = receivers(nb.pl, torch.bfloat16)
+    F.fsdp_adamw_step_then_gather(pl, ADAMW, 1, [to_dev(g) for g in grads], md, m_d, v_d, pd,
+                                  nb.pl, to_dev(nb.param.reshape(-1)), recv)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        mo, mm, vv, pp = O.shard_step(po, grads, master, np.zeros_like(master),
+                                      np.zeros_like(master), 1, ADAMW, "bf16")
+    for got, want, name in ((to_host(md).reshape(R, S), mo, "master"),
+                            (to_host(m_d).reshape(R, S), mm, "m"),
+                            (to_host(v_d).reshape(R, S), vv, "v")):
+        nan = np.isnan(want)
+        assert nan.any() or name != "master"
+        assert np.array_equal(np.isnan(got), nan), name
+        assert_bitexact(np.where(nan, 0, got), np.where(nan, 0, want), name)
+    gq = to_host(pd).reshape(R, S)
+    qnan = (pp & 0x7FFF) > 0x7F80
+    assert np.array_equal((gq & 0x7FFF) > 0x7F80, qnan)
+    assert_bitexact(np.where(qnan, 0, gq), np.where(qnan, 0, pp), "param")
+    full, _ = O.gather_unflatten(nb.po, nb.param)
+    for r in recv:
+        assert_bitexact(to_host(r), full, "gather")
 
 
 @pytest.mark.parametrize("R", [1, 2, 64])
