@@ -109,9 +109,9 @@ def kernel_src_hash():
 # fragments that select their dispatches in a rocprofv3 counter CSV, what
 # the kernel is).
 TRAFFIC_KERNELS = {
-    "fused": (("::k_fused<", "::k_fused_one<"),
-              "k_fused / k_fused_one (fused reduce-scatter-average + AdamW + bf16 recast, "
-              "alone)"),
+    "fused": (("::k_fused<", "::k_fused_one<", "::k_fused_pair<"),
+              "k_fused / k_fused_one / k_fused_pair (fused reduce-scatter-average + AdamW + "
+              "bf16 recast, alone)"),
     "fused_gather": (("::k_fused_two_gather<", "::k_fused_gather<"),
                      "k_fused_two_gather / k_fused_gather (one unit's fused step, then the "
                      "next unit's gather, in one launch)"),

@@ -8,10 +8,11 @@
 //   * the arithmetic kernels move 4 consecutive elements per lane per pass
 //     (8-byte bf16 and 16-byte fp32 accesses), the copy kernels 16 bytes per
 //     lane; 4 elements per lane beat 8 because twice as many waves keep
-//     requests in flight for the same registers.  The fused step takes one
-//     element per lane in short launches of its own (k_fused_one) and two
-//     adjacent ones in the launch it shares with a gather at R >= 8
-//     (k_fused_two_gather), where those measured faster;
+//     requests in flight for the same registers.  At R >= 8 the fused step
+//     takes one element per lane in short launches of its own
+//     (k_fused_one; also at R = 3 and 4) and two adjacent ones in longer
+//     launches and in the launch it shares with a gather (k_fused_pair,
+//     k_fused_two_gather), where those measured faster;
 //   * every streaming access is nontemporal: the data is touched once, and
 //     keeping it out of the caches raised the fused kernel from 4.8 to
 //     5.6 TB/s in isolation (the overlapping word pairs of misaligned
@@ -226,10 +227,10 @@ struct Io<u16> {
 // per lane, and that arithmetic of the last workgroups is what a short
 // launch waits for at its end.  Measured on MI355X, back-to-back launches
 // on the 12-layer model's 3.1M-element units (R = 8, bf16 gradients): 23.15
-// against 24.05 us.  In the reduce-scatter and AdamW kernels alone and in
-// long capped launches four elements per lane stayed faster, and in the
-// launch shared with a gather two adjacent elements per lane (31.2 us,
-// against 31.8 with one or four).
+// against 24.05 us.  In the reduce-scatter and AdamW kernels alone four
+// elements per lane stayed faster, and in the launch shared with a gather
+// and in long capped launches at R >= 8 two adjacent elements per lane
+// (paired: 31.2 us, against 31.8 with one or four).
 template <typename T>
 struct One;
 template <>
@@ -944,17 +945,19 @@ __device__ __forceinline__ void fused_ne_wg(const Work* __restrict__ work,
 // The fused step with two adjacent elements per lane: workgroup b takes
 // elements [512 (b % 2), + 512) of work item b / 2, lane t the pair at
 // 2t, so every state, gradient and parameter access moves a lane's two
-// elements at once (8 or 4 bytes, naturally aligned).  That needs an even
-// destination offset, length and source offset; an item without them (an
-// odd-sized piece of a parameter) takes fused_ne_wg's two strided
-// elements, on the same workgroup-to-item mapping.  div_bias divides.
+// elements at once (8 or 4 bytes, naturally aligned).  That needs 16-byte
+// aligned bases (a.vec) and an even destination offset, length and source
+// offset; otherwise (an odd-sized piece of a parameter, a base aligned to
+// its element only) the item takes fused_ne_wg's two strided elements, on
+// the same workgroup-to-item mapping.  div_bias divides.
 template <typename G, typename P, int RT, bool REC>
 __device__ __forceinline__ void fused_pair_wg(const Work* __restrict__ work,
                                               const FusedArgs<ptr_cap(RT)>& a, int b) {
   const Work w = work[b / 2];
   const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
   args_in_sgprs<RT, REC>(w, a);
-  const bool even = ((w.dst | w.len) & 1) == 0 && (w.src < 0 || (w.src & 1) == 0);
+  const bool even =
+      a.vec != 0 && ((w.dst | w.len) & 1) == 0 && (w.src < 0 || (w.src & 1) == 0);
   if (!even) {
     fused_ne_wg<G, P, RT, REC, 2, true>(work, a, b);
     return;
@@ -973,6 +976,20 @@ __device__ __forceinline__ void fused_pair_wg(const Work* __restrict__ work,
   Two<float>::store(a.m + e, m);
   Two<float>::store(a.v + e, v);
   Two<P>::store(static_cast<P*>(a.param) + e, p);
+}
+
+// The fused step alone in the two-element form: launches of more than
+// 4,096 work items at R >= 8, two workgroups per item, 4 per CU
+// (fused_pair_lds).  On the 872M-parameter group (852k items, alternating
+// runs on one machine): 5.66-5.72 ms against 5.93-5.96 ms with four
+// elements per lane at 3 per CU, 6.40-6.48 TB/s; the cap at 3, 5-6 or 8
+// per CU: 6.12, 5.77-5.79 and 6.14 ms.  The 12-layer model in 2-block
+// units (6,260 items): 43.5-43.6 against 44.3-44.7 us; in 4-block units
+// (12,520): 87.7-88.7 against 88.9-90.0 us.
+template <typename G, typename P, int RT, bool REC>
+__global__ __launch_bounds__(kThreads) void k_fused_pair(const Work* __restrict__ work,
+                                                         FusedArgs<ptr_cap(RT)> a) {
+  fused_pair_wg<G, P, RT, REC>(work, a, static_cast<int>(blockIdx.x));
 }
 
 // The fused step of one unit and the gather of another in one launch:
@@ -1139,6 +1156,11 @@ unsigned fused_lds(int64_t n_work) {
   return 48 * 1024;                             // 3 per CU
 }
 
+// The cap of the two-element form (fused_pair_wg: alone or paired with a
+// gather), whose own resources allow 8 per CU: none up to 4,096 items, 4
+// per CU above at every length.
+unsigned fused_pair_lds(int64_t n_work) { return n_work <= kSmallFusedLaunch ? 0 : 32 * 1024; }
+
 // The same cap for the unfused AdamW step (8 streams per workgroup: the
 // reduced gradient, master, m and v read; master, m, v and the parameter
 // written), whose best is 4 per CU.  One pass per workgroup, on the
@@ -1203,8 +1225,7 @@ const void* pick_fused(int R) {
     case 5: return reinterpret_cast<const void*>(&k_fused<G, P, 5, REC>);
     case 6: return reinterpret_cast<const void*>(&k_fused<G, P, 6, REC>);
     case 7: return reinterpret_cast<const void*>(&k_fused<G, P, 7, REC>);
-    case 8: return reinterpret_cast<const void*>(&k_fused<G, P, 8, REC>);
-    default: return reinterpret_cast<const void*>(&k_fused<G, P, 0, REC>);
+    default: return nullptr;  // R >= 8 takes the one- or two-element forms
   }
 }
 
@@ -1214,6 +1235,21 @@ const void* pick_fused_one(int R) {
        : R == 4 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 4, REC>)
        : R == 3 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 3, REC>)
                 : reinterpret_cast<const void*>(&k_fused_one<G, P, 0, REC>);
+}
+
+template <typename G, typename P, bool REC>
+const void* pick_fused_pair(int R) {
+  return R == 8 ? reinterpret_cast<const void*>(&k_fused_pair<G, P, 8, REC>)
+                : reinterpret_cast<const void*>(&k_fused_pair<G, P, 0, REC>);
+}
+
+template <bool REC>
+const void* fused_pair_fn(int grad_dt, int param_dt, int R) {
+  if (grad_dt == FSDP_BF16)
+    return param_dt == FSDP_BF16 ? pick_fused_pair<u16, u16, REC>(R)
+                                 : pick_fused_pair<u16, float, REC>(R);
+  return param_dt == FSDP_BF16 ? pick_fused_pair<float, u16, REC>(R)
+                               : pick_fused_pair<float, float, REC>(R);
 }
 
 template <bool REC>
@@ -1226,8 +1262,8 @@ const void* fused_one_fn(int grad_dt, int param_dt, int R) {
 }
 
 // The one-element form runs short standalone fused steps (no workgroup cap)
-// with 3, 4 or at least 8 replicas; everything else takes four elements per
-// lane.  On the hidden-512 block (3.1M parameters), alternating runs on one
+// with 3, 4 or at least 8 replicas; longer ones at R >= 8 take two adjacent
+// elements per lane (k_fused_pair), everything else four.  On the hidden-512 block (3.1M parameters), alternating runs on one
 // machine, it took the fused step alone at R = 4 from 20.7-21.5 to
 // 19.9-20.1 us (FSDP1 layout 20.8-23.1 -> 20.6 us) and at R = 3 from
 // 20.4-20.5 to 19.6-19.7 us (FSDP1 19.4-19.8 -> 19.1-19.4 us).  R = 5..7,
@@ -1246,8 +1282,7 @@ const void* pick_fused_gather(int R) {
     case 5: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 5, REC>);
     case 6: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 6, REC>);
     case 7: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 7, REC>);
-    case 8: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 8, REC>);
-    default: return reinterpret_cast<const void*>(&k_fused_gather<G, P, 0, REC>);
+    default: return nullptr;  // R >= 8 takes k_fused_two_gather
   }
 }
 
@@ -1359,24 +1394,33 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
                         int grad_dt, float* master, float* m, float* v, void* param,
                         int param_dt, const AdamScalars& sc, const AdamScalars* scp,
                         bool vec, const Sink& stream) {
-  if (fused_one_lane(n_work, R)) {
+  // short launches at R = 3, 4 or >= 8: one element per lane, kSplit
+  // workgroups per item; longer ones at R >= 8: two, two workgroups per item
+  const bool one = fused_one_lane(n_work, R);
+  if (one || R >= 8) {
     if (n_work <= 0) return hipSuccess;
-    if (n_work > kMaxBlocks / kSplit) return hipErrorInvalidValue;
-    const void* fn = scp ? fused_one_fn<true>(grad_dt, param_dt, R)
-                         : fused_one_fn<false>(grad_dt, param_dt, R);
-    const dim3 grid(static_cast<unsigned>(n_work * kSplit));
+    const int64_t split = one ? kSplit : 2;
+    if (n_work > kMaxBlocks / split) return hipErrorInvalidValue;
+    const void* fn = one ? (scp ? fused_one_fn<true>(grad_dt, param_dt, R)
+                                : fused_one_fn<false>(grad_dt, param_dt, R))
+                         : (scp ? fused_pair_fn<true>(grad_dt, param_dt, R)
+                                : fused_pair_fn<false>(grad_dt, param_dt, R));
+    const unsigned lds = one ? 0 : fused_pair_lds(n_work);
+    const dim3 grid(static_cast<unsigned>(n_work * split));
     if (R <= kSmallPtrs) {
-      FusedArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), master, m, v, param, sc, scp, R, 1};
+      FusedArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), master, m, v, param, sc, scp, R,
+                              vec ? 1 : 0};
       void* args[] = {const_cast<Work**>(&work), &a};
-      return stream.launch(fn, grid, dim3(kThreads), args, 0);
+      return stream.launch(fn, grid, dim3(kThreads), args, lds);
     }
     FusedArgs<FSDP_MAX_RANKS> a{narrow<FSDP_MAX_RANKS>(grads), master, m, v, param, sc, scp, R,
-                                1};
+                                vec ? 1 : 0};
     void* args[] = {const_cast<Work**>(&work), &a};
-    return stream.launch(fn, grid, dim3(kThreads), args, 0);
+    return stream.launch(fn, grid, dim3(kThreads), args, lds);
   }
   const void* fn = scp ? fused_fn<true>(grad_dt, param_dt, R)
                        : fused_fn<false>(grad_dt, param_dt, R);
+  if (fn == nullptr) return hipErrorInvalidValue;
   if (R <= kSmallPtrs) {
     FusedArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), master, m, v, param, sc, scp, R,
                             vec ? 1 : 0};
@@ -1476,7 +1520,8 @@ hipError_t launch_fused_gather(const Work* fwork, int64_t n_fused, const PtrArra
                               : fused_two_gather_fn<false>(grad_dt, param_dt, R))
                        : (scp ? fused_gather_fn<true>(grad_dt, param_dt, R)
                               : fused_gather_fn<false>(grad_dt, param_dt, R));
-  const unsigned lds = fused_lds(n_fused);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  const unsigned lds = two ? fused_pair_lds(n_fused) : fused_lds(n_fused);
   const dim3 grid(static_cast<unsigned>(fused_blocks + n_gather));
   if (R <= kSmallPtrs) {   // the specialised kernel: 8 slots for both arrays
     if (n_dst > kSmallPtrs) return hipErrorInvalidValue;

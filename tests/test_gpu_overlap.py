@@ -226,6 +226,40 @@ def test_specials_through_the_paired_step(R):
         assert_bitexact(to_host(r), full, "gather")
 
 
+def test_pair_with_bases_off_alignment():
+    """The paired call at R = 8 with the step's arrays a few elements past
+    16-byte alignment: every item takes the two strided elements instead of
+    the adjacent pairs; bit for bit against the oracle."""
+    print("[gpu] step_then_gather, bases off alignment", flush=True)
+    blk, lin = shapes_of(BLOCK_512), shapes_of(LINEARS_512)
+    a, b = HostUnit(blk, 8, "per_param", 26), HostUnit(lin, 8, "flat", 27)
+
+    def place(x: np.ndarray, k: int):
+        t = to_dev(x.reshape(-1))
+        base = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+        base[k:k + t.numel()].copy_(t)
+        return base[k:k + t.numel()]
+
+    md, m_d, v_d = place(a.master, 1), place(a.m, 3), place(a.v, 1)
+    pd = place(a.param, 1)
+    g_d = [place(g, 1 + q % 3) for q, g in enumerate(a.grads)]
+    recv = receivers(b.pl, torch.bfloat16)
+    nparam = to_dev(b.param.reshape(-1))
+    mo, mm, vv = a.master, a.m, a.v
+    for t in (1, 2):
+        F.fsdp_adamw_step_then_gather(a.pl, ADAMW, t, g_d, md, m_d, v_d, pd, b.pl, nparam, recv)
+        mo, mm, vv, pp = O.shard_step(a.po, a.grads, mo, mm, vv, t, ADAMW, "bf16")
+    torch.cuda.synchronize()
+    R, S = a.po.R, a.po.S
+    assert_bitexact(to_host(md).reshape(R, S), mo, "master")
+    assert_bitexact(to_host(m_d).reshape(R, S), mm, "m")
+    assert_bitexact(to_host(v_d).reshape(R, S), vv, "v")
+    assert_bitexact(to_host(pd).reshape(R, S), pp, "param")
+    full, _ = O.gather_unflatten(b.po, b.param)
+    for r in recv:
+        assert_bitexact(to_host(r), full, "gather")
+
+
 @pytest.mark.parametrize("R", [1, 2, 64])
 def test_pair_at_extreme_world_sizes(R):
     """One rank (the step is local, the gather a copy) and 64 ranks (most

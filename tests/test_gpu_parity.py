@@ -700,6 +700,52 @@ def test_fused_r3_above_4096_items_misaligned_four_element_form():
         assert_bitexact(to_host(pd).reshape(R, S), po16, f"param t={t}")
 
 
+@pytest.mark.parametrize("R,shapes,aligned", [
+    (8, [(2049, 2050), (9,)], True),     # even pieces, one 1-element piece
+    (9, [(2043, 2049), (10,)], True),    # odd S: odd head and tail items
+    (16, [(4100, 1030)], True),          # R > 8: the 64-slot instance
+    (8, [(2049, 2050), (9,)], False),    # bases off 16-byte alignment
+])
+def test_long_fused_step_two_element_form(R, shapes, aligned):
+    """The standalone fused step at R >= 8 with more than 4,096 work items:
+    the two-element kernel (adjacent pairs where the item's offsets, length
+    and the bases allow, else two strided elements), capped at 4 per CU.
+    Bit for bit against the oracle (master, m, v, parameter), 2 steps."""
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    items = pg.work_items(0)
+    assert len(items) > 4096
+    banner(f"fused two-element form, R={R}, {len(items)} items, aligned={aligned}")
+    rng = np.random.default_rng(81 + R)
+
+    def place(a: np.ndarray, k: int):
+        """a on the device, k elements past a 256-byte aligned base."""
+        t = to_dev(a)
+        if aligned:
+            return t
+        base = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+        base[k:k + t.numel()].copy_(t)
+        return base[k:k + t.numel()]
+
+    master = O.shard_pack(po, rng.uniform(-0.05, 0.05, T).astype(np.float32))
+    md = place(master.reshape(-1), 1)
+    m_d = place(np.zeros(R * S, np.float32), 3)
+    v_d = place(np.zeros(R * S, np.float32), 1)
+    pd = place(np.zeros(R * S, np.uint16), 1)
+    mo, vo = np.zeros_like(master), np.zeros_like(master)
+    for t in (1, 2):
+        grads = [O.bf16_rne((rng.standard_normal(T) * 1e-3).astype(np.float32))
+                 for _ in range(R)]
+        F.fsdp_adamw_shard_step(pg, ADAMW, t, [place(g, 1 + q % 5) for q, g in enumerate(grads)],
+                                md, m_d, v_d, pd)
+        master, mo, vo, po16 = O.shard_step(po, grads, master, mo, vo, t, ADAMW, "bf16")
+        assert_bitexact(to_host(md).reshape(R, S), master, f"master t={t}")
+        assert_bitexact(to_host(m_d).reshape(R, S), mo, f"m t={t}")
+        assert_bitexact(to_host(v_d).reshape(R, S), vo, f"v t={t}")
+        assert_bitexact(to_host(pd).reshape(R, S), po16, f"param t={t}")
+
+
 @pytest.mark.parametrize("R", [3, 4, 8, 11])
 def test_specials_through_the_one_element_fused_step(R):
     """NaN, +-Inf, -0 and overflow in the gradients of a short launch at
