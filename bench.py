@@ -116,7 +116,8 @@ TRAFFIC_KERNELS = {
                      "k_fused_two_gather / k_fused_gather (one unit's fused step, then the "
                      "next unit's gather, in one launch)"),
     "allreduce": (("::k_allreduce<",), "k_allreduce (DDP all-reduce-average to R receivers)"),
-    "adamw": (("::k_adamw<",), "k_adamw (AdamW + recast on an fp32 gradient)"),
+    "adamw": (("::k_adamw<", "::k_adamw_two<"),
+              "k_adamw / k_adamw_two (AdamW + recast on an fp32 gradient)"),
     "gather": (("::k_copy<2, 16, 8, 8>",),
                "k_copy (bf16 gather + unflatten to 8 receivers, 16-byte lanes)"),
     "accumulate": (("::k_accumulate<",), "k_accumulate (fp32 gradient accumulation)"),

@@ -761,6 +761,46 @@ __global__ __launch_bounds__(kThreads) void k_rs_avg(const Work* __restrict__ wo
     rs_item<G, RT, false, true>(w, a, k);
 }
 
+// The reduce-scatter alone in short launches at R >= 8: two adjacent
+// elements per lane and two workgroups per item, on fused_pair_wg's layout
+// (two strided elements where an item's offsets, length or the bases do
+// not allow the pair), the descriptor and pointers in one round of scalar
+// loads.  The 12-layer model's units: 11.6-11.8 us against 12.1 us with
+// four elements per lane (alternating runs on one machine); on the
+// 872M-parameter group the two forms measured level, so long launches keep
+// four.
+template <typename G, int RT>
+__global__ __launch_bounds__(kThreads) void k_rs_two(const Work* __restrict__ work,
+                                                     RsArgs<ptr_cap(RT)> a) {
+  const int b = static_cast<int>(blockIdx.x);
+  const Work w = work[b / 2];
+  if constexpr (RT == 8) {
+    asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.g.p[0]), "s"(a.g.p[1]),
+                 "s"(a.g.p[2]), "s"(a.g.p[3]), "s"(a.g.p[4]), "s"(a.g.p[5]), "s"(a.g.p[6]),
+                 "s"(a.g.p[7]), "s"(a.out));
+  } else {
+    asm volatile("" ::"s"(w.dst), "s"(w.src), "s"(w.len), "s"(a.out));
+  }
+  const int64_t half = static_cast<int64_t>(b % 2) * (2 * kThreads);
+  const bool even =
+      a.vec != 0 && ((w.dst | w.len) & 1) == 0 && (w.src < 0 || (w.src & 1) == 0);
+  if (even) {
+    const int64_t off = half + 2 * threadIdx.x;
+    if (off >= w.len) return;
+    float avg[2] = {0.0f, 0.0f};
+    if (w.src >= 0) grad_avg_two<G, RT>(a.g, a.R, w.src + off, avg);
+    Two<float>::store(a.out + w.dst + off, avg);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t off = half + j * kThreads + threadIdx.x;
+    if (off >= w.len) return;
+    const float x = w.src < 0 ? 0.0f : grad_avg_one<G, RT>(a.g, a.R, w.src + off);
+    One<float>::store(a.out + w.dst + off, x);
+  }
+}
+
 // ------------------------------------------------------------------ AdamW
 struct AdamArgs {
   const float* g;
@@ -774,8 +814,9 @@ struct AdamArgs {
   int vec;
 };
 
-// One pass per workgroup: lane c of the grid owns elements [4c, 4c + 4).
-template <typename P, bool REC, bool FASTDIV>
+// One pass per workgroup: lane c of the grid owns elements [4c, 4c + 4)
+// (long launches; IEEE division).
+template <typename P, bool REC>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
   P* __restrict__ param = static_cast<P*>(a.param);
   const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
@@ -789,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
     Io<float>::load4(a.m + e0, true, m);
     Io<float>::load4(a.v + e0, true, v);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) adamw1<FASTDIV>(g[k], p[k], m[k], v[k], sc);
+    for (int k = 0; k < 4; ++k) adamw1<false>(g[k], p[k], m[k], v[k], sc);
     Io<float>::store4(a.master + e0, true, p);
     Io<float>::store4(a.m + e0, true, m);
     Io<float>::store4(a.v + e0, true, v);
@@ -798,12 +839,48 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamArgs a) {
     const int64_t hi = e0 + kEPL < a.n ? e0 + kEPL : a.n;
     for (int64_t e = e0; e < hi; ++e) {
       float p = a.master[e], m = a.m[e], v = a.v[e];
-      adamw1<FASTDIV>(a.g[e], p, m, v, sc);
+      adamw1<false>(a.g[e], p, m, v, sc);
       a.master[e] = p;
       a.m[e] = m;
       a.v[e] = v;
       Io<P>::store1(param + e, p);
     }
+  }
+}
+
+// AdamW alone in short launches (up to 4,096 four-element workgroups): two
+// adjacent elements per lane (8-byte state and gradient accesses when the
+// bases are 16-byte aligned), the division of div_bias.  The 12-layer
+// model's units: 17.9-18.0 us against 18.5-18.6 us with four elements per
+// lane (alternating runs on one machine); on the 872M-parameter group four
+// elements at 4 per CU stayed faster (4.25 against 4.29-4.33 ms).
+template <typename P, bool REC>
+__global__ __launch_bounds__(kThreads) void k_adamw_two(AdamArgs a) {
+  const AdamScalars sc = scalars_of<REC>(a.sc, a.scp);
+  const int64_t e = 2 * (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x);
+  if (e >= a.n) return;
+  if (a.vec && e + 1 < a.n) {
+    float g[2], p[2], m[2], v[2];
+    Two<float>::load(a.g + e, g);
+    Two<float>::load(a.master + e, p);
+    Two<float>::load(a.m + e, m);
+    Two<float>::load(a.v + e, v);
+    adamw1<true>(g[0], p[0], m[0], v[0], sc);
+    adamw1<true>(g[1], p[1], m[1], v[1], sc);
+    Two<float>::store(a.master + e, p);
+    Two<float>::store(a.m + e, m);
+    Two<float>::store(a.v + e, v);
+    Two<P>::store(static_cast<P*>(a.param) + e, p);
+    return;
+  }
+  const int64_t hi = e + 2 < a.n ? e + 2 : a.n;
+  for (int64_t i = e; i < hi; ++i) {
+    float p = a.master[i], m = a.m[i], v = a.v[i];
+    adamw1<true>(a.g[i], p, m, v, sc);
+    a.master[i] = p;
+    a.m[i] = m;
+    a.v[i] = v;
+    Io<P>::store1(static_cast<P*>(a.param) + i, p);
   }
 }
 
@@ -1180,13 +1257,23 @@ unsigned adamw_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 32
 // 345.5 us.
 unsigned allreduce_lds(int64_t blocks) { return blocks <= kSmallFusedLaunch ? 0 : 48 * 1024; }
 
-template <bool FASTDIV>
+// The AdamW kernel for the parameter dtype and the scalars' source: the
+// two-element form (TWO) or the four-element one.
+template <bool TWO>
 const void* adamw_fn(int param_dt, bool rec) {
-  if (rec)
-    return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, true, FASTDIV>)
-                                 : reinterpret_cast<const void*>(&k_adamw<float, true, FASTDIV>);
-  return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, false, FASTDIV>)
-                               : reinterpret_cast<const void*>(&k_adamw<float, false, FASTDIV>);
+  if constexpr (TWO) {
+    if (rec)
+      return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw_two<u16, true>)
+                                   : reinterpret_cast<const void*>(&k_adamw_two<float, true>);
+    return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw_two<u16, false>)
+                                 : reinterpret_cast<const void*>(&k_adamw_two<float, false>);
+  } else {
+    if (rec)
+      return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, true>)
+                                   : reinterpret_cast<const void*>(&k_adamw<float, true>);
+    return param_dt == FSDP_BF16 ? reinterpret_cast<const void*>(&k_adamw<u16, false>)
+                                 : reinterpret_cast<const void*>(&k_adamw<float, false>);
+  }
 }
 
 template <typename G>
@@ -1202,6 +1289,12 @@ const void* pick_rs(int R) {
     case 8: return reinterpret_cast<const void*>(&k_rs_avg<G, 8>);
     default: return reinterpret_cast<const void*>(&k_rs_avg<G, 0>);
   }
+}
+
+template <typename G>
+const void* pick_rs_two(int R) {
+  return R == 8 ? reinterpret_cast<const void*>(&k_rs_two<G, 8>)
+                : reinterpret_cast<const void*>(&k_rs_two<G, 0>);
 }
 
 template <typename G, typename O>
@@ -1366,6 +1459,18 @@ hipError_t launch_pack_cast(const Work* work, int64_t n_work, const void* src, i
 
 hipError_t launch_rs_avg(const Work* work, int64_t n_work, const PtrArray& grads, int R,
                          int grad_dt, float* out, bool vec, const Sink& stream) {
+  if (R >= 8 && n_work > 0 && n_work <= kSmallFusedLaunch) {  // short: two per lane
+    const void* fn = grad_dt == FSDP_BF16 ? pick_rs_two<u16>(R) : pick_rs_two<float>(R);
+    const dim3 grid(static_cast<unsigned>(2 * n_work));
+    if (R <= kSmallPtrs) {
+      RsArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), out, R, vec ? 1 : 0};
+      void* args[] = {const_cast<Work**>(&work), &a};
+      return stream.launch(fn, grid, dim3(kThreads), args, 0);
+    }
+    RsArgs<FSDP_MAX_RANKS> a{narrow<FSDP_MAX_RANKS>(grads), out, R, vec ? 1 : 0};
+    void* args[] = {const_cast<Work**>(&work), &a};
+    return stream.launch(fn, grid, dim3(kThreads), args, 0);
+  }
   const void* fn = grad_dt == FSDP_BF16 ? pick_rs<u16>(R) : pick_rs<float>(R);
   if (R <= kSmallPtrs) {
     RsArgs<kSmallPtrs> a{narrow<kSmallPtrs>(grads), out, R, vec ? 1 : 0};
@@ -1383,10 +1488,14 @@ hipError_t launch_adamw(int64_t n, const float* g, float* master, float* m, floa
   const int64_t chunks = (n + kEPL - 1) / kEPL;
   const int64_t blocks = (chunks + kThreads - 1) / kThreads;
   if (blocks > kMaxBlocks) return hipErrorInvalidValue;
-  const void* fn = blocks <= kSmallFusedLaunch ? adamw_fn<true>(param_dt, scp != nullptr)
-                                               : adamw_fn<false>(param_dt, scp != nullptr);
   void* args[] = {&a};
-  return stream.launch(fn, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
+  if (blocks <= kSmallFusedLaunch) {  // short: two elements per lane
+    const int64_t blocks2 = (n + 2 * kThreads - 1) / (2 * kThreads);
+    return stream.launch(adamw_fn<true>(param_dt, scp != nullptr),
+                         dim3(static_cast<unsigned>(blocks2)), dim3(kThreads), args, 0);
+  }
+  return stream.launch(adamw_fn<false>(param_dt, scp != nullptr),
+                       dim3(static_cast<unsigned>(blocks)), dim3(kThreads), args,
                        adamw_lds(blocks));
 }
 

@@ -246,6 +246,49 @@ def test_misaligned_base_pointers_take_the_scalar_path():
         assert_bf16_within_ulp(to_host(recv[r]), want, "gather misaligned")
 
 
+@pytest.mark.parametrize("R,aligned", [(8, True), (8, False), (9, True), (9, False)])
+def test_short_reduce_scatter_and_adamw_two_element_forms(R, aligned):
+    """The reduce-scatter alone and AdamW alone in short launches at R >= 8
+    (two elements per lane: adjacent pairs on 16-byte aligned bases and even
+    items, two strided elements otherwise; AdamW's odd-length tail element
+    by element), on an odd-sized unit with bases aligned or a few elements
+    off: bit for bit against the oracle, 2 steps."""
+    shapes = [(75, 33), (7,), (40, 16), (9,)]
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    assert (R * S) % 2 == (1 if R == 9 else 0)
+    banner(f"short reduce-scatter + AdamW, R={R}, aligned={aligned}")
+    rng = np.random.default_rng(400 + 2 * R + int(aligned))
+
+    def place(a: np.ndarray, k: int):
+        t = to_dev(a.reshape(-1))
+        if aligned:
+            return t
+        base = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+        base[k:k + t.numel()].copy_(t)
+        return base[k:k + t.numel()]
+
+    master = O.shard_pack(po, rng.uniform(-1, 1, T).astype(np.float32))
+    md, m_d, v_d = place(master, 1), place(np.zeros((R, S), np.float32), 3), \
+        place(np.zeros((R, S), np.float32), 1)
+    pd = place(np.zeros((R, S), np.uint16), 1)
+    rs_d = place(np.zeros((R, S), np.float32), 3)
+    mo, vo = np.zeros_like(master), np.zeros_like(master)
+    for t in (1, 2):
+        grads = [O.bf16_rne((rng.standard_normal(T) * 1e-2).astype(np.float32))
+                 for _ in range(R)]
+        F.fsdp_reduce_scatter_avg(pg, [place(g, 1 + q % 3) for q, g in enumerate(grads)], rs_d)
+        rs = O.reduce_scatter_avg(po, grads)
+        assert_bitexact(to_host(rs_d).reshape(R, S), rs, f"rs t={t}")
+        F.fsdp_adamw_shard_step(pg, ADAMW, t, rs_d, md, m_d, v_d, pd, grads_are_replicas=False)
+        master, mo, vo = O.adamw_step(master, mo, vo, rs, t, **ADAMW)
+        assert_bitexact(to_host(md).reshape(R, S), master, f"master t={t}")
+        assert_bitexact(to_host(m_d).reshape(R, S), mo, f"m t={t}")
+        assert_bitexact(to_host(v_d).reshape(R, S), vo, f"v t={t}")
+        assert_bitexact(to_host(pd).reshape(R, S), O.bf16_rne(master), f"param t={t}")
+
+
 def test_nan_inf_and_signed_zero_propagate_like_the_oracle():
     banner("nan/inf")
     shapes = [(6, 4)]
@@ -636,9 +679,9 @@ def test_unfused_adamw_above_4096_workgroups_r8():
 
 
 @pytest.mark.parametrize("gdt", ["bf16", "f32"])
-def test_fused_r8_above_4096_items_four_element_form(gdt):
+def test_fused_r8_above_4096_items_two_element_form(gdt):
     """The standalone fused step at R = 8 on a two-block unit (6,146 work
-    items: the four-element kernel with its occupancy cap, where a one-block
+    items: the two-element kernel with its occupancy cap, where a one-block
     unit takes the one-element kernel), bit for bit against the oracle, 2
     steps, bf16 and fp32 gradients."""
     shapes = two_block_unit()
@@ -647,7 +690,7 @@ def test_fused_r8_above_4096_items_four_element_form(gdt):
     pg = F.Plan(shapes, R, O.PER_PARAM)
     T, S = po.T, po.S
     assert len(pg.work_items(0)) > 4096
-    banner(f"fused R=8 four-element form, {gdt} grads")
+    banner(f"fused R=8 two-element form, {gdt} grads")
     rng = np.random.default_rng(78)
     master = O.shard_pack(po, rng.uniform(-0.05, 0.05, T).astype(np.float32))
     md = to_dev(master.reshape(-1))
