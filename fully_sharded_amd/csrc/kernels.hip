@@ -10,9 +10,10 @@
 //     lane; 4 elements per lane beat 8 because twice as many waves keep
 //     requests in flight for the same registers.  At R >= 8 the fused step
 //     takes one element per lane in short launches of its own
-//     (k_fused_one; also at R = 3 and 4) and two adjacent ones in longer
-//     launches and in the launch it shares with a gather (k_fused_pair,
-//     k_fused_two_gather), where those measured faster;
+//     (k_fused_one) and two adjacent ones in longer launches and in the
+//     launch it shares with a gather (k_fused_pair, k_fused_two_gather);
+//     so do short launches at R = 3 and 4, and the short reduce-scatter
+//     (R >= 8) and AdamW launches: where those measured faster;
 //   * every streaming access is nontemporal: the data is touched once, and
 //     keeping it out of the caches raised the fused kernel from 4.8 to
 //     5.6 TB/s in isolation (the overlapping word pairs of misaligned
@@ -219,18 +220,18 @@ struct Io<u16> {
 };
 
 // ------------------------------------------------- one element per lane
-// A second form of the fused step for short launches (R = 3, 4 or >= 8:
-// fused_one_lane) gives each lane one element (every access one naturally
+// A second form of the fused step for short launches at R >= 8
+// (fused_one_lane) gives each lane one element (every access one naturally
 // aligned 2- or 4-byte element, so no alignment case exists) and each
 // 1024-element work item four workgroups.  A wave's float64 arithmetic
 // after its loads return is then a quarter of what it is with four elements
 // per lane, and that arithmetic of the last workgroups is what a short
 // launch waits for at its end.  Measured on MI355X, back-to-back launches
 // on the 12-layer model's 3.1M-element units (R = 8, bf16 gradients): 23.15
-// against 24.05 us.  In the reduce-scatter and AdamW kernels alone four
-// elements per lane stayed faster, and in the launch shared with a gather
-// and in long capped launches at R >= 8 two adjacent elements per lane
-// (paired: 31.2 us, against 31.8 with one or four).
+// against 24.05 us.  In the reduce-scatter and AdamW kernels alone, in the
+// launch shared with a gather, in long capped launches at R >= 8 and in
+// short ones at R = 3 and 4, two adjacent elements per lane measured
+// faster (paired: 31.2 us, against 31.8 with one or four).
 template <typename T>
 struct One;
 template <>
@@ -1325,14 +1326,14 @@ const void* pick_fused(int R) {
 template <typename G, typename P, bool REC>
 const void* pick_fused_one(int R) {
   return R == 8 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 8, REC>)
-       : R == 4 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 4, REC>)
-       : R == 3 ? reinterpret_cast<const void*>(&k_fused_one<G, P, 3, REC>)
                 : reinterpret_cast<const void*>(&k_fused_one<G, P, 0, REC>);
 }
 
 template <typename G, typename P, bool REC>
 const void* pick_fused_pair(int R) {
   return R == 8 ? reinterpret_cast<const void*>(&k_fused_pair<G, P, 8, REC>)
+       : R == 4 ? reinterpret_cast<const void*>(&k_fused_pair<G, P, 4, REC>)
+       : R == 3 ? reinterpret_cast<const void*>(&k_fused_pair<G, P, 3, REC>)
                 : reinterpret_cast<const void*>(&k_fused_pair<G, P, 0, REC>);
 }
 
@@ -1354,15 +1355,20 @@ const void* fused_one_fn(int grad_dt, int param_dt, int R) {
                                : pick_fused_one<float, float, REC>(R);
 }
 
-// The one-element form runs short standalone fused steps (no workgroup cap)
-// with 3, 4 or at least 8 replicas; longer ones at R >= 8 take two adjacent
-// elements per lane (k_fused_pair), everything else four.  On the hidden-512 block (3.1M parameters), alternating runs on one
-// machine, it took the fused step alone at R = 4 from 20.7-21.5 to
-// 19.9-20.1 us (FSDP1 layout 20.8-23.1 -> 20.6 us) and at R = 3 from
-// 20.4-20.5 to 19.6-19.7 us (FSDP1 19.4-19.8 -> 19.1-19.4 us).  R = 5..7,
-// unmeasured, keep their four-element instances.
-bool fused_one_lane(int64_t n_work, int R) {
-  return (R == 3 || R == 4 || R >= 8) && n_work <= kSmallFusedLaunch;
+// Which form runs a standalone fused step.  One element per lane: short
+// launches at R >= 8.  Two adjacent elements (k_fused_pair): longer ones at
+// R >= 8 (4 per CU), and short ones at R = 3 and 4.  Four: everything else
+// (R = 5..7, unmeasured in the other forms, and long launches below R = 8).
+// On the hidden-512 block (3.1M parameters, short launches), alternating
+// runs on one machine: at R = 4 four elements 20.7-21.5 us, one 19.9-20.1,
+// two 19.8-20.1 (the step 27.3-27.9 -> 26.6-26.9 us); at R = 3 four
+// 20.4-20.5, one 19.6-20.0, two 19.1-19.6 us; in the FSDP1 layout at R = 4
+// one 20.8-21.0, two 21.0-21.3 us (the step level at 27.8-28.3 us), at R = 3
+// one 19.4-20.2, two 19.0-19.2 us (the step 25.7-26.5 -> 24.9-25.1 us).
+bool fused_one_lane(int64_t n_work, int R) { return R >= 8 && n_work <= kSmallFusedLaunch; }
+bool fused_pair_lane(int64_t n_work, int R) {
+  return R >= 8 ? n_work > kSmallFusedLaunch
+                : (R == 3 || R == 4) && n_work <= kSmallFusedLaunch;
 }
 
 template <typename G, typename P, bool REC>
@@ -1503,10 +1509,9 @@ hipError_t launch_fused(const Work* work, int64_t n_work, const PtrArray& grads,
                         int grad_dt, float* master, float* m, float* v, void* param,
                         int param_dt, const AdamScalars& sc, const AdamScalars* scp,
                         bool vec, const Sink& stream) {
-  // short launches at R = 3, 4 or >= 8: one element per lane, kSplit
-  // workgroups per item; longer ones at R >= 8: two, two workgroups per item
+  // one element per lane, kSplit workgroups per item, or two, two per item
   const bool one = fused_one_lane(n_work, R);
-  if (one || R >= 8) {
+  if (one || fused_pair_lane(n_work, R)) {
     if (n_work <= 0) return hipSuccess;
     const int64_t split = one ? kSplit : 2;
     if (n_work > kMaxBlocks / split) return hipErrorInvalidValue;

@@ -1,5 +1,6 @@
-"""The division by a bias correction that the one-element fused step and
-short AdamW launches use, checked with exact rational arithmetic on the CPU.
+"""The division by a bias correction that the one- and two-element fused
+steps and short AdamW launches use, checked with exact rational arithmetic
+on the CPU.
 
 For b = 1 - beta^t and the host's two-part reciprocal hi = RN(1/b),
 lo = RN((1 - b hi) / b), the device computes

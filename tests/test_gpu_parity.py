@@ -713,7 +713,7 @@ def test_fused_r8_above_4096_items_two_element_form(gdt):
 def test_fused_r3_above_4096_items_misaligned_four_element_form():
     """The standalone fused step at R = 3 on a two-block per-parameter unit:
     6,147 work items, so the four-element kernel with its occupancy cap
-    (short steps at R = 3 take the one-element kernel), whose ranks after 0
+    (short steps at R = 3 take the two-element kernel), whose ranks after 0
     read their gradient windows off the lane alignment (the funnelled
     loads).  Bit for bit against the oracle, 2 steps."""
     shapes = two_block_unit()
@@ -790,17 +790,17 @@ def test_long_fused_step_two_element_form(R, shapes, aligned):
 
 
 @pytest.mark.parametrize("R", [3, 4, 8, 11])
-def test_specials_through_the_one_element_fused_step(R):
+def test_specials_through_the_short_fused_step(R):
     """NaN, +-Inf, -0 and overflow in the gradients of a short launch at
-    R = 3, 4 or R >= 8 (the one-element kernel, specialised at R = 3, 4 and
-    8, generic above):
+    R = 3 or 4 (the two-element kernel) or R >= 8 (the one-element kernel,
+    specialised at 8, generic above):
     master, m, v and the parameter equal the oracle's bit for bit, NaN
     compared by class."""
     shapes = [(16, 5), (3,)]
     po = O.plan_layout(shapes, R, O.PER_PARAM)
     pg = F.Plan(shapes, R, O.PER_PARAM)
     T, S = po.T, po.S
-    banner(f"specials, one-element fused step, R={R}")
+    banner(f"specials, short fused step, R={R}")
     rng = np.random.default_rng(90 + R)
     grads = [(rng.standard_normal(T) * 1e-3).astype(np.float32) for _ in range(R)]
     for g in grads:

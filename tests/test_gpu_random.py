@@ -104,8 +104,8 @@ def test_random_sequence_matches_the_oracle(seed):
         for r in recv:
             assert_bitexact(to_host(r), want, "next unit's gather")
 
-    # a third step through the standalone fused call (at R = 4 or R >= 8 and this
-    # size, the one-element kernel)
+    # a third step through the standalone fused call (at this size the
+    # two-element kernel at R = 3 or 4, the one-element kernel at R >= 8)
     F.fsdp_adamw_shard_step(pg, ADAMW, 3, g_d, master, m, v, param)
     mo, om, ov, po_param = O.shard_step(po, grads, mo, om, ov, 3, ADAMW, "bf16")
     torch.cuda.synchronize()
