@@ -62,10 +62,14 @@ def both_entry_points(plan, inputs, step):
 
 
 def test_noalloc_matches_the_allocating_step_on_consecutive_calls():
-    big = F.Plan(shapes_of(BLOCK_512), 8, "per_param")               # 3,130 work items
+    # two blocks at R = 8: 6,146 work items, the capped two-element launch;
+    # one block: 3,130, the one-element launch; ragged R = 3: two-element
+    two = F.Plan(shapes_of(BLOCK_512) * 2, 8, "per_param")
+    big = F.Plan(shapes_of(BLOCK_512), 8, "per_param")
     small = F.Plan([(300, 17), (45,), (1000, 3)], 3, "per_param")
-    assert len(small.work_items(0)) < len(big.work_items(0))
-    for what, plan, seed, step in (("block R=8", big, 1, 3), ("ragged R=3 (smaller)", small, 2, 2),
+    assert len(small.work_items(0)) < len(big.work_items(0)) < 4096 < len(two.work_items(0))
+    for what, plan, seed, step in (("two blocks R=8", two, 6, 2), ("block R=8 (smaller)", big, 1, 3),
+                                   ("ragged R=3 (smaller)", small, 2, 2),
                                    ("block R=8 again", big, 3, 5)):
         banner(f"noalloc vs allocating step: {what}")
         ref, got = both_entry_points(plan, unit_inputs(plan, seed), step)
