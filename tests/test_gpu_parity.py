@@ -327,6 +327,60 @@ def test_nan_inf_and_signed_zero_propagate_like_the_oracle():
     assert_bf16_within_ulp(to_host(p_d).reshape(R, S), pp, "param specials")
 
 
+@pytest.mark.parametrize("R", [8, 16])
+def test_specials_through_the_short_reduce_scatter_and_adamw(R):
+    """NaN, +-Inf, -0 and overflow through the reduce-scatter alone and
+    AdamW alone in short launches at R >= 8 (two elements per lane): in a
+    rank's even piece (adjacent pairs) and in 1-element pieces (the strided
+    path); the reduced gradient, master, m, v and the parameter equal the
+    oracle's bit for bit, NaN compared by class."""
+    shapes = [(2 * R, 6), (R // 2,)]
+    po = O.plan_layout(shapes, R, O.PER_PARAM)
+    pg = F.Plan(shapes, R, O.PER_PARAM)
+    T, S = po.T, po.S
+    banner(f"specials, short reduce-scatter + AdamW, R={R}")
+    rng = np.random.default_rng(500 + R)
+    grads = [(rng.standard_normal(T) * 1e-3).astype(np.float32) for _ in range(R)]
+    for base in (0, 12 * R):       # the first parameter's and the second's first elements
+        for g in grads:
+            g[base] = -0.0
+        grads[0][base + 1] = np.nan
+        grads[1][base + 2], grads[2][base + 2] = np.inf, -np.inf
+        grads[3][base + 3] = np.inf
+    for g in grads:
+        g[4] = 3.0e38
+    grads = [O.bf16_rne(g) for g in grads]
+    rs_d = torch.empty(R * S, dtype=torch.float32, device=DEV)
+    F.fsdp_reduce_scatter_avg(pg, [to_dev(g) for g in grads], rs_d)
+    with np.errstate(invalid="ignore", over="ignore"):
+        rs = O.reduce_scatter_avg(po, grads)
+    got = to_host(rs_d).reshape(R, S)
+    nan = np.isnan(rs)
+    assert nan.any() and np.isinf(rs).any()
+    assert np.array_equal(np.isnan(got), nan)
+    assert_bitexact(np.where(nan, 0, got), np.where(nan, 0, rs), "rs")
+    master = O.shard_pack(po, rng.uniform(-1, 1, T).astype(np.float32))
+    master[0, 0] = -0.0
+    md = to_dev(master.reshape(-1))
+    m_d, v_d = torch.zeros_like(md), torch.zeros_like(md)
+    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    F.fsdp_adamw_shard_step(pg, ADAMW, 1, rs_d, md, m_d, v_d, pd, grads_are_replicas=False)
+    with np.errstate(invalid="ignore", over="ignore"):
+        mo, mm, vv = O.adamw_step(master, np.zeros_like(master), np.zeros_like(master), rs, 1,
+                                  **ADAMW)
+        pp = O.bf16_rne(mo)
+    for got, want, name in ((to_host(md).reshape(R, S), mo, "master"),
+                            (to_host(m_d).reshape(R, S), mm, "m"),
+                            (to_host(v_d).reshape(R, S), vv, "v")):
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), name
+        assert_bitexact(np.where(nan, 0, got), np.where(nan, 0, want), name)
+    gq = to_host(pd).reshape(R, S)
+    qnan = (pp & 0x7FFF) > 0x7F80
+    assert np.array_equal((gq & 0x7FFF) > 0x7F80, qnan)
+    assert_bitexact(np.where(qnan, 0, gq), np.where(qnan, 0, pp), "param")
+
+
 def test_bf16_recast_over_every_fp32_pattern():
     """The kernels' fp32 -> bf16 rounding (the pack-cast kernel; the fused
     step stores its parameter through the same device function) on all
