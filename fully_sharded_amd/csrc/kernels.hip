@@ -1056,9 +1056,10 @@ __device__ __forceinline__ void fused_pair_wg(const Work* __restrict__ work,
   Two<P>::store(static_cast<P*>(a.param) + e, p);
 }
 
-// The fused step alone in the two-element form: launches of more than
-// 4,096 work items at R >= 8, two workgroups per item, 4 per CU
-// (fused_pair_lds).  On the 872M-parameter group (852k items, alternating
+// The fused step alone in the two-element form (fused_pair_lane): launches
+// of more than 4,096 work items at R >= 8, two workgroups per item, 4 per
+// CU (fused_pair_lds); short launches at R = 3 and 4, uncapped.  On the
+// 872M-parameter group (852k items, alternating
 // runs on one machine): 5.66-5.72 ms against 5.93-5.96 ms with four
 // elements per lane at 3 per CU, 6.40-6.48 TB/s; the cap at 3, 5-6 or 8
 // per CU: 6.12, 5.77-5.79 and 6.14 ms.  The 12-layer model in 2-block
