@@ -732,32 +732,33 @@ def test_unfused_adamw_above_4096_workgroups_r8():
         assert_bitexact(to_host(pd).reshape(R, S), O.bf16_rne(master), f"param t={t}")
 
 
-@pytest.mark.parametrize("gdt", ["bf16", "f32"])
-def test_fused_r8_above_4096_items_two_element_form(gdt):
+@pytest.mark.parametrize("gdt,pdt", [("bf16", "bf16"), ("f32", "bf16"), ("bf16", "f32"),
+                                     ("f32", "f32")])
+def test_fused_r8_above_4096_items_two_element_form(gdt, pdt):
     """The standalone fused step at R = 8 on a two-block unit (6,146 work
     items: the two-element kernel with its occupancy cap, where a one-block
     unit takes the one-element kernel), bit for bit against the oracle, 2
-    steps, bf16 and fp32 gradients."""
+    steps, bf16 and fp32 gradients and parameters."""
     shapes = two_block_unit()
     R = 8
     po = O.plan_layout(shapes, R, O.PER_PARAM)
     pg = F.Plan(shapes, R, O.PER_PARAM)
     T, S = po.T, po.S
     assert len(pg.work_items(0)) > 4096
-    banner(f"fused R=8 two-element form, {gdt} grads")
+    banner(f"fused R=8 two-element form, {gdt} grads, {pdt} params")
     rng = np.random.default_rng(78)
     master = O.shard_pack(po, rng.uniform(-0.05, 0.05, T).astype(np.float32))
     md = to_dev(master.reshape(-1))
     m_d = torch.zeros_like(md)
     v_d = torch.zeros_like(md)
-    pd = torch.empty(R * S, dtype=torch.bfloat16, device=DEV)
+    pd = torch.empty(R * S, dtype=tdt(pdt), device=DEV)
     mo, vo = np.zeros_like(master), np.zeros_like(master)
     for t in (1, 2):
         grads = [(rng.standard_normal(T) * 1e-3).astype(np.float32) for _ in range(R)]
         if gdt == "bf16":
             grads = [O.bf16_rne(g) for g in grads]
         F.fsdp_adamw_shard_step(pg, ADAMW, t, [to_dev(g) for g in grads], md, m_d, v_d, pd)
-        master, mo, vo, po16 = O.shard_step(po, grads, master, mo, vo, t, ADAMW, "bf16")
+        master, mo, vo, po16 = O.shard_step(po, grads, master, mo, vo, t, ADAMW, pdt)
         assert_bitexact(to_host(md).reshape(R, S), master, f"master t={t}")
         assert_bitexact(to_host(m_d).reshape(R, S), mo, f"m t={t}")
         assert_bitexact(to_host(v_d).reshape(R, S), vo, f"v t={t}")
